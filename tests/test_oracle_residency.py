@@ -1,0 +1,163 @@
+"""Pins for the oracle's global LRU cache and q* miss split — CPU only."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from oracle.residency import Residency
+
+
+def test_hand_worked_lru_sequence():
+    r = Residency(capacity=2, layers=1, experts=4, bp_mbps=1, bh_mbps=1)
+    p = r.lookup_plan(0, [[0, 1]])
+    assert p.fills == [(0, 0), (1, 1)] and p.host == [] and p.hits == []
+    p = r.lookup_plan(0, [[2]])           # both stamps 1: key 0 is the lower key
+    assert p.evicted == [0] and p.fills == [(2, 0)]
+    p = r.lookup_plan(0, [[1, 3]])        # 1 hits (now stamp 3); 2 is the only victim
+    assert p.hits == [(1, 1)] and p.evicted == [2] and p.fills == [(3, 0)]
+    p = r.lookup_plan(0, [[0, 2]])        # both at stamp 3: evict key 1, then key 3
+    assert p.evicted == [1, 3] and p.fills == [(0, 0), (2, 1)]
+    p = r.lookup_plan(0, [[0, 1], [2, 3]])  # 2 hits fill the cache: overflow to host
+    assert p.hits == [(0, 0), (2, 1)] and p.q == 2 and p.q_fill == 0 and p.host == [1, 3]
+    assert r.snapshot() == ([0, 2], [5, 5], 5, 0)
+
+
+def test_misses_ranked_by_token_count_then_id():
+    r = Residency(capacity=8, layers=1, experts=4, bp_mbps=1, bh_mbps=2)
+    p = r.lookup_plan(0, [[0, 1], [1, 2], [1, 0]])  # counts 0:2, 1:3, 2:1
+    # m = 3, q = floor(3*1/2) = 1: the most-routed expert is filled
+    assert p.q == 1 and [e for e, _ in p.fills] == [1] and p.host == [0, 2]
+    assert p.counts == {0: 2, 1: 3, 2: 1} and p.credit == 1
+
+
+def test_credit_hand_worked_quarter_split():
+    # B_P / B_H = 1/4 with one miss per call: every fourth miss is filled
+    r = Residency(capacity=100, layers=100, experts=1, bp_mbps=1, bh_mbps=4)
+    qs = [r.lookup_plan(l, [[0]]).q for l in range(12)]
+    assert qs == [0, 0, 0, 1] * 3
+
+
+def _random_calls(seed, n, L, E, k, T=1):
+    rng = np.random.default_rng(seed)
+    calls = []
+    for _ in range(n):
+        l = int(rng.integers(0, L))
+        ids = [list(rng.choice(E, size=k, replace=False)) for _ in range(T)]
+        calls.append((l, ids))
+    return calls
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_invariants_on_random_calls(seed):
+    rng = np.random.default_rng(100 + seed)
+    L, E, k = 3, 12, int(rng.integers(1, 5))
+    C = int(rng.integers(0, 3 * k + 2))
+    bp, bh = int(rng.integers(1, 200)), int(rng.integers(1, 200))
+    r = Residency(C, L, E, bp, bh)
+    for l, ids in _random_calls(seed, 200, L, E, k, T=int(rng.integers(1, 4))):
+        before = r.resident()
+        stamps = list(r.slot_stamp)
+        p = r.lookup_plan(l, ids)
+        after = r.resident()
+        keys = {l * E + int(e) for row in ids for e in row}
+        assert len(p.hits) + p.m == len(keys)
+        assert all(l * E + e in before for e, _ in p.hits)
+        assert all(l * E + e not in before for e in p.host)
+        assert all(after.get(l * E + e) == s for e, s in p.fills)
+        assert all(l * E + e not in after for e in p.host)
+        assert len(after) <= C and len(set(r.slot_key) - {-1}) == len(after)
+        assert p.q_fill == min(p.q, C - len(p.hits)) and 0 <= p.credit < bh
+        # victims were the least recently used among the slots not touched now
+        untouched = [(stamps[s], key) for key, s in before.items()
+                     if key not in keys]
+        worst = sorted(untouched)[:len(p.evicted)]
+        assert sorted(p.evicted) == sorted(kk for _, kk in worst)
+
+
+def test_matches_ordered_list_lru_when_every_miss_fills():
+    L, E, k, C = 4, 16, 4, 10
+    r = Residency(C, L, E, 7, 7)
+    last_use = {}
+    for n, (l, ids) in enumerate(_random_calls(7, 400, L, E, k), start=1):
+        r.lookup_plan(l, ids)
+        for e in ids[0]:
+            last_use[l * E + int(e)] = n
+        top = sorted(last_use, key=lambda key: (last_use[key], key), reverse=True)[:C]
+        assert set(r.resident()) == set(top)
+
+
+def test_mattson_inclusion():
+    L, E, k = 4, 16, 4
+    calls = _random_calls(9, 300, L, E, k)
+    misses, sets = [], []
+    for C in range(k, 40):
+        r = Residency(C, L, E, 5, 5)
+        tot = 0
+        for l, ids in calls:
+            tot += r.lookup_plan(l, ids).m
+        misses.append(tot)
+        sets.append(set(r.resident()))
+    assert all(a >= b for a, b in zip(misses, misses[1:]))
+    assert all(a <= b for a, b in zip(sets, sets[1:]))
+
+
+def test_full_capacity_gives_compulsory_misses_only():
+    L, E, k = 3, 8, 3
+    calls = _random_calls(11, 150, L, E, k)
+    r = Residency(L * E, L, E, 3, 3)
+    seen, tot = set(), 0
+    for l, ids in calls:
+        tot += r.lookup_plan(l, ids).m
+        seen |= {l * E + int(e) for e in ids[0]}
+    assert tot == len(seen)
+
+
+@pytest.mark.parametrize("bp,bh", [(11800, 47500), (9, 10), (1, 3), (123, 124)])
+def test_q_closed_form(bp, bh):
+    rng = np.random.default_rng(bp)
+    r = Residency(8, 500, 8, bp, bh)  # q does not depend on capacity
+    ms, qs = [], []
+    for n in range(500):
+        m = int(rng.integers(0, 9))
+        p = r.lookup_plan(n, [list(range(m))] if m else [[]])
+        ms.append(m)
+        qs.append(p.q)
+        assert p.q in (m * bp // bh, -(-m * bp // bh))
+    assert sum(qs) == (sum(ms) * bp) // bh
+
+
+def test_equal_bandwidths_fill_every_miss():
+    r = Residency(64, 1000, 8, 50, 50)
+    for n in range(100):
+        p = r.lookup_plan(n, [[0, 1, 2]])
+        assert p.q == p.q_fill == 3 and p.host == []
+
+
+def test_page_worked_splits(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "q_split_pages.json")))
+    lap = g["laptop_lpddr5"]
+    bp, bh = int(lap["B_P_GBps"] * 1000), int(lap["B_H_GBps"] * 1000)
+    trace = synth.sticky_zipf_trace(0, 200, 4, 32, 4)
+    r = Residency(16, 4, 32, bp, bh)
+    m = q = 0
+    for s in range(trace.shape[0]):
+        for l in range(4):
+            p = r.lookup_plan(l, [trace[s, l]])
+            m, q = m + p.m, q + p.q
+    assert abs((m - q) / m - lap["host_share_about"]) < 0.02
+    desk = g["desktop_ddr5"]
+    r = Residency(16, 4, 32, 900, 1000)  # B_P slightly below B_H
+    m = q = 0
+    for s in range(trace.shape[0]):
+        for l in range(4):
+            p = r.lookup_plan(l, [trace[s, l]])
+            m, q = m + p.m, q + p.q
+    assert abs(q / m - desk["fill_share_about"]) < 0.02
+
+
+def test_capacity_below_k_overflows_to_host():
+    r = Residency(2, 1, 8, 1, 1)
+    p = r.lookup_plan(0, [[0, 1, 2, 3]])
+    assert p.q == 4 and p.q_fill == 2 and p.fills == [(0, 0), (1, 1)] and p.host == [2, 3]

@@ -1,0 +1,997 @@
+// Engine and C ABI: the MoE expert-layer forward over a device-resident global
+// LRU expert cache backed by a pinned host expert pool (FreeToken; zhichai.net
+// article, section 2: Prefill, Decode and LRU paragraphs).
+//
+// Per layer call: route -> lookup/plan (device) -> the host reads the plan from
+// mapped memory -> fills on the copy stream (SDMA, host->device) -> device FFN
+// on the hits and fills -> host-core FFN on the host list, overlapped with the
+// device -> combine. Prefill streams whole layers into two staging buffers.
+#include <algorithm>
+#include <chrono>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include <immintrin.h>
+
+#include "eo_internal.h"
+
+namespace eo {
+int plan_max_slots();
+}
+
+using namespace eo;
+
+namespace {
+
+thread_local std::string g_err;
+
+eo_status fail(eo_status s, const std::string& msg) {
+    g_err = msg;
+    return s;
+}
+
+#define HIPCHK(expr)                                                                       \
+    do {                                                                                   \
+        hipError_t e_ = (expr);                                                            \
+        if (e_ != hipSuccess)                                                              \
+            return fail(EO_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_));   \
+    } while (0)
+
+#define EOCHK(expr)                          \
+    do {                                     \
+        eo_status s_ = (expr);               \
+        if (s_ != EO_OK) return s_;          \
+    } while (0)
+
+uint64_t round_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+struct TimedPair {
+    hipEvent_t a, b;
+};
+
+}  // namespace
+
+namespace eo {
+
+Layout layout_of(int H, int I, int fmt) {
+    Layout l;
+    const uint64_t n13 = 2ull * I * H, n2 = (uint64_t)H * I;
+    switch (fmt) {
+    case EO_W_FP32: l.d13 = 0; l.d2 = 4 * n13; l.s13 = l.s2 = l.gl = l.bytes = 4 * (n13 + n2); break;
+    case EO_W_BF16: l.d13 = 0; l.d2 = 2 * n13; l.s13 = l.s2 = l.gl = l.bytes = 2 * (n13 + n2); break;
+    case EO_W_MXFP4:
+        l.d13 = 0; l.d2 = n13 / 2; l.s13 = l.d2 + n2 / 2; l.s2 = l.s13 + n13 / 32;
+        l.gl = l.bytes = l.s2 + n2 / 32; break;
+    case EO_W_NVFP4:
+        l.d13 = 0; l.d2 = n13 / 2; l.s13 = l.d2 + n2 / 2; l.s2 = l.s13 + n13 / 16;
+        l.gl = l.s2 + n2 / 16; l.bytes = l.gl + 12; break;
+    case EO_W_FP8:
+        l.d13 = 0; l.d2 = n13; l.s13 = l.d2 + n2; l.s2 = l.s13 + 4 * 2ull * I;
+        l.gl = l.bytes = l.s2 + 4ull * H; break;
+    default: break;
+    }
+    return l;
+}
+
+}  // namespace eo
+
+struct eo_engine {
+    eo_config cfg{};
+    Layout lay;
+    uint64_t S = 0, S_pad = 0;
+    int L = 0, E = 0, k = 0, H = 0, I = 0, shared = 0, fmt = 0, act_bf16 = 0;
+    int64_t C = 0;
+    int act_size = 4;
+
+    std::vector<uint8_t*> pool;  // per layer, E * S_pad pinned bytes
+    uint8_t* d_slots = nullptr;
+    uint8_t* d_shared = nullptr;
+    float* d_router = nullptr;
+    int32_t* d_slot_key = nullptr;
+    int64_t* d_slot_stamp = nullptr;
+    int32_t* d_key2slot = nullptr;
+    DevState* d_state = nullptr;
+    DevPlan* d_plan = nullptr;
+    DevPlan* h_plan = nullptr;  // mapped, coherent
+    DevPlan* h_plan_dev = nullptr;
+    int32_t* h_ids = nullptr;
+    int32_t* h_ids_dev = nullptr;
+    float* h_w = nullptr;
+    float* h_w_dev = nullptr;
+    uint8_t* h_x = nullptr;
+    uint8_t* h_x_dev = nullptr;
+
+    int32_t* d_ids = nullptr;
+    float* d_w = nullptr;
+    float* d_z = nullptr;
+    float* d_y = nullptr;
+    float* d_hgemv = nullptr;
+    float* d_yparts = nullptr;
+    float* d_yhost = nullptr;
+    float* h_yhost = nullptr;
+    std::vector<float> xf;  // host fp32 copy of x for the host routine
+    std::vector<float> host_scratch;
+
+    // grouped-FFN buffers, sized for gemm_T tokens
+    int gemm_T = 0;
+    PermuteBufs pb{};
+    void* d_hbuf = nullptr;
+    float* d_opairs = nullptr;
+
+    uint8_t* d_staging[2] = {nullptr, nullptr};
+    hipStream_t copy_stream = nullptr;
+    hipEvent_t ev_fill = nullptr, ev_copy[2] = {nullptr, nullptr}, ev_comp[2] = {nullptr, nullptr};
+    hipEvent_t ev_start = nullptr;
+
+    ThreadPool* tp = nullptr;
+    uint32_t bp = 1, bh = 1;
+
+    // plan bookkeeping
+    bool plan_pending = false, plan_ready = false, host_staged = false, mirrored = false;
+    int plan_seq = 0, plan_layer = -1, plan_T = 0;
+    eo_plan_host last_plan{};
+
+    eo_stats stats{};
+
+    bool timing = false;
+    std::vector<TimedPair> gemv_ev, gemm_ev, free_ev;
+    double gemv_ms = 0, gemm_ms = 0;
+    int64_t gemv_n = 0, gemm_n = 0;
+
+    void* cap_x = nullptr;
+    float* cap_y = nullptr;
+    int32_t* cap_ids = nullptr;
+    float* cap_w = nullptr;
+    int cap_T = 0;
+};
+
+namespace {
+
+eo_status get_pair(eo_engine* e, TimedPair* p) {
+    if (!e->free_ev.empty()) {
+        *p = e->free_ev.back();
+        e->free_ev.pop_back();
+        return EO_OK;
+    }
+    HIPCHK(hipEventCreate(&p->a));
+    HIPCHK(hipEventCreate(&p->b));
+    return EO_OK;
+}
+
+eo_status harvest_times(eo_engine* e) {
+    for (auto* v : {&e->gemv_ev, &e->gemm_ev}) {
+        for (auto& p : *v) {
+            HIPCHK(hipEventSynchronize(p.b));
+            float ms = 0;
+            HIPCHK(hipEventElapsedTime(&ms, p.a, p.b));
+            if (v == &e->gemv_ev) {
+                e->gemv_ms += ms;
+                e->gemv_n += 1;
+            } else {
+                e->gemm_ms += ms;
+                e->gemm_n += 1;
+            }
+            e->free_ev.push_back(p);
+        }
+        v->clear();
+    }
+    return EO_OK;
+}
+
+eo_status check_layer(eo_engine* e, int layer) {
+    if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
+    if (layer < 0 || layer >= e->L) return fail(EO_ERR_INVALID_ARG, "layer out of range");
+    return EO_OK;
+}
+
+eo_status check_T(eo_engine* e, int T) {
+    if (T < 1 || T > e->cfg.max_tokens) return fail(EO_ERR_INVALID_ARG, "T out of range [1, max_tokens]");
+    return EO_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Grow the grouped-FFN buffers to hold T tokens.
+eo_status ensure_gemm(eo_engine* e, int T, hipStream_t s) {
+    if (T <= e->gemm_T) return EO_OK;
+    HIPCHK(hipStreamSynchronize(s));
+    auto fr = [](void* p) { if (p) (void)hipFree(p); };
+    fr(e->pb.counts); fr(e->pb.offsets); fr(e->pb.tile_off); fr(e->pb.perm_pair);
+    fr(e->pb.chunk_cnt); fr(e->pb.x_perm); fr(e->d_hbuf); fr(e->d_opairs);
+    e->pb = PermuteBufs{};
+    e->d_hbuf = nullptr;
+    e->d_opairs = nullptr;
+    e->gemm_T = 0;
+    const size_t P = (size_t)T * e->k + T;
+    const size_t nchunks = ((size_t)T * e->k + 1023) / 1024 + 1;
+    HIPCHK(hipMalloc(&e->pb.counts, sizeof(int32_t) * (e->E + 2)));
+    HIPCHK(hipMalloc(&e->pb.offsets, sizeof(int32_t) * (e->E + 2)));
+    HIPCHK(hipMalloc(&e->pb.tile_off, sizeof(int32_t) * (e->E + 2)));
+    HIPCHK(hipMalloc(&e->pb.perm_pair, sizeof(int32_t) * P));
+    HIPCHK(hipMalloc(&e->pb.chunk_cnt, sizeof(int32_t) * nchunks * e->E));
+    HIPCHK(hipMalloc(&e->pb.x_perm, (size_t)e->act_size * P * e->H));
+    HIPCHK(hipMalloc(&e->d_hbuf, sizeof(float) * P * e->I));
+    HIPCHK(hipMalloc(&e->d_opairs, sizeof(float) * P * e->H));
+    e->gemm_T = T;
+    return EO_OK;
+}
+
+// Spin on the mapped plan mirror until the device has written this call's plan.
+eo_status wait_plan(eo_engine* e) {
+    if (!e->plan_pending) return fail(EO_ERR_STATE, "no pending plan (call eo_lookup_plan first)");
+    if (e->plan_ready) return EO_OK;
+    auto t0 = std::chrono::steady_clock::now();
+    uint64_t spins = 0;
+    while (__atomic_load_n(&e->h_plan->seq, __ATOMIC_ACQUIRE) != e->plan_seq) {
+        _mm_pause();
+        if ((++spins & 0xFFFF) == 0) {
+            hipError_t he = hipGetLastError();
+            if (he != hipSuccess) {
+                e->plan_pending = false;
+                return fail(EO_ERR_HIP, std::string("device error while waiting for plan: ") +
+                                            hipGetErrorString(he));
+            }
+            if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(60)) {
+                e->plan_pending = false;
+                return fail(EO_ERR_HIP, "timed out waiting for the device plan");
+            }
+        }
+    }
+    const DevPlan* hp = e->h_plan;
+    if (hp->pad != 0) {
+        e->plan_pending = false;
+        return fail(EO_ERR_INVALID_ARG, hp->pad == 1 ? "expert id out of range in ids"
+                                                     : "expert id repeated within a token");
+    }
+    eo_plan_host& p = e->last_plan;
+    p.layer = hp->layer;
+    p.m = hp->m;
+    p.q = hp->q;
+    p.q_fill = hp->q_fill;
+    p.n_hit = hp->n_hit;
+    p.n_host = hp->n_host;
+    p.n_evict = hp->n_evict;
+    p.clock = hp->clock;
+    p.credit = hp->credit;
+    std::memcpy(p.hit_expert, hp->hit_e, sizeof(int32_t) * p.n_hit);
+    std::memcpy(p.hit_slot, hp->hit_slot, sizeof(int32_t) * p.n_hit);
+    std::memcpy(p.fill_expert, hp->fill_e, sizeof(int32_t) * p.q_fill);
+    std::memcpy(p.fill_slot, hp->fill_slot, sizeof(int32_t) * p.q_fill);
+    std::memcpy(p.host_expert, hp->host_e, sizeof(int32_t) * p.n_host);
+    std::memcpy(p.evicted_key, hp->evict_key, sizeof(int32_t) * p.n_evict);
+    e->stats.lookups += 1;
+    e->stats.hits += p.n_hit;
+    e->stats.misses += p.m;
+    e->plan_ready = true;
+    return EO_OK;
+}
+
+eo_status do_plan(eo_engine* e, int layer, const int32_t* ids, const float* w, const void* x,
+                  int T, hipStream_t s) {
+    const size_t xb = (size_t)T * e->H * e->act_size;
+    hipError_t he = launch_plan(layer, ids, w ? w : nullptr, x, xb, T, e->k, e->E, e->C,
+                                e->d_slot_key, e->d_slot_stamp, e->d_key2slot, e->d_state,
+                                e->d_plan, e->h_plan_dev, w ? e->h_ids_dev : nullptr,
+                                w ? e->h_w_dev : nullptr, x ? e->h_x_dev : nullptr, s);
+    if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("plan launch: ") + hipGetErrorString(he));
+    e->plan_seq += 1;
+    e->plan_pending = true;
+    e->plan_ready = false;
+    e->host_staged = false;
+    e->mirrored = (w != nullptr && x != nullptr);
+    e->plan_layer = layer;
+    e->plan_T = T;
+    return EO_OK;
+}
+
+eo_status do_fill(eo_engine* e, hipStream_t s) {
+    EOCHK(wait_plan(e));
+    const eo_plan_host& p = e->last_plan;
+    if (p.q_fill == 0) return EO_OK;
+    uint8_t* base = e->pool[p.layer];
+    for (int r = 0; r < p.q_fill; ++r) {
+        HIPCHK(hipMemcpyAsync(e->d_slots + (uint64_t)p.fill_slot[r] * e->S_pad,
+                              base + (uint64_t)p.fill_expert[r] * e->S_pad, e->S,
+                              hipMemcpyHostToDevice, e->copy_stream));
+    }
+    HIPCHK(hipEventRecord(e->ev_fill, e->copy_stream));
+    HIPCHK(hipStreamWaitEvent(s, e->ev_fill, 0));
+    e->stats.fills += p.q_fill;
+    e->stats.pcie_bytes += (int64_t)p.q_fill * (int64_t)e->S;
+    return EO_OK;
+}
+
+eo_status do_host(eo_engine* e, const void* x, const int32_t* ids, const float* w, hipStream_t s) {
+    EOCHK(wait_plan(e));
+    const eo_plan_host& p = e->last_plan;
+    if (p.n_host == 0) return EO_OK;
+    const int T = e->plan_T, k = e->k, H = e->H;
+    const int32_t* hids;
+    const float* hw;
+    const uint8_t* hx;
+    if (e->mirrored) {
+        hids = e->h_ids;
+        hw = e->h_w;
+        hx = e->h_x;
+    } else {
+        HIPCHK(hipMemcpyAsync(e->h_ids, ids, sizeof(int32_t) * T * k, hipMemcpyDeviceToHost, s));
+        HIPCHK(hipMemcpyAsync(e->h_w, w, sizeof(float) * T * k, hipMemcpyDeviceToHost, s));
+        HIPCHK(hipMemcpyAsync(e->h_x, x, (size_t)T * H * e->act_size, hipMemcpyDeviceToHost, s));
+        HIPCHK(hipStreamSynchronize(s));
+        hids = e->h_ids;
+        hw = e->h_w;
+        hx = e->h_x;
+    }
+    e->xf.resize((size_t)T * H);
+    if (e->act_bf16) {
+        const uint16_t* xb = (const uint16_t*)hx;
+        for (size_t i = 0; i < (size_t)T * H; ++i) {
+            uint32_t u = (uint32_t)xb[i] << 16;
+            std::memcpy(&e->xf[i], &u, 4);
+        }
+    } else {
+        std::memcpy(e->xf.data(), hx, sizeof(float) * T * H);
+    }
+    std::vector<const uint8_t*> table(e->E, nullptr);
+    for (int i = 0; i < p.n_host; ++i)
+        table[p.host_expert[i]] = e->pool[p.layer] + (uint64_t)p.host_expert[i] * e->S_pad;
+    std::memset(e->h_yhost, 0, sizeof(float) * T * H);
+    HostJob jb;
+    jb.fmt = e->fmt;
+    jb.lay = e->lay;
+    jb.H = H;
+    jb.I = e->I;
+    jb.T = T;
+    jb.k = k;
+    jb.x = e->xf.data();
+    jb.ids = hids;
+    jb.w = hw;
+    jb.experts = table.data();
+    jb.y = e->h_yhost;
+    host_ffn(e->tp, jb, e->host_scratch);
+    HIPCHK(hipMemcpyAsync(e->d_yhost, e->h_yhost, sizeof(float) * T * H, hipMemcpyHostToDevice, s));
+    e->host_staged = true;
+    e->stats.host_experts += p.n_host;
+    e->stats.host_bytes += (int64_t)p.n_host * (int64_t)e->S;
+    return EO_OK;
+}
+
+GroupW slots_gw(eo_engine* e, int layer) {
+    GroupW gw;
+    gw.slots = e->d_slots;
+    gw.e2slot = e->d_plan->e2slot;
+    gw.stride = e->S_pad;
+    gw.shared_w = e->shared ? e->d_shared + (uint64_t)layer * e->S_pad : nullptr;
+    return gw;
+}
+
+// Device FFN part for the current plan; T == 1 uses the GEMV path.
+eo_status do_ffn_device(eo_engine* e, int layer, const void* x, const int32_t* ids, const float* w,
+                        hipStream_t s) {
+    const int T = e->plan_T;
+    GroupW gw = slots_gw(e, layer);
+    TimedPair tpair{};
+    if (e->timing) EOCHK(get_pair(e, &tpair));
+    hipError_t he;
+    if (T == 1) {
+        he = launch_ffn_gemv(e->fmt, e->lay, gw, e->d_plan, ids, w, e->k, e->E, e->shared, e->H,
+                             e->I, x, e->act_bf16, e->d_hgemv, e->d_yparts, s,
+                             e->timing ? tpair.a : nullptr, e->timing ? tpair.b : nullptr);
+        if (e->timing) e->gemv_ev.push_back(tpair);
+    } else {
+        EOCHK(ensure_gemm(e, T, s));
+        he = launch_permute(ids, e->d_plan->e2slot, 0, T, e->k, e->E, e->shared, x, e->act_bf16,
+                            e->H, e->pb, s);
+        if (he == hipSuccess) {
+            if (e->timing) HIPCHK(hipEventRecord(tpair.a, s));
+            he = launch_ffn_gemm(e->fmt, e->lay, gw, e->E, e->shared, e->H, e->I,
+                                 T * e->k + T, e->pb.offsets, e->pb.tile_off, e->pb.x_perm,
+                                 e->d_hbuf, e->pb.perm_pair, ids, w, e->k, T, e->d_opairs, s);
+            if (e->timing) {
+                HIPCHK(hipEventRecord(tpair.b, s));
+                e->gemm_ev.push_back(tpair);
+            }
+        }
+    }
+    if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("ffn launch: ") + hipGetErrorString(he));
+    return EO_OK;
+}
+
+eo_status do_combine(eo_engine* e, const int32_t* ids, float* y, void* x_res, hipStream_t s) {
+    const int T = e->plan_T;
+    const float* yh = e->host_staged ? e->d_yhost : nullptr;
+    hipError_t he;
+    if (T == 1)
+        he = launch_gemv_reduce(e->d_yparts, e->k + e->shared, yh, e->H, y, x_res, e->act_bf16, s);
+    else
+        he = launch_combine(e->d_opairs, ids, e->d_plan->e2slot, 0, e->shared, yh, T, e->k, e->H,
+                            y, x_res, e->act_bf16, s, e->E);
+    if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("combine: ") + hipGetErrorString(he));
+    e->plan_pending = false;
+    e->plan_ready = false;
+    e->host_staged = false;
+    return EO_OK;
+}
+
+// One full layer through the cache. x_res != null applies the residual in place.
+eo_status moe_layer_impl(eo_engine* e, int layer, const void* x, float* y, int T,
+                         const int32_t* forced, int32_t* ids, float* w, void* x_res,
+                         hipStream_t s) {
+    hipError_t he = launch_route(x, e->act_bf16, e->d_router + (size_t)layer * e->E * e->H, T,
+                                 e->E, e->H, e->k, forced, ids, w, e->d_z, s);
+    if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("route: ") + hipGetErrorString(he));
+    EOCHK(do_plan(e, layer, ids, w, x, T, s));
+    EOCHK(do_fill(e, s));
+    EOCHK(do_ffn_device(e, layer, x, ids, w, s));
+    EOCHK(do_host(e, x, ids, w, s));
+    return do_combine(e, ids, y, x_res, s);
+}
+
+eo_status reset_cache(eo_engine* e) {
+    if (e->C > 0) {
+        std::vector<int32_t> keys(e->C, -1);
+        HIPCHK(hipMemcpy(e->d_slot_key, keys.data(), sizeof(int32_t) * e->C, hipMemcpyHostToDevice));
+        HIPCHK(hipMemset(e->d_slot_stamp, 0, sizeof(int64_t) * e->C));
+    }
+    std::vector<int32_t> k2s((size_t)e->L * e->E, -1);
+    HIPCHK(hipMemcpy(e->d_key2slot, k2s.data(), sizeof(int32_t) * k2s.size(), hipMemcpyHostToDevice));
+    DevState st{};
+    HIPCHK(hipMemcpy(&st, e->d_state, sizeof(DevState), hipMemcpyDeviceToHost));
+    st.clock = 0;
+    st.credit = 0;
+    st.bp = (int32_t)e->bp;
+    st.bh = (int32_t)e->bh;
+    HIPCHK(hipMemcpy(e->d_state, &st, sizeof(DevState), hipMemcpyHostToDevice));
+    return EO_OK;
+}
+
+void destroy_all(eo_engine* e) {
+    if (!e) return;
+    (void)hipSetDevice(e->cfg.device);
+    (void)hipDeviceSynchronize();
+    for (auto p : e->pool)
+        if (p) (void)hipHostFree(p);
+    auto fr = [](void* p) { if (p) (void)hipFree(p); };
+    auto fh = [](void* p) { if (p) (void)hipHostFree(p); };
+    fr(e->d_slots); fr(e->d_shared); fr(e->d_router); fr(e->d_slot_key); fr(e->d_slot_stamp);
+    fr(e->d_key2slot); fr(e->d_state); fr(e->d_plan); fr(e->d_ids); fr(e->d_w); fr(e->d_z);
+    fr(e->d_y); fr(e->d_hgemv); fr(e->d_yparts); fr(e->d_yhost);
+    fr(e->pb.counts); fr(e->pb.offsets); fr(e->pb.tile_off); fr(e->pb.perm_pair);
+    fr(e->pb.chunk_cnt); fr(e->pb.x_perm); fr(e->d_hbuf); fr(e->d_opairs);
+    fr(e->d_staging[0]); fr(e->d_staging[1]);
+    fh(e->h_plan); fh(e->h_ids); fh(e->h_w); fh(e->h_x); fh(e->h_yhost);
+    if (e->copy_stream) (void)hipStreamDestroy(e->copy_stream);
+    for (hipEvent_t ev : {e->ev_fill, e->ev_copy[0], e->ev_copy[1], e->ev_comp[0], e->ev_comp[1],
+                          e->ev_start})
+        if (ev) (void)hipEventDestroy(ev);
+    for (auto* v : {&e->gemv_ev, &e->gemm_ev, &e->free_ev})
+        for (auto& p : *v) {
+            (void)hipEventDestroy(p.a);
+            (void)hipEventDestroy(p.b);
+        }
+    if (e->tp) threadpool_destroy(e->tp);
+    delete e;
+}
+
+template <typename T>
+eo_status dmalloc(T** p, size_t bytes) {
+    if (bytes == 0) bytes = 16;
+    hipError_t he = hipMalloc((void**)p, bytes);
+    if (he != hipSuccess) {
+        *p = nullptr;
+        (void)hipGetLastError();
+        return fail(he == hipErrorOutOfMemory ? EO_ERR_OOM : EO_ERR_HIP,
+                    std::string("hipMalloc: ") + hipGetErrorString(he));
+    }
+    return EO_OK;
+}
+
+template <typename T>
+eo_status hmalloc(T** p, size_t bytes, unsigned flags) {
+    if (bytes == 0) bytes = 16;
+    hipError_t he = hipHostMalloc((void**)p, bytes, flags);
+    if (he != hipSuccess) {
+        *p = nullptr;
+        (void)hipGetLastError();
+        return fail(EO_ERR_OOM, std::string("hipHostMalloc: ") + hipGetErrorString(he));
+    }
+    return EO_OK;
+}
+
+eo_status create_impl(const eo_config* cfg, eo_engine* e) {
+    e->cfg = *cfg;
+    e->L = cfg->layers;
+    e->E = cfg->experts;
+    e->k = cfg->top_k;
+    e->H = cfg->hidden;
+    e->I = cfg->inter;
+    e->shared = cfg->shared_experts;
+    e->fmt = cfg->wfmt;
+    e->act_bf16 = cfg->act_bf16;
+    e->C = cfg->cache_slots;
+    e->act_size = e->act_bf16 ? 2 : 4;
+    e->lay = layout_of(e->H, e->I, e->fmt);
+    e->S = e->lay.bytes;
+    e->S_pad = round_up(e->S, kPoolAlign);
+    HIPCHK(hipSetDevice(cfg->device));
+
+    e->pool.assign(e->L, nullptr);
+    for (int l = 0; l < e->L; ++l) EOCHK(hmalloc(&e->pool[l], e->E * e->S_pad, hipHostMallocDefault));
+    EOCHK(dmalloc(&e->d_slots, e->C * e->S_pad));
+    if (e->shared) {
+        EOCHK(dmalloc(&e->d_shared, (size_t)e->L * e->S_pad));
+        HIPCHK(hipMemset(e->d_shared, 0, (size_t)e->L * e->S_pad));
+    }
+    EOCHK(dmalloc(&e->d_router, sizeof(float) * e->L * e->E * e->H));
+    HIPCHK(hipMemset(e->d_router, 0, sizeof(float) * e->L * e->E * e->H));
+    EOCHK(dmalloc(&e->d_slot_key, sizeof(int32_t) * e->C));
+    EOCHK(dmalloc(&e->d_slot_stamp, sizeof(int64_t) * e->C));
+    EOCHK(dmalloc(&e->d_key2slot, sizeof(int32_t) * e->L * e->E));
+    EOCHK(dmalloc(&e->d_state, sizeof(DevState)));
+    HIPCHK(hipMemset(e->d_state, 0, sizeof(DevState)));
+    EOCHK(dmalloc(&e->d_plan, sizeof(DevPlan)));
+    HIPCHK(hipMemset(e->d_plan, 0, sizeof(DevPlan)));
+    const unsigned mflags = hipHostMallocMapped | hipHostMallocCoherent;
+    const int Tm = cfg->max_tokens;
+    EOCHK(hmalloc(&e->h_plan, sizeof(DevPlan), mflags));
+    std::memset(e->h_plan, 0, sizeof(DevPlan));
+    EOCHK(hmalloc(&e->h_ids, sizeof(int32_t) * Tm * e->k, mflags));
+    EOCHK(hmalloc(&e->h_w, sizeof(float) * Tm * e->k, mflags));
+    EOCHK(hmalloc(&e->h_x, (size_t)e->act_size * Tm * e->H, mflags));
+    HIPCHK(hipHostGetDevicePointer((void**)&e->h_plan_dev, e->h_plan, 0));
+    HIPCHK(hipHostGetDevicePointer((void**)&e->h_ids_dev, e->h_ids, 0));
+    HIPCHK(hipHostGetDevicePointer((void**)&e->h_w_dev, e->h_w, 0));
+    HIPCHK(hipHostGetDevicePointer((void**)&e->h_x_dev, e->h_x, 0));
+    EOCHK(dmalloc(&e->d_ids, sizeof(int32_t) * Tm * e->k));
+    EOCHK(dmalloc(&e->d_w, sizeof(float) * Tm * e->k));
+    EOCHK(dmalloc(&e->d_z, sizeof(float) * Tm * e->E));
+    EOCHK(dmalloc(&e->d_y, sizeof(float) * Tm * e->H));
+    EOCHK(dmalloc(&e->d_hgemv, sizeof(float) * (e->k + 1) * e->I));
+    EOCHK(dmalloc(&e->d_yparts, sizeof(float) * (e->k + 1) * e->H));
+    EOCHK(dmalloc(&e->d_yhost, sizeof(float) * Tm * e->H));
+    EOCHK(hmalloc(&e->h_yhost, sizeof(float) * Tm * e->H, hipHostMallocDefault));
+    HIPCHK(hipStreamCreateWithFlags(&e->copy_stream, hipStreamNonBlocking));
+    HIPCHK(hipEventCreateWithFlags(&e->ev_fill, hipEventDisableTiming));
+    HIPCHK(hipEventCreateWithFlags(&e->ev_start, hipEventDisableTiming));
+    for (int i = 0; i < 2; ++i) {
+        HIPCHK(hipEventCreateWithFlags(&e->ev_copy[i], hipEventDisableTiming));
+        HIPCHK(hipEventCreateWithFlags(&e->ev_comp[i], hipEventDisableTiming));
+    }
+    int nt = cfg->host_threads;
+    if (nt <= 0) nt = std::min(16, (int)std::max(1u, std::thread::hardware_concurrency()));
+    e->tp = threadpool_create(nt);
+    e->bp = e->bh = 1;
+    EOCHK(reset_cache(e));
+    HIPCHK(hipDeviceSynchronize());
+    return EO_OK;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+extern "C" {
+
+const char* eo_last_error(void) { return g_err.c_str(); }
+
+uint64_t eo_expert_bytes(int32_t hidden, int32_t inter, int32_t wfmt) {
+    if (hidden <= 0 || inter <= 0 || wfmt < 0 || wfmt > 4) return 0;
+    return layout_of(hidden, inter, wfmt).bytes;
+}
+
+eo_status eo_create(const eo_config* cfg, eo_engine** out) {
+    if (!cfg || !out) return fail(EO_ERR_INVALID_ARG, "null argument");
+    *out = nullptr;
+    const eo_config& c = *cfg;
+    if (c.layers < 1 || c.experts < 1 || c.experts > EO_MAX_EXPERTS || c.top_k < 1 ||
+        c.top_k > kMaxK || c.top_k > c.experts)
+        return fail(EO_ERR_INVALID_ARG, "layers >= 1, 1 <= experts <= 1024, 1 <= top_k <= min(16, experts)");
+    if (c.hidden < 128 || c.hidden % 128 || c.inter < 64 || c.inter % 64)
+        return fail(EO_ERR_INVALID_ARG, "hidden must be a multiple of 128, inter a multiple of 64");
+    if (c.shared_experts != 0 && c.shared_experts != 1)
+        return fail(EO_ERR_INVALID_ARG, "shared_experts must be 0 or 1");
+    if (c.wfmt < EO_W_FP32 || c.wfmt > EO_W_FP8) return fail(EO_ERR_INVALID_ARG, "unknown wfmt");
+    if ((c.wfmt == EO_W_FP32) != (c.act_bf16 == 0))
+        return fail(EO_ERR_UNSUPPORTED, "fp32 weights need fp32 activations; other formats need bf16 activations");
+    if (c.cache_slots < 0 || c.cache_slots > plan_max_slots())
+        return fail(EO_ERR_INVALID_ARG, "cache_slots out of range [0, 8192]");
+    if ((int64_t)c.layers * c.experts >= (1 << 24))
+        return fail(EO_ERR_INVALID_ARG, "layers * experts must be below 2^24");
+    if (c.max_tokens < 1) return fail(EO_ERR_INVALID_ARG, "max_tokens >= 1");
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || c.device < 0 || c.device >= ndev)
+        return fail(EO_ERR_INVALID_ARG, "no such HIP device");
+    eo_engine* e = new eo_engine();
+    eo_status s = create_impl(cfg, e);
+    if (s != EO_OK) {
+        std::string msg = g_err;
+        destroy_all(e);
+        g_err = msg;
+        return s;
+    }
+    *out = e;
+    return EO_OK;
+}
+
+eo_status eo_destroy(eo_engine* e) {
+    destroy_all(e);
+    return EO_OK;
+}
+
+eo_status eo_pool_expert(eo_engine* e, int32_t layer, int32_t expert, void** host_ptr,
+                         uint64_t* bytes) {
+    EOCHK(check_layer(e, layer));
+    if (expert < 0 || expert >= e->E || !host_ptr) return fail(EO_ERR_INVALID_ARG, "bad expert");
+    *host_ptr = e->pool[layer] + (uint64_t)expert * e->S_pad;
+    if (bytes) *bytes = e->S;
+    return EO_OK;
+}
+
+eo_status eo_set_shared_expert(eo_engine* e, int32_t layer, const void* host_block, uint64_t bytes) {
+    EOCHK(check_layer(e, layer));
+    if (!e->shared) return fail(EO_ERR_STATE, "engine has no shared expert");
+    if (!host_block || bytes != e->S) return fail(EO_ERR_INVALID_ARG, "block size mismatch");
+    HIPCHK(hipSetDevice(e->cfg.device));
+    HIPCHK(hipMemcpy(e->d_shared + (uint64_t)layer * e->S_pad, host_block, bytes, hipMemcpyHostToDevice));
+    return EO_OK;
+}
+
+eo_status eo_set_router(eo_engine* e, int32_t layer, const float* host_w) {
+    EOCHK(check_layer(e, layer));
+    if (!host_w) return fail(EO_ERR_INVALID_ARG, "null router");
+    HIPCHK(hipSetDevice(e->cfg.device));
+    HIPCHK(hipMemcpy(e->d_router + (size_t)layer * e->E * e->H, host_w,
+                     sizeof(float) * e->E * e->H, hipMemcpyHostToDevice));
+    return EO_OK;
+}
+
+eo_status eo_set_bandwidth(eo_engine* e, uint32_t bp_mbps, uint32_t bh_mbps) {
+    if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
+    if (bp_mbps == 0 || bh_mbps == 0 || bp_mbps > 0x7FFFFFFFu || bh_mbps > 0x7FFFFFFFu)
+        return fail(EO_ERR_INVALID_ARG, "bandwidths must be in [1, 2^31)");
+    HIPCHK(hipSetDevice(e->cfg.device));
+    HIPCHK(hipDeviceSynchronize());
+    DevState st{};
+    HIPCHK(hipMemcpy(&st, e->d_state, sizeof(DevState), hipMemcpyDeviceToHost));
+    st.bp = (int32_t)bp_mbps;
+    st.bh = (int32_t)bh_mbps;
+    if (st.credit > (int64_t)bh_mbps - 1) st.credit = (int64_t)bh_mbps - 1;
+    HIPCHK(hipMemcpy(e->d_state, &st, sizeof(DevState), hipMemcpyHostToDevice));
+    e->bp = bp_mbps;
+    e->bh = bh_mbps;
+    return EO_OK;
+}
+
+eo_status eo_measure_bandwidth(eo_engine* e, uint32_t* bp_out, uint32_t* bh_out) {
+    if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
+    HIPCHK(hipSetDevice(e->cfg.device));
+    HIPCHK(hipDeviceSynchronize());
+    uint8_t* dst = e->d_slots;
+    uint8_t* tmp = nullptr;
+    if (e->C == 0) {
+        EOCHK(dmalloc(&tmp, e->S));
+        dst = tmp;
+    }
+    const int reps = 9, warm = 2;
+    const int n_exp = e->L * e->E;
+    hipEvent_t a, b;
+    HIPCHK(hipEventCreate(&a));
+    HIPCHK(hipEventCreate(&b));
+    std::vector<double> tp, th;
+    for (int r = 0; r < reps + warm; ++r) {
+        int id = (r * 7919) % n_exp;
+        const uint8_t* src = e->pool[id / e->E] + (uint64_t)(id % e->E) * e->S_pad;
+        HIPCHK(hipEventRecord(a, e->copy_stream));
+        HIPCHK(hipMemcpyAsync(dst, src, e->S, hipMemcpyHostToDevice, e->copy_stream));
+        HIPCHK(hipEventRecord(b, e->copy_stream));
+        HIPCHK(hipEventSynchronize(b));
+        float ms = 0;
+        HIPCHK(hipEventElapsedTime(&ms, a, b));
+        if (r >= warm) tp.push_back(ms * 1e-3);
+    }
+    (void)hipEventDestroy(a);
+    (void)hipEventDestroy(b);
+    if (tmp) (void)hipFree(tmp);
+    // host routine over one expert at T = 1
+    std::vector<float> x(e->H, 0.01f), y(e->H);
+    std::vector<const uint8_t*> table(e->E, nullptr);
+    int32_t ids[kMaxK];
+    float w[kMaxK];
+    for (int j = 0; j < e->k; ++j) {
+        ids[j] = j;
+        w[j] = j == 0 ? 1.0f : 0.0f;
+    }
+    for (int r = 0; r < reps + warm; ++r) {
+        int id = (r * 104729 + 17) % n_exp;
+        const int le = id % e->E;
+        std::fill(table.begin(), table.end(), nullptr);
+        // route the single token to expert `le` (slot 0), other slots to non-host experts
+        ids[0] = le;
+        for (int j = 1; j < e->k; ++j) ids[j] = (le + j) % e->E;
+        table[le] = e->pool[id / e->E] + (uint64_t)le * e->S_pad;
+        HostJob jb;
+        jb.fmt = e->fmt;
+        jb.lay = e->lay;
+        jb.H = e->H;
+        jb.I = e->I;
+        jb.T = 1;
+        jb.k = e->k;
+        jb.x = x.data();
+        jb.ids = ids;
+        jb.w = w;
+        jb.experts = table.data();
+        std::fill(y.begin(), y.end(), 0.0f);
+        jb.y = y.data();
+        auto t0 = std::chrono::steady_clock::now();
+        host_ffn(e->tp, jb, e->host_scratch);
+        double dt = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+        if (r >= warm) th.push_back(dt);
+    }
+    std::sort(tp.begin(), tp.end());
+    std::sort(th.begin(), th.end());
+    double bp = (double)e->S / tp[tp.size() / 2] / 1e6, bh = (double)e->S / th[th.size() / 2] / 1e6;
+    uint32_t bpi = (uint32_t)std::max(1.0, std::min(2e9, bp));
+    uint32_t bhi = (uint32_t)std::max(1.0, std::min(2e9, bh));
+    e->bp = bpi;
+    e->bh = bhi;
+    EOCHK(reset_cache(e));
+    if (bp_out) *bp_out = bpi;
+    if (bh_out) *bh_out = bhi;
+    return EO_OK;
+}
+
+eo_status eo_route(eo_engine* e, int32_t layer, const void* x, int32_t T, const int32_t* forced_ids,
+                   int32_t* ids, float* w, void* stream) {
+    EOCHK(check_layer(e, layer));
+    EOCHK(check_T(e, T));
+    if (!x || !ids || !w) return fail(EO_ERR_INVALID_ARG, "null pointer");
+    hipError_t he = launch_route(x, e->act_bf16, e->d_router + (size_t)layer * e->E * e->H, T, e->E,
+                                 e->H, e->k, forced_ids, ids, w, e->d_z, (hipStream_t)stream);
+    if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("route: ") + hipGetErrorString(he));
+    return EO_OK;
+}
+
+eo_status eo_lookup_plan(eo_engine* e, int32_t layer, const int32_t* ids, int32_t T, void* stream) {
+    EOCHK(check_layer(e, layer));
+    EOCHK(check_T(e, T));
+    if (!ids) return fail(EO_ERR_INVALID_ARG, "null ids");
+    return do_plan(e, layer, ids, nullptr, nullptr, T, (hipStream_t)stream);
+}
+
+eo_status eo_fill(eo_engine* e, void* stream) {
+    if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
+    return do_fill(e, (hipStream_t)stream);
+}
+
+eo_status eo_host_execute(eo_engine* e, const void* x, const int32_t* ids, const float* w,
+                          void* stream) {
+    if (!e || !x || !ids || !w) return fail(EO_ERR_INVALID_ARG, "null argument");
+    return do_host(e, x, ids, w, (hipStream_t)stream);
+}
+
+eo_status eo_expert_ffn_combine(eo_engine* e, int32_t layer, const void* x, const int32_t* ids,
+                                const float* w, float* y, void* stream) {
+    EOCHK(check_layer(e, layer));
+    if (!x || !ids || !w || !y) return fail(EO_ERR_INVALID_ARG, "null argument");
+    EOCHK(wait_plan(e));
+    if (layer != e->plan_layer) return fail(EO_ERR_STATE, "layer differs from the pending plan's");
+    if (!aligned16(x) || !aligned16(y)) return fail(EO_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    EOCHK(do_ffn_device(e, layer, x, ids, w, s));
+    return do_combine(e, ids, y, nullptr, s);
+}
+
+eo_status eo_moe_layer(eo_engine* e, int32_t layer, const void* x, float* y, int32_t T,
+                       const int32_t* forced_ids, void* stream) {
+    EOCHK(check_layer(e, layer));
+    EOCHK(check_T(e, T));
+    if (!x || !y) return fail(EO_ERR_INVALID_ARG, "null argument");
+    if (!aligned16(x) || !aligned16(y)) return fail(EO_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+    EOCHK(moe_layer_impl(e, layer, x, y, T, forced_ids, e->d_ids, e->d_w, nullptr,
+                         (hipStream_t)stream));
+    if (e->timing) EOCHK(harvest_times(e));
+    return EO_OK;
+}
+
+eo_status eo_decode_step(eo_engine* e, void* x_inout, int32_t T, const int32_t* forced_ids,
+                         void* stream) {
+    if (!e || !x_inout) return fail(EO_ERR_INVALID_ARG, "null argument");
+    EOCHK(check_T(e, T));
+    if (!aligned16(x_inout)) return fail(EO_ERR_INVALID_ARG, "x must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    const size_t xb = (size_t)T * e->H * e->act_size;
+    const bool cap = e->cap_y && T <= e->cap_T;
+    for (int l = 0; l < e->L; ++l) {
+        const int32_t* forced = forced_ids ? forced_ids + (size_t)l * T * e->k : nullptr;
+        int32_t* ids = e->d_ids;
+        float* w = e->d_w;
+        float* y = e->d_y;
+        if (cap) {
+            HIPCHK(hipMemcpyAsync((uint8_t*)e->cap_x + (size_t)l * e->cap_T * e->H * e->act_size,
+                                  x_inout, xb, hipMemcpyDeviceToDevice, s));
+            ids = e->cap_ids + (size_t)l * e->cap_T * e->k;
+            w = e->cap_w + (size_t)l * e->cap_T * e->k;
+            y = e->cap_y + (size_t)l * e->cap_T * e->H;
+        }
+        EOCHK(moe_layer_impl(e, l, x_inout, y, T, forced, ids, w, x_inout, s));
+    }
+    if (e->timing) EOCHK(harvest_times(e));
+    return EO_OK;
+}
+
+eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t double_buffer, void* stream) {
+    if (!e || !x_inout) return fail(EO_ERR_INVALID_ARG, "null argument");
+    EOCHK(check_T(e, T));
+    if (!aligned16(x_inout)) return fail(EO_ERR_INVALID_ARG, "x must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    HIPCHK(hipSetDevice(e->cfg.device));
+    const uint64_t layer_bytes = (uint64_t)e->E * e->S_pad;
+    for (int i = 0; i < 2; ++i)
+        if (!e->d_staging[i]) EOCHK(dmalloc(&e->d_staging[i], layer_bytes));
+    EOCHK(ensure_gemm(e, T, s));
+    const size_t xb = (size_t)T * e->H * e->act_size;
+    const bool cap = e->cap_y && T <= e->cap_T;
+    // the first copy must not overwrite staging still read by earlier work on s
+    HIPCHK(hipEventRecord(e->ev_start, s));
+    HIPCHK(hipStreamWaitEvent(e->copy_stream, e->ev_start, 0));
+    HIPCHK(hipMemcpyAsync(e->d_staging[0], e->pool[0], layer_bytes, hipMemcpyHostToDevice, e->copy_stream));
+    HIPCHK(hipEventRecord(e->ev_copy[0], e->copy_stream));
+    for (int l = 0; l < e->L; ++l) {
+        const int b = l & 1, nb = b ^ 1;
+        HIPCHK(hipStreamWaitEvent(s, e->ev_copy[b], 0));
+        if (double_buffer && l + 1 < e->L) {
+            // buffer nb was last read by layer l-1's compute
+            if (l >= 1) HIPCHK(hipStreamWaitEvent(e->copy_stream, e->ev_comp[nb], 0));
+            HIPCHK(hipMemcpyAsync(e->d_staging[nb], e->pool[l + 1], layer_bytes,
+                                  hipMemcpyHostToDevice, e->copy_stream));
+            HIPCHK(hipEventRecord(e->ev_copy[nb], e->copy_stream));
+        }
+        int32_t* ids = e->d_ids;
+        float* w = e->d_w;
+        float* y = nullptr;
+        if (cap) {
+            HIPCHK(hipMemcpyAsync((uint8_t*)e->cap_x + (size_t)l * e->cap_T * e->H * e->act_size,
+                                  x_inout, xb, hipMemcpyDeviceToDevice, s));
+            ids = e->cap_ids + (size_t)l * e->cap_T * e->k;
+            w = e->cap_w + (size_t)l * e->cap_T * e->k;
+            y = e->cap_y + (size_t)l * e->cap_T * e->H;
+        }
+        hipError_t he = launch_route(x_inout, e->act_bf16, e->d_router + (size_t)l * e->E * e->H, T,
+                                     e->E, e->H, e->k, nullptr, ids, w, e->d_z, s);
+        if (he == hipSuccess)
+            he = launch_permute(ids, nullptr, 1, T, e->k, e->E, e->shared, x_inout, e->act_bf16,
+                                e->H, e->pb, s);
+        TimedPair tpair{};
+        if (e->timing) {
+            EOCHK(get_pair(e, &tpair));
+            HIPCHK(hipEventRecord(tpair.a, s));
+        }
+        if (he == hipSuccess) {
+            GroupW gw;
+            gw.slots = e->d_staging[b];
+            gw.e2slot = nullptr;
+            gw.stride = e->S_pad;
+            gw.shared_w = e->shared ? e->d_shared + (uint64_t)l * e->S_pad : nullptr;
+            he = launch_ffn_gemm(e->fmt, e->lay, gw, e->E, e->shared, e->H, e->I, T * e->k + T,
+                                 e->pb.offsets, e->pb.tile_off, e->pb.x_perm, e->d_hbuf,
+                                 e->pb.perm_pair, ids, w, e->k, T, e->d_opairs, s);
+        }
+        if (e->timing) {
+            HIPCHK(hipEventRecord(tpair.b, s));
+            e->gemm_ev.push_back(tpair);
+        }
+        if (he == hipSuccess)
+            he = launch_combine(e->d_opairs, ids, nullptr, 1, e->shared, nullptr, T, e->k, e->H, y,
+                                x_inout, e->act_bf16, s, e->E);
+        if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("prefill layer: ") + hipGetErrorString(he));
+        HIPCHK(hipEventRecord(e->ev_comp[b], s));
+        if (!double_buffer && l + 1 < e->L) {
+            HIPCHK(hipStreamWaitEvent(e->copy_stream, e->ev_comp[b], 0));
+            HIPCHK(hipMemcpyAsync(e->d_staging[nb], e->pool[l + 1], layer_bytes,
+                                  hipMemcpyHostToDevice, e->copy_stream));
+            HIPCHK(hipEventRecord(e->ev_copy[nb], e->copy_stream));
+        }
+    }
+    e->stats.prefill_layers += e->L;
+    e->stats.pcie_bytes += (int64_t)layer_bytes * e->L;
+    if (e->timing) EOCHK(harvest_times(e));
+    return EO_OK;
+}
+
+eo_status eo_set_capture(eo_engine* e, void* x_in, float* y, int32_t* ids, float* w,
+                         int32_t tokens_per_layer) {
+    if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
+    if (y && (!x_in || !ids || !w || tokens_per_layer < 1))
+        return fail(EO_ERR_INVALID_ARG, "capture needs all four buffers and a capacity");
+    e->cap_x = x_in;
+    e->cap_y = y;
+    e->cap_ids = ids;
+    e->cap_w = w;
+    e->cap_T = y ? tokens_per_layer : 0;
+    return EO_OK;
+}
+
+eo_status eo_cache_snapshot(eo_engine* e, int32_t* slot_key, int64_t* slot_stamp, int64_t* clock,
+                            int64_t* credit) {
+    if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
+    HIPCHK(hipSetDevice(e->cfg.device));
+    HIPCHK(hipDeviceSynchronize());
+    if (slot_key && e->C) HIPCHK(hipMemcpy(slot_key, e->d_slot_key, sizeof(int32_t) * e->C, hipMemcpyDeviceToHost));
+    if (slot_stamp && e->C)
+        HIPCHK(hipMemcpy(slot_stamp, e->d_slot_stamp, sizeof(int64_t) * e->C, hipMemcpyDeviceToHost));
+    DevState st{};
+    HIPCHK(hipMemcpy(&st, e->d_state, sizeof(DevState), hipMemcpyDeviceToHost));
+    if (clock) *clock = st.clock;
+    if (credit) *credit = st.credit;
+    return EO_OK;
+}
+
+eo_status eo_last_plan(eo_engine* e, eo_plan_host* out) {
+    if (!e || !out) return fail(EO_ERR_INVALID_ARG, "null argument");
+    if (e->plan_pending && !e->plan_ready) EOCHK(wait_plan(e));
+    *out = e->last_plan;
+    return EO_OK;
+}
+
+eo_status eo_dequant(eo_engine* e, int32_t layer, int32_t expert, float* out_host) {
+    EOCHK(check_layer(e, layer));
+    if (expert < 0 || expert >= e->E || !out_host) return fail(EO_ERR_INVALID_ARG, "bad expert");
+    HIPCHK(hipSetDevice(e->cfg.device));
+    uint8_t* blk = nullptr;
+    float* out = nullptr;
+    const size_t n = 3ull * e->H * e->I;
+    EOCHK(dmalloc(&blk, e->S_pad));
+    eo_status st = dmalloc(&out, sizeof(float) * n);
+    if (st != EO_OK) {
+        (void)hipFree(blk);
+        return st;
+    }
+    hipError_t he = hipMemcpy(blk, e->pool[layer] + (uint64_t)expert * e->S_pad, e->S, hipMemcpyHostToDevice);
+    if (he == hipSuccess) he = launch_dequant(e->fmt, e->lay, blk, e->H, e->I, out, nullptr);
+    if (he == hipSuccess) he = hipMemcpy(out_host, out, sizeof(float) * n, hipMemcpyDeviceToHost);
+    (void)hipFree(blk);
+    (void)hipFree(out);
+    if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("dequant: ") + hipGetErrorString(he));
+    return EO_OK;
+}
+
+eo_status eo_stats_get(eo_engine* e, eo_stats* out) {
+    if (!e || !out) return fail(EO_ERR_INVALID_ARG, "null argument");
+    *out = e->stats;
+    return EO_OK;
+}
+
+eo_status eo_set_timing(eo_engine* e, int32_t enable) {
+    if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
+    e->timing = enable != 0;
+    return EO_OK;
+}
+
+eo_status eo_kernel_times(eo_engine* e, double* gemv_ms, int64_t* gemv_launches, double* gemm_ms,
+                          int64_t* gemm_launches, int32_t reset) {
+    if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
+    EOCHK(harvest_times(e));
+    if (gemv_ms) *gemv_ms = e->gemv_ms;
+    if (gemv_launches) *gemv_launches = e->gemv_n;
+    if (gemm_ms) *gemm_ms = e->gemm_ms;
+    if (gemm_launches) *gemm_launches = e->gemm_n;
+    if (reset) {
+        e->gemv_ms = e->gemm_ms = 0;
+        e->gemv_n = e->gemm_n = 0;
+    }
+    return EO_OK;
+}
+
+eo_status eo_sync(eo_engine* e) {
+    if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
+    HIPCHK(hipSetDevice(e->cfg.device));
+    HIPCHK(hipStreamSynchronize(e->copy_stream));
+    HIPCHK(hipDeviceSynchronize());
+    HIPCHK(hipGetLastError());
+    return EO_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Host-side declarations shared by the engine and the host-core expert
+// routine (no HIP dependency, so the routine builds with the host compiler).
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "../../include/eo.h"
+
+namespace eo {
+
+constexpr int kMaxE = EO_MAX_EXPERTS;
+constexpr int kMaxK = 16;
+constexpr uint64_t kPoolAlign = 4096;
+
+// Byte offsets of the sections of one packed expert block (see eo.h).
+struct Layout {
+    uint64_t d13 = 0, d2 = 0, s13 = 0, s2 = 0, gl = 0, bytes = 0;
+};
+Layout layout_of(int H, int I, int fmt);
+
+// Host-core expert routine: for every expert with a non-null `experts` entry,
+// y[t] += w[t,j] * FFN_e(x_t) over the pairs (t, j) routed to it, in fp32.
+class ThreadPool;
+struct HostJob {
+    int fmt;
+    Layout lay;
+    int H, I, T, k;
+    const float* x;                 // [T,H] fp32
+    const int32_t* ids;             // [T,k]
+    const float* w;                 // [T,k]
+    const uint8_t* const* experts;  // pool block per expert id (null: not host-executed)
+    float* y;                       // [T,H] accumulated (zeroed by the caller)
+};
+void host_ffn(ThreadPool* pool, const HostJob& job, std::vector<float>& scratch);
+ThreadPool* threadpool_create(int n);
+void threadpool_destroy(ThreadPool* p);
+int threadpool_size(ThreadPool* p);
+
+}  // namespace eo

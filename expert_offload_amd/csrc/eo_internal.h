@@ -1,0 +1,104 @@
+// Internal declarations shared by the engine and its kernels (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/eo.h"
+#include "eo_host.h"
+
+namespace eo {
+
+// ---------------------------------------------------------------- plan
+// Device-side plan of one lookup call. The lists hold experts of `layer`.
+struct DevPlan {
+    int32_t seq;  // written last; the host polls the mirror's copy
+    int32_t layer, T, k;
+    int32_t m, q, q_fill, n_hit, n_host, n_evict, n_res, pad;
+    int64_t clock, credit;
+    int32_t e2slot[kMaxE];  // slot of each routed resident expert (hit or fill), else -1
+    int32_t count[kMaxE];   // tokens routed to each expert
+    int32_t hit_e[kMaxE], hit_slot[kMaxE];
+    int32_t fill_e[kMaxE], fill_slot[kMaxE];
+    int32_t host_e[kMaxE];
+    int32_t evict_key[kMaxE];
+};
+
+// Residency state in device memory.
+struct DevState {
+    int64_t clock, credit;
+    int32_t bp, bh;  // MB/s
+    int32_t seq, pad;
+};
+
+// ---------------------------------------------------------------- launches
+// Router (fixed-order fp32 logits, top-k, softmax).
+hipError_t launch_route(const void* x, int act_bf16, const float* R, int T, int E, int H, int k,
+                        const int32_t* forced, int32_t* ids, float* w, float* z_scratch,
+                        hipStream_t s);
+
+// Lookup + LRU + miss plan, single workgroup; writes plan to d_plan and a
+// mirror (header, lists, ids, w and, when x_mirror != null, x) to host memory.
+hipError_t launch_plan(int layer, const int32_t* ids, const float* w, const void* x,
+                       size_t x_bytes, int T, int k, int E, int64_t C, int32_t* slot_key,
+                       int64_t* slot_stamp, int32_t* key2slot, DevState* st, DevPlan* d_plan,
+                       DevPlan* h_plan, int32_t* h_ids, float* h_w, void* h_x, hipStream_t s);
+
+// Permute: group the (token, k) pairs whose expert is resident by expert,
+// stable in pair order; the shared expert (when present) is group E holding
+// every token. Produces offsets [E+2], tile offsets, perm_pair, x_perm.
+struct PermuteBufs {
+    int32_t* counts;     // [E+1]
+    int32_t* offsets;    // [E+2]
+    int32_t* tile_off;   // [E+2], tiles of kTileM rows per group
+    int32_t* perm_pair;  // [P_max], pair index t*k+j (shared rows: T*k + t)
+    int32_t* chunk_cnt;  // [nchunks, E]
+    void* x_perm;        // [P_max, H]
+};
+hipError_t launch_permute(const int32_t* ids, const int32_t* e2slot, int all_resident, int T,
+                          int k, int E, int has_shared, const void* x, int act_bf16, int H,
+                          PermuteBufs b, hipStream_t s);
+
+// Grouped SwiGLU FFN (GEMM path). Weight base of group g: shared_w for g == E,
+// else (e2slot ? slots + e2slot[g]*stride : slots + g*stride).
+struct GroupW {
+    const uint8_t* slots;
+    const int32_t* e2slot;  // null: group g lives at slots + g*stride
+    uint64_t stride;
+    const uint8_t* shared_w;
+};
+hipError_t launch_ffn_gemm(int fmt, const Layout& lay, GroupW gw, int E, int has_shared, int H,
+                           int I, int P_max, const int32_t* offsets, const int32_t* tile_off,
+                           const void* x_perm, void* h_buf, const int32_t* perm_pair,
+                           const int32_t* ids, const float* w, int k, int T, float* o_pairs,
+                           hipStream_t s);
+
+// Combine: y[t] = sum_j (resident) o_pairs[t*k+j] + o_pairs[T*k+t] (shared)
+// + y_host[t] (if given). Optional residual: x_out = act(x + y).
+hipError_t launch_combine(const float* o_pairs, const int32_t* ids, const int32_t* e2slot,
+                          int all_resident, int has_shared, const float* y_host, int T, int k,
+                          int H, float* y, void* x_res, int act_bf16, hipStream_t s, int E);
+
+// Decode GEMV path (T == 1): phase A gate/up -> h, phase B down with weights.
+hipError_t launch_ffn_gemv(int fmt, const Layout& lay, GroupW gw, const DevPlan* plan,
+                           const int32_t* ids, const float* w, int k, int E, int has_shared,
+                           int H, int I, const void* x, int act_bf16, float* h_buf,
+                           float* y_parts, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+// Sum of the GEMV partials (k + shared rows of [H]) plus host results.
+hipError_t launch_gemv_reduce(const float* y_parts, int nparts, const float* y_host, int H,
+                              float* y, void* x_res, int act_bf16, hipStream_t s);
+
+// Residual add: x = act(x + y), T*H elements.
+hipError_t launch_residual(void* x, const float* y, int64_t n, int act_bf16, hipStream_t s);
+
+// Debug dequant of one expert block to fp32 (device decoder).
+hipError_t launch_dequant(int fmt, const Layout& lay, const uint8_t* blk, int H, int I, float* out,
+                          hipStream_t s);
+
+constexpr int kTileM = 128;  // grouped GEMM tile rows
+
+}  // namespace eo

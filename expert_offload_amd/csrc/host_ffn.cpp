@@ -1,0 +1,324 @@
+// Host-core expert routine: runs a missed expert's SwiGLU FFN on the CPU,
+// reading its packed block straight from the pinned host pool.
+//
+// zhichai.net article, section 2, Decode paragraph: misses that the bandwidth
+// split does not send over PCIe are executed in place on the host cores, so
+// host memory bandwidth (B_H) is put to use instead of sitting idle. The
+// routine is fp32 on the host (decoding the block's format in-line) and is
+// spread over a pool of threads: phase 1 over the gate/up rows of every host
+// expert, phase 2 over the output rows, where each token's host pairs are summed
+// in slot order j.
+#include <immintrin.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <condition_variable>
+#include <cstring>
+#include <functional>
+#include <mutex>
+#include <thread>
+
+#include "eo_host.h"
+
+namespace eo {
+
+// ------------------------------------------------------------ thread pool
+class ThreadPool {
+  public:
+    explicit ThreadPool(int n) : n_(std::max(1, n)) {
+        for (int i = 1; i < n_; ++i) workers_.emplace_back([this] { loop(); });
+    }
+    ~ThreadPool() {
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            stop_ = true;
+            gen_.fetch_add(1, std::memory_order_release);
+        }
+        cv_.notify_all();
+        for (auto& t : workers_) t.join();
+    }
+    int size() const { return n_; }
+
+    // Run fn(task) for task in [0, ntasks) on all threads (the caller included).
+    void run(int ntasks, const std::function<void(int)>& fn) {
+        if (ntasks <= 0) return;
+        if (n_ == 1 || ntasks == 1) {
+            for (int i = 0; i < ntasks; ++i) fn(i);
+            return;
+        }
+        fn_ = &fn;
+        ntasks_ = ntasks;
+        next_.store(0, std::memory_order_relaxed);
+        done_.store(0, std::memory_order_relaxed);
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            gen_.fetch_add(1, std::memory_order_release);
+        }
+        cv_.notify_all();
+        work();
+        while (done_.load(std::memory_order_acquire) < n_ - 1) _mm_pause();
+    }
+
+  private:
+    void work() {
+        for (;;) {
+            int i = next_.fetch_add(1, std::memory_order_relaxed);
+            if (i >= ntasks_) break;
+            (*fn_)(i);
+        }
+    }
+    void loop() {
+        uint64_t seen = gen_.load(std::memory_order_acquire);
+        for (;;) {
+            // spin briefly for low dispatch latency, then sleep
+            int spins = 0;
+            while (gen_.load(std::memory_order_acquire) == seen && spins < 200000) {
+                _mm_pause();
+                ++spins;
+            }
+            if (gen_.load(std::memory_order_acquire) == seen) {
+                std::unique_lock<std::mutex> lk(mu_);
+                cv_.wait(lk, [&] { return gen_.load(std::memory_order_acquire) != seen; });
+            }
+            seen = gen_.load(std::memory_order_acquire);
+            if (stop_) return;
+            work();
+            done_.fetch_add(1, std::memory_order_acq_rel);
+        }
+    }
+
+    int n_;
+    std::vector<std::thread> workers_;
+    std::mutex mu_;
+    std::condition_variable cv_;
+    std::atomic<uint64_t> gen_{0};
+    std::atomic<int> next_{0}, done_{0};
+    const std::function<void(int)>* fn_ = nullptr;
+    int ntasks_ = 0;
+    bool stop_ = false;
+};
+
+ThreadPool* threadpool_create(int n) { return new ThreadPool(n); }
+void threadpool_destroy(ThreadPool* p) { delete p; }
+int threadpool_size(ThreadPool* p) { return p->size(); }
+
+// ------------------------------------------------------------ decoding
+namespace {
+
+float e2m1_val(uint32_t c) {
+    static const float t[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
+    float v = t[c & 7];
+    return (c & 8) ? -v : v;
+}
+float e4m3_val(uint32_t c) {
+    uint32_t e = (c >> 3) & 15, m = c & 7;
+    float v;
+    if (e == 15 && m == 7) v = NAN;
+    else if (e == 0) v = std::ldexp((float)m, -9);
+    else v = std::ldexp(1.0f + m / 8.0f, (int)e - 7);
+    return (c & 0x80) ? -v : v;
+}
+float e8m0_val(uint32_t c) { return c == 0xFF ? NAN : std::ldexp(1.0f, (int)c - 127); }
+
+// Decode row `row` (K elements) of a matrix section into out (fp32).
+void decode_row(int fmt, const uint8_t* data, const uint8_t* scal, float gscale, int row, int K,
+                float* out) {
+    switch (fmt) {
+    case EO_W_FP32: std::memcpy(out, (const float*)data + (size_t)row * K, sizeof(float) * K); break;
+    case EO_W_BF16: {
+        const uint16_t* p = (const uint16_t*)data + (size_t)row * K;
+        int i = 0;
+        for (; i + 8 <= K; i += 8) {
+            __m128i b = _mm_loadu_si128((const __m128i*)(p + i));
+            __m256i w = _mm256_slli_epi32(_mm256_cvtepu16_epi32(b), 16);
+            _mm256_storeu_ps(out + i, _mm256_castsi256_ps(w));
+        }
+        for (; i < K; ++i) {
+            uint32_t u = (uint32_t)p[i] << 16;
+            std::memcpy(out + i, &u, 4);
+        }
+        break;
+    }
+    case EO_W_FP8: {
+        const uint8_t* p = data + (size_t)row * K;
+        float s = ((const float*)scal)[row];
+        for (int i = 0; i < K; ++i) out[i] = e4m3_val(p[i]) * s;
+        break;
+    }
+    case EO_W_MXFP4: {
+        const uint8_t* p = data + (size_t)row * (K / 2);
+        const uint8_t* sp = scal + (size_t)row * (K / 32);
+        for (int b = 0; b < K / 32; ++b) {
+            float s = e8m0_val(sp[b]);
+            for (int i = 0; i < 16; ++i) {
+                uint32_t byte = p[b * 16 + i];
+                out[b * 32 + 2 * i] = e2m1_val(byte & 0xF) * s;
+                out[b * 32 + 2 * i + 1] = e2m1_val(byte >> 4) * s;
+            }
+        }
+        break;
+    }
+    case EO_W_NVFP4: {
+        const uint8_t* p = data + (size_t)row * (K / 2);
+        const uint8_t* sp = scal + (size_t)row * (K / 16);
+        for (int b = 0; b < K / 16; ++b) {
+            float s = e4m3_val(sp[b]);
+            for (int i = 0; i < 8; ++i) {
+                uint32_t byte = p[b * 8 + i];
+                out[b * 16 + 2 * i] = (e2m1_val(byte & 0xF) * s) * gscale;
+                out[b * 16 + 2 * i + 1] = (e2m1_val(byte >> 4) * s) * gscale;
+            }
+        }
+        break;
+    }
+    }
+}
+
+inline float hsum256(__m256 v) {
+    __m128 lo = _mm256_castps256_ps128(v), hi = _mm256_extractf128_ps(v, 1);
+    __m128 s = _mm_add_ps(lo, hi);
+    s = _mm_add_ps(s, _mm_movehl_ps(s, s));
+    s = _mm_add_ss(s, _mm_shuffle_ps(s, s, 1));
+    return _mm_cvtss_f32(s);
+}
+
+float dot(const float* a, const float* b, int K) {
+    __m256 s0 = _mm256_setzero_ps(), s1 = _mm256_setzero_ps();
+    int i = 0;
+    for (; i + 16 <= K; i += 16) {
+        s0 = _mm256_fmadd_ps(_mm256_loadu_ps(a + i), _mm256_loadu_ps(b + i), s0);
+        s1 = _mm256_fmadd_ps(_mm256_loadu_ps(a + i + 8), _mm256_loadu_ps(b + i + 8), s1);
+    }
+    float s = hsum256(_mm256_add_ps(s0, s1));
+    for (; i < K; ++i) s += a[i] * b[i];
+    return s;
+}
+
+// bf16 row (raw) dot fp32 vector, no staging.
+float dot_bf16(const uint16_t* w, const float* x, int K) {
+    __m256 s0 = _mm256_setzero_ps(), s1 = _mm256_setzero_ps();
+    int i = 0;
+    for (; i + 16 <= K; i += 16) {
+        __m256i b = _mm256_loadu_si256((const __m256i*)(w + i));
+        __m256 lo = _mm256_castsi256_ps(
+            _mm256_slli_epi32(_mm256_cvtepu16_epi32(_mm256_castsi256_si128(b)), 16));
+        __m256 hi = _mm256_castsi256_ps(
+            _mm256_slli_epi32(_mm256_cvtepu16_epi32(_mm256_extracti128_si256(b, 1)), 16));
+        s0 = _mm256_fmadd_ps(lo, _mm256_loadu_ps(x + i), s0);
+        s1 = _mm256_fmadd_ps(hi, _mm256_loadu_ps(x + i + 8), s1);
+    }
+    float s = hsum256(_mm256_add_ps(s0, s1));
+    for (; i < K; ++i) {
+        uint32_t u = (uint32_t)w[i] << 16;
+        float f;
+        std::memcpy(&f, &u, 4);
+        s += f * x[i];
+    }
+    return s;
+}
+
+}  // namespace
+
+void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) {
+    const int H = jb.H, I = jb.I, T = jb.T, k = jb.k;
+    // host experts and their pairs
+    std::vector<int> exps;  // expert ids, ascending
+    std::vector<int> slot_of(EO_MAX_EXPERTS, -1);
+    for (int p = 0; p < T * k; ++p) {
+        int e = jb.ids[p];
+        if (e >= 0 && e < EO_MAX_EXPERTS && jb.experts[e] && slot_of[e] < 0) {
+            slot_of[e] = 0;
+            exps.push_back(e);
+        }
+    }
+    if (exps.empty()) return;
+    std::sort(exps.begin(), exps.end());
+    const int ne = (int)exps.size();
+    for (int i = 0; i < ne; ++i) slot_of[exps[i]] = i;
+    // tokens per host expert
+    std::vector<std::vector<int>> toks(ne);
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int e = jb.ids[t * k + j];
+            if (e >= 0 && e < EO_MAX_EXPERTS && jb.experts[e]) toks[slot_of[e]].push_back(t);
+        }
+    // h[i][t_idx][I]
+    std::vector<size_t> hoff(ne + 1, 0);
+    for (int i = 0; i < ne; ++i) hoff[i + 1] = hoff[i] + toks[i].size() * (size_t)I;
+    if (scratch.size() < hoff[ne]) scratch.resize(hoff[ne]);
+    float* h = scratch.data();
+    const int fmt = jb.fmt;
+    const Layout lay = jb.lay;
+
+    auto gl = [&](const uint8_t* b, int t) -> float {
+        return fmt == EO_W_NVFP4 ? ((const float*)(b + lay.gl))[t] : 1.0f;
+    };
+
+    constexpr int RB = 16;
+    const int nb1 = (I + RB - 1) / RB;
+    pool->run(ne * nb1, [&](int task) {
+        const int ei = task / nb1, rb = task % nb1;
+        const uint8_t* b = jb.experts[exps[ei]];
+        thread_local std::vector<float> rg, ru;
+        rg.resize(H);
+        ru.resize(H);
+        for (int r = rb * RB; r < std::min(I, rb * RB + RB); ++r) {
+            const float* gr;
+            const float* ur;
+            if (fmt == EO_W_BF16) {
+                gr = ur = nullptr;
+            } else {
+                decode_row(fmt, b + lay.d13, b + lay.s13, gl(b, 0), r, H, rg.data());
+                decode_row(fmt, b + lay.d13, b + lay.s13, gl(b, 1), I + r, H, ru.data());
+                gr = rg.data();
+                ur = ru.data();
+            }
+            for (size_t ti = 0; ti < toks[ei].size(); ++ti) {
+                const float* xt = jb.x + (size_t)toks[ei][ti] * H;
+                float g, u;
+                if (fmt == EO_W_BF16) {
+                    const uint16_t* W = (const uint16_t*)(b + lay.d13);
+                    g = dot_bf16(W + (size_t)r * H, xt, H);
+                    u = dot_bf16(W + (size_t)(I + r) * H, xt, H);
+                } else {
+                    g = dot(gr, xt, H);
+                    u = dot(ur, xt, H);
+                }
+                h[hoff[ei] + ti * I + r] = g / (1.0f + std::exp(-g)) * u;
+            }
+        }
+    });
+
+    const int nb2 = (H + RB - 1) / RB;
+    pool->run(nb2, [&](int task) {
+        thread_local std::vector<float> rd;
+        rd.resize(I);
+        for (int o = task * RB; o < std::min(H, task * RB + RB); ++o) {
+            for (int t = 0; t < T; ++t) {
+                float acc = 0.0f;
+                for (int j = 0; j < k; ++j) {
+                    int e = jb.ids[t * k + j];
+                    if (e < 0 || e >= EO_MAX_EXPERTS || !jb.experts[e]) continue;
+                    int ei = slot_of[e];
+                    const uint8_t* b = jb.experts[e];
+                    // position of t in toks[ei]
+                    const std::vector<int>& tl = toks[ei];
+                    int ti = (int)(std::lower_bound(tl.begin(), tl.end(), t) - tl.begin());
+                    const float* ht = h + hoff[ei] + (size_t)ti * I;
+                    float v;
+                    if (fmt == EO_W_BF16) {
+                        v = dot_bf16((const uint16_t*)(b + lay.d2) + (size_t)o * I, ht, I);
+                    } else {
+                        decode_row(fmt, b + lay.d2, b + lay.s2, gl(b, 2), o, I, rd.data());
+                        v = dot(rd.data(), ht, I);
+                    }
+                    acc += jb.w[t * k + j] * v;
+                }
+                jb.y[(size_t)t * H + o] += acc;
+            }
+        }
+    });
+}
+
+}  // namespace eo

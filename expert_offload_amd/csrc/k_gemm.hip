@@ -1,0 +1,359 @@
+// Grouped SwiGLU expert FFN for many tokens (prefill, and any call with T > 1).
+//
+// Per expert e with its M_e permuted rows X_e (bf16):
+//   GEMM1: G = X_e . W13^T, h = silu(G_gate) * G_up  -> bf16 [M_e, I]
+//   GEMM2: O = h . W2^T, scaled by the pair's routing weight -> o_pairs (fp32)
+// on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulate). Weight
+// tiles are decoded into LDS as bf16: bf16 as stored; e4m3 (FP8) and
+// e2m1 * e8m0 (MXFP4) and e2m1 * e4m3 (NVFP4) are exact in bf16, so the only
+// factors left over — the FP8 per-row scale and the NVFP4 per-tensor global
+// scale — are applied to the fp32 accumulators in the epilogue. The format
+// list is the juejin.cn overview's (section 5).
+//
+// Tiles: 128 x 128 outputs per 256-thread workgroup (2 x 2 wavefronts of 64 x 64,
+// each 2 x 2 MFMA blocks of 32 x 32), K step 64. A flat tile index runs over the
+// groups' row tiles (tile_off, 128-row tiles); the N tiles are blockIdx.y.
+// GEMM1's N tile is 64 gate columns plus the same 64 up columns, split so that
+// each wavefront holds matching gate and up accumulators and forms h in
+// registers.
+//
+// fp32 weights with fp32 activations (small test models) use a plain VALU
+// kernel with the same grouping and epilogues.
+#include "dev_common.h"
+#include "eo_internal.h"
+
+namespace eo {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;  // LDS row stride in bf16
+
+struct GemmArgs {
+    GroupW gw;
+    Layout lay;
+    int E, G, K;  // G = groups incl. shared; K = contraction length
+    int H, I;
+    const int32_t* offsets;
+    const int32_t* tile_off;
+    const uint16_t* A;    // [rows, K] bf16
+    uint16_t* h_out;      // GEMM1 output [rows, I] bf16
+    const int32_t* perm_pair;
+    const float* w;
+    int Tk;
+    float* o_pairs;       // GEMM2 output [Tk + T, H]
+};
+
+__device__ __forceinline__ int find_group(const int32_t* tile_off, int G, int tile) {
+    int lo = 0, hi = G;  // tile_off[lo] <= tile < tile_off[hi]
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (tile_off[mid] <= tile) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ const uint8_t* group_base(const GroupW& gw, int g, int E) {
+    if (g == E) return gw.shared_w;
+    int s = gw.e2slot ? gw.e2slot[g] : g;
+    return gw.slots + (uint64_t)s * gw.stride;
+}
+
+__device__ __forceinline__ uint32_t bf_hi(float v) { return __float_as_uint(v) >> 16; }
+
+// Decode 32 fp4 codes (16 bytes) with per-16 multipliers sc0 (elements 0..15)
+// and sc1 (16..31) into 32 bf16 at dst (exact: at most 6 significant bits).
+__device__ __forceinline__ void fp4x32_to_lds(uint4 q, float sc0, float sc1, uint16_t* dst) {
+    uint32_t words[4] = {q.x, q.y, q.z, q.w};
+    uint32_t out[16];
+#pragma unroll
+    for (int wi = 0; wi < 4; ++wi) {
+        float sc = wi < 2 ? sc0 : sc1;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            uint32_t byte = (words[wi] >> (8 * b)) & 0xFFu;
+            uint32_t lo = bf_hi(e2m1_f32(byte & 0xFu) * sc);
+            uint32_t hi = bf_hi(e2m1_f32(byte >> 4) * sc);
+            out[wi * 4 + b] = lo | (hi << 16);
+        }
+    }
+    uint4* d = (uint4*)dst;
+    d[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    d[1] = make_uint4(out[4], out[5], out[6], out[7]);
+    d[2] = make_uint4(out[8], out[9], out[10], out[11]);
+    d[3] = make_uint4(out[12], out[13], out[14], out[15]);
+}
+
+template <int FMT, int MODE>
+__global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
+
+    const int tile = blockIdx.x;
+    if (tile >= a.tile_off[a.G]) return;
+    const int g = find_group(a.tile_off, a.G, tile);
+    const int m0 = a.offsets[g] + (tile - a.tile_off[g]) * BM;
+    const int m_end = a.offsets[g + 1];
+    const uint8_t* wb = group_base(a.gw, g, a.E);
+    const int K = a.K;
+    const uint8_t* wdata = wb + (MODE == 0 ? a.lay.d13 : a.lay.d2);
+    const uint8_t* wscal = wb + (MODE == 0 ? a.lay.s13 : a.lay.s2);
+    const int n0 = blockIdx.y * (MODE == 0 ? 64 : 128);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    auto wrow = [&](int i) -> int {  // LDS B row -> weight row
+        if (MODE == 0) return i < 64 ? n0 + i : a.I + n0 + (i - 64);
+        return n0 + i;
+    };
+
+    for (int k0 = 0; k0 < K; k0 += BK) {
+        // A tile: 128 rows x 64 bf16, 4 x 16 B per thread
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            int c = tid + 256 * it, r = c >> 3, seg = c & 7;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (m0 + r < m_end)
+                v = *(const uint4*)(a.A + (size_t)(m0 + r) * K + k0 + seg * 8);
+            *(uint4*)(As + r * LDK + seg * 8) = v;
+        }
+        // B tile: 128 weight rows x 64 elements, decoded to bf16
+        if (FMT == EO_W_BF16) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                int c = tid + 256 * it, r = c >> 3, seg = c & 7;
+                const uint16_t* src = (const uint16_t*)wdata + (size_t)wrow(r) * K + k0 + seg * 8;
+                *(uint4*)(Bs + r * LDK + seg * 8) = *(const uint4*)src;
+            }
+        } else if (FMT == EO_W_FP8) {
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                int c = tid + 256 * it, r = c >> 2, seg = c & 3;
+                uint4 q = *(const uint4*)(wdata + (size_t)wrow(r) * K + k0 + seg * 16);
+                uint32_t words[4] = {q.x, q.y, q.z, q.w}, out[8];
+#pragma unroll
+                for (int wi = 0; wi < 4; ++wi) {
+                    uint32_t wv = words[wi];
+                    out[2 * wi] = bf_hi(e4m3_f32(wv & 0xFF)) | (bf_hi(e4m3_f32((wv >> 8) & 0xFF)) << 16);
+                    out[2 * wi + 1] =
+                        bf_hi(e4m3_f32((wv >> 16) & 0xFF)) | (bf_hi(e4m3_f32(wv >> 24)) << 16);
+                }
+                uint4* d = (uint4*)(Bs + r * LDK + seg * 16);
+                d[0] = make_uint4(out[0], out[1], out[2], out[3]);
+                d[1] = make_uint4(out[4], out[5], out[6], out[7]);
+            }
+        } else {  // MXFP4 / NVFP4: one 32-element chunk per thread
+            int r = tid >> 1, half = tid & 1;
+            int wr = wrow(r);
+            int kk = k0 + half * 32;
+            uint4 q = *(const uint4*)(wdata + (size_t)wr * (K / 2) + kk / 2);
+            float sc0, sc1;
+            if (FMT == EO_W_MXFP4) {
+                sc0 = sc1 = e8m0_f32(wscal[(size_t)wr * (K / 32) + kk / 32]);
+            } else {
+                const uint8_t* sp = wscal + (size_t)wr * (K / 16) + kk / 16;
+                sc0 = e4m3_f32(sp[0]);
+                sc1 = e4m3_f32(sp[1]);
+            }
+            fp4x32_to_lds(q, sc0, sc1, Bs + r * LDK + half * 32);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int kc = ks * 16 + (lane >> 5) * 8;
+            bf16x8 av[2], bv[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                av[i] = *(const bf16x8*)(As + (wm * 64 + i * 32 + (lane & 31)) * LDK + kc);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                int br = MODE == 0 ? (j * 64 + wn * 32 + (lane & 31)) : (wn * 64 + j * 32 + (lane & 31));
+                bv[j] = *(const bf16x8*)(Bs + br * LDK + kc);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+    // epilogue
+    const int col = lane & 31;
+    if (MODE == 0) {
+        const int n = n0 + wn * 32 + col;
+        float sg = 1.0f, su = 1.0f;
+        if (FMT == EO_W_FP8) {
+            sg = ((const float*)wscal)[n];
+            su = ((const float*)wscal)[a.I + n];
+        } else if (FMT == EO_W_NVFP4) {
+            const float* gl = (const float*)(wb + a.lay.gl);
+            sg = gl[0];
+            su = gl[1];
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (m0 + row < m_end) {
+                    float gv = acc[i][0][v] * sg, uv = acc[i][1][v] * su;
+                    float hv = silu_f32(gv) * uv;
+                    a.h_out[(size_t)(m0 + row) * a.I + n] = (uint16_t)f32_bf16_rne(hv);
+                }
+            }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = n0 + wn * 64 + j * 32 + col;
+            float sc = 1.0f;
+            if (FMT == EO_W_FP8) sc = ((const float*)wscal)[n];
+            else if (FMT == EO_W_NVFP4) sc = ((const float*)(wb + a.lay.gl))[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    if (m0 + row < m_end) {
+                        int pair = a.perm_pair[m0 + row];
+                        float wp = pair < a.Tk ? a.w[pair] : 1.0f;
+                        a.o_pairs[(size_t)pair * a.H + n] = acc[i][j][v] * sc * wp;
+                    }
+                }
+        }
+    }
+}
+
+// fp32 weights and activations: 128 x 64 tile, 8 x 4 outputs per thread.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs a, const float* __restrict__ Af,
+                                                  float* __restrict__ hf) {
+    constexpr int TBM = 128, TBN = 64, TBK = 16;
+    __shared__ float As[TBK][TBM + 4];
+    __shared__ float Bs[TBK][TBN + 4];
+    const int tile = blockIdx.x;
+    if (tile >= a.tile_off[a.G]) return;
+    const int g = find_group(a.tile_off, a.G, tile);
+    const int m0 = a.offsets[g] + (tile - a.tile_off[g]) * TBM;
+    const int m_end = a.offsets[g + 1];
+    const uint8_t* wb = group_base(a.gw, g, a.E);
+    const float* W = (const float*)(wb + (MODE == 0 ? a.lay.d13 : a.lay.d2));
+    const int K = a.K;
+    const int n0 = blockIdx.y * (MODE == 0 ? 32 : 64);
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    float acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+    for (int k0 = 0; k0 < K; k0 += TBK) {
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            int c = tid + 256 * it, r = c >> 4, kk = c & 15;
+            As[kk][r] = (m0 + r < m_end) ? Af[(size_t)(m0 + r) * K + k0 + kk] : 0.0f;
+        }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            int c = tid + 256 * it, r = c >> 4, kk = c & 15;
+            int wr = MODE == 0 ? (r < 32 ? n0 + r : a.I + n0 + r - 32) : n0 + r;
+            Bs[kk][r] = W[(size_t)wr * K + k0 + kk];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < TBK; ++kk) {
+            float av[8], bv[4];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) av[i] = As[kk][ty + 16 * i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx + 16 * j];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int row = ty + 16 * i;
+        if (m0 + row >= m_end) continue;
+        if (MODE == 0) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                int n = n0 + tx + 16 * j;
+                hf[(size_t)(m0 + row) * a.I + n] = silu_f32(acc[i][j]) * acc[i][j + 2];
+            }
+        } else {
+            int pair = a.perm_pair[m0 + row];
+            float wp = pair < a.Tk ? a.w[pair] : 1.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                int n = n0 + tx + 16 * j;
+                a.o_pairs[(size_t)pair * a.H + n] = acc[i][j] * wp;
+            }
+        }
+    }
+}
+
+template <int FMT>
+void run_mfma(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s) {
+    k_gemm_mfma<FMT, 0><<<dim3(tiles, I / 64), 256, 0, s>>>(a1);
+    k_gemm_mfma<FMT, 1><<<dim3(tiles, H / 128), 256, 0, s>>>(a2);
+}
+
+}  // namespace
+
+hipError_t launch_ffn_gemm(int fmt, const Layout& lay, GroupW gw, int E, int has_shared, int H,
+                           int I, int P_max, const int32_t* offsets, const int32_t* tile_off,
+                           const void* x_perm, void* h_buf, const int32_t* perm_pair,
+                           const int32_t* ids, const float* w, int k, int T, float* o_pairs,
+                           hipStream_t s) {
+    (void)ids;
+    const int G = E + (has_shared ? 1 : 0);
+    const int tiles = (P_max + kTileM - 1) / kTileM + G;  // upper bound on row tiles
+    GemmArgs a1{};
+    a1.gw = gw;
+    a1.lay = lay;
+    a1.E = E;
+    a1.G = G;
+    a1.H = H;
+    a1.I = I;
+    a1.offsets = offsets;
+    a1.tile_off = tile_off;
+    a1.perm_pair = perm_pair;
+    a1.w = w;
+    a1.Tk = T * k;
+    a1.o_pairs = o_pairs;
+    GemmArgs a2 = a1;
+    a1.K = H;
+    a1.A = (const uint16_t*)x_perm;
+    a1.h_out = (uint16_t*)h_buf;
+    a2.K = I;
+    a2.A = (const uint16_t*)h_buf;
+    switch (fmt) {
+    case EO_W_FP32:
+        k_gemm_f32<0><<<dim3(tiles, I / 32), 256, 0, s>>>(a1, (const float*)x_perm, (float*)h_buf);
+        k_gemm_f32<1><<<dim3(tiles, H / 64), 256, 0, s>>>(a2, (const float*)h_buf, nullptr);
+        break;
+    case EO_W_BF16: run_mfma<EO_W_BF16>(a1, a2, tiles, I, H, s); break;
+    case EO_W_FP8: run_mfma<EO_W_FP8>(a1, a2, tiles, I, H, s); break;
+    case EO_W_MXFP4: run_mfma<EO_W_MXFP4>(a1, a2, tiles, I, H, s); break;
+    case EO_W_NVFP4: run_mfma<EO_W_NVFP4>(a1, a2, tiles, I, H, s); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace eo

@@ -1,0 +1,235 @@
+// Token permutation by expert, weighted combine and residual.
+//
+// Grouped expert execution needs each expert's tokens contiguous: the (token,
+// slot) pairs whose expert is device-resident are grouped by expert, stable in
+// pair order (t*k + j), and their rows of X gathered into x_perm. The shared
+// expert (papers.ananclaw.com explainer, "core method" section 4, names it as
+// an architecture axis) is one more group holding every token. After the
+// grouped FFN, each pair's weighted output sits at o_pairs[t*k + j] (shared:
+// o_pairs[T*k + t]) and the combine sums a token's rows in fixed j order.
+#include "dev_common.h"
+#include "eo_internal.h"
+
+namespace eo {
+
+namespace {
+
+constexpr int kChunk = 1024;  // pairs per permute block
+
+__device__ __forceinline__ bool pair_resident(const int32_t* e2slot, int all_resident, int e,
+                                              int E) {
+    if (e < 0 || e >= E) return false;
+    return all_resident || e2slot[e] >= 0;
+}
+
+// Per-chunk expert histogram: chunk_cnt[b][e].
+__global__ __launch_bounds__(1024) void k_hist(const int32_t* __restrict__ ids,
+                                               const int32_t* __restrict__ e2slot,
+                                               int all_resident, int P, int E,
+                                               int32_t* __restrict__ chunk_cnt) {
+    __shared__ int h[kMaxE];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) h[e] = 0;
+    __syncthreads();
+    int p = blockIdx.x * kChunk + threadIdx.x;
+    if (p < P) {
+        int e = ids[p];
+        if (pair_resident(e2slot, all_resident, e, E)) atomicAdd(&h[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        chunk_cnt[(size_t)blockIdx.x * E + e] = h[e];
+}
+
+// Single block: per expert, exclusive scan over chunks (in place: chunk base
+// within the expert); group counts, offsets and tile offsets.
+__global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ chunk_cnt, int nchunks,
+                                               int E, int has_shared, int T,
+                                               int32_t* __restrict__ counts,
+                                               int32_t* __restrict__ offsets,
+                                               int32_t* __restrict__ tile_off) {
+    __shared__ int cnt[kMaxE + 1];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int run = 0;
+        for (int b = 0; b < nchunks; ++b) {
+            int c = chunk_cnt[(size_t)b * E + e];
+            chunk_cnt[(size_t)b * E + e] = run;
+            run += c;
+        }
+        cnt[e] = run;
+    }
+    if (threadIdx.x == 0) cnt[E] = has_shared ? T : 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int off = 0, toff = 0;
+        for (int g = 0; g <= E; ++g) {
+            counts[g] = cnt[g];
+            offsets[g] = off;
+            tile_off[g] = toff;
+            off += cnt[g];
+            toff += (cnt[g] + kTileM - 1) / kTileM;
+        }
+        offsets[E + 1] = off;
+        tile_off[E + 1] = toff;
+    }
+}
+
+// Scatter: stable rank of each pair within its expert inside the chunk, then
+// its destination row; rows of x are copied by whole wavefronts (16 B/lane).
+__global__ __launch_bounds__(1024) void k_scatter(const int32_t* __restrict__ ids,
+                                                  const int32_t* __restrict__ e2slot,
+                                                  int all_resident, int P, int k, int E,
+                                                  const int32_t* __restrict__ chunk_base,
+                                                  const int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ perm_pair,
+                                                  const uint8_t* __restrict__ x, int row_bytes,
+                                                  uint8_t* __restrict__ x_perm) {
+    __shared__ int se[kChunk];
+    __shared__ int dst[kChunk];
+    const int tid = threadIdx.x;
+    const int p0 = blockIdx.x * kChunk;
+    const int p = p0 + tid;
+    int e = -1;
+    if (p < P) {
+        int ee = ids[p];
+        if (pair_resident(e2slot, all_resident, ee, E)) e = ee;
+    }
+    se[tid] = e;
+    __syncthreads();
+    int d = -1;
+    if (e >= 0) {
+        int r = 0;
+        for (int i = 0; i < tid; ++i) r += (se[i] == e);
+        d = offsets[e] + chunk_base[(size_t)blockIdx.x * E + e] + r;
+        perm_pair[d] = p;
+    }
+    dst[tid] = d;
+    __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n = min(kChunk, P - p0);
+    for (int i = wave; i < n; i += 16) {
+        int di = dst[i];
+        if (di < 0) continue;
+        const uint4* src = (const uint4*)(x + (size_t)((p0 + i) / k) * row_bytes);
+        uint4* out = (uint4*)(x_perm + (size_t)di * row_bytes);
+        for (int c = lane; c < row_bytes / 16; c += 64) out[c] = src[c];
+    }
+}
+
+// Shared-expert group: rows offsets[E] + t hold token t.
+__global__ __launch_bounds__(256) void k_shared_rows(int T, int Tk, const int32_t* __restrict__ offsets,
+                                                     int E, int32_t* __restrict__ perm_pair,
+                                                     const uint8_t* __restrict__ x, int row_bytes,
+                                                     uint8_t* __restrict__ x_perm) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int d = offsets[E] + t;
+    if (lane == 0) perm_pair[d] = Tk + t;
+    const uint4* src = (const uint4*)(x + (size_t)t * row_bytes);
+    uint4* out = (uint4*)(x_perm + (size_t)d * row_bytes);
+    for (int c = lane; c < row_bytes / 16; c += 64) out[c] = src[c];
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o_pairs,
+                                                 const int32_t* __restrict__ ids,
+                                                 const int32_t* __restrict__ e2slot,
+                                                 int all_resident, int has_shared,
+                                                 const float* __restrict__ y_host, int T, int k,
+                                                 int E, int H, float* __restrict__ y,
+                                                 void* __restrict__ x_res) {
+    const int t = blockIdx.y;
+    const int h4 = blockIdx.x * blockDim.x + threadIdx.x;
+    if (h4 * 4 >= H) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+        int e = ids[(size_t)t * k + j];
+        if (!pair_resident(e2slot, all_resident, e, E)) continue;
+        float4 v = ((const float4*)(o_pairs + ((size_t)t * k + j) * H))[h4];
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    if (has_shared) {
+        float4 v = ((const float4*)(o_pairs + ((size_t)T * k + t) * H))[h4];
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    if (y_host) {
+        float4 v = ((const float4*)(y_host + (size_t)t * H))[h4];
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    if (y) ((float4*)(y + (size_t)t * H))[h4] = acc;
+    if (x_res) {
+        if (BF16) {
+            uint2* xp = (uint2*)((uint16_t*)x_res + (size_t)t * H) + h4;
+            uint2 xv = *xp;
+            float a = bf16_f32(xv.x & 0xFFFFu) + acc.x, b = bf16_f32(xv.x >> 16) + acc.y;
+            float c = bf16_f32(xv.y & 0xFFFFu) + acc.z, d = bf16_f32(xv.y >> 16) + acc.w;
+            *xp = make_uint2(f32_bf16_rne(a) | (f32_bf16_rne(b) << 16),
+                             f32_bf16_rne(c) | (f32_bf16_rne(d) << 16));
+        } else {
+            float4* xp = (float4*)((float*)x_res + (size_t)t * H) + h4;
+            float4 xv = *xp;
+            *xp = make_float4(xv.x + acc.x, xv.y + acc.y, xv.z + acc.z, xv.w + acc.w);
+        }
+    }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_residual(void* __restrict__ x, const float* __restrict__ y,
+                                                  int64_t n) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    if (BF16) {
+        uint16_t* xp = (uint16_t*)x;
+        xp[i] = (uint16_t)f32_bf16_rne(bf16_f32(xp[i]) + y[i]);
+    } else {
+        float* xp = (float*)x;
+        xp[i] = xp[i] + y[i];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const int32_t* ids, const int32_t* e2slot, int all_resident, int T,
+                          int k, int E, int has_shared, const void* x, int act_bf16, int H,
+                          PermuteBufs b, hipStream_t s) {
+    const int P = T * k;
+    const int nchunks = (P + kChunk - 1) / kChunk;
+    const int row_bytes = H * (act_bf16 ? 2 : 4);
+    if (nchunks > 0)
+        k_hist<<<nchunks, 1024, 0, s>>>(ids, e2slot, all_resident, P, E, b.chunk_cnt);
+    k_scan<<<1, 1024, 0, s>>>(b.chunk_cnt, nchunks, E, has_shared, T, b.counts, b.offsets,
+                              b.tile_off);
+    if (nchunks > 0)
+        k_scatter<<<nchunks, 1024, 0, s>>>(ids, e2slot, all_resident, P, k, E, b.chunk_cnt,
+                                           b.offsets, b.perm_pair, (const uint8_t*)x, row_bytes,
+                                           (uint8_t*)b.x_perm);
+    if (has_shared)
+        k_shared_rows<<<(T + 3) / 4, 256, 0, s>>>(T, P, b.offsets, E, b.perm_pair,
+                                                  (const uint8_t*)x, row_bytes,
+                                                  (uint8_t*)b.x_perm);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* o_pairs, const int32_t* ids, const int32_t* e2slot,
+                          int all_resident, int has_shared, const float* y_host, int T, int k,
+                          int H, float* y, void* x_res, int act_bf16, hipStream_t s, int E) {
+    dim3 grid((H / 4 + 255) / 256, T);
+    if (act_bf16)
+        k_combine<true><<<grid, 256, 0, s>>>(o_pairs, ids, e2slot, all_resident, has_shared,
+                                             y_host, T, k, E, H, y, x_res);
+    else
+        k_combine<false><<<grid, 256, 0, s>>>(o_pairs, ids, e2slot, all_resident, has_shared,
+                                              y_host, T, k, E, H, y, x_res);
+    return hipGetLastError();
+}
+
+hipError_t launch_residual(void* x, const float* y, int64_t n, int act_bf16, hipStream_t s) {
+    int64_t blocks = (n + 255) / 256;
+    if (act_bf16)
+        k_residual<true><<<(unsigned)blocks, 256, 0, s>>>(x, y, n);
+    else
+        k_residual<false><<<(unsigned)blocks, 256, 0, s>>>(x, y, n);
+    return hipGetLastError();
+}
+
+}  // namespace eo

@@ -1,0 +1,339 @@
+// Expert-cache lookup, global LRU update and miss plan (one workgroup).
+//
+// zhichai.net article, section 2: the Decode paragraph has most routed experts
+// hit a device-resident LRU expert cache and splits the m misses of a step
+// by the measured bandwidths, q* = m * B_P / B_H filled over PCIe and the rest
+// executed on the host; the LRU paragraph makes the cache one global LRU over
+// all layers. Integer rules (exactly reproducible):
+//   clock += 1 per call; hits get stamp = clock;
+//   q = min(m, floor((c + m*B_P)/B_H)), c <- min(c + m*B_P - q*B_H, B_H - 1);
+//   q_fill = min(q, C - hits); misses ranked by (tokens desc, id asc), the
+//   first q_fill filled, the rest host-executed and not inserted;
+//   evict max(0, q_fill - empty) slots not touched this call in
+//   (stamp asc, key asc) order; empty + freed slots, ascending, go to the
+//   fills in rank order.
+// The slot table is staged in LDS for the call (C <= kMaxSlotsLds) and
+// written back; key2slot (L*E entries) stays in global memory, each entry
+// touched by one thread only.
+#include "dev_common.h"
+#include "eo_internal.h"
+
+namespace eo {
+
+namespace {
+
+constexpr int kThreads = 1024;
+
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+        uint32_t lo = __shfl_xor((uint32_t)v, s, 64);
+        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), s, 64);
+        uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o < v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
+    return v;
+}
+
+// Block-wide sum; every thread gets the total.
+__device__ int block_sum(int v, int* red) {
+    v = wave_sum_i32(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    int tot = 0;
+    for (int i = 0; i < kThreads / 64; ++i) tot += red[i];
+    return tot;
+}
+
+// Block-wide exclusive prefix of v in thread order; returns (prefix, total).
+__device__ int2 block_scan(int v, int* red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+        int o = __shfl_up(incl, s, 64);
+        if (lane >= s) incl += o;
+    }
+    __syncthreads();
+    if (lane == 63) red[wave] = incl;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int i = 0; i < kThreads / 64; ++i) {
+        if (i < wave) base += red[i];
+        tot += red[i];
+    }
+    return make_int2(base + incl - v, tot);
+}
+
+__device__ uint64_t block_min_u64(uint64_t v, uint64_t* red) {
+    v = wave_min_u64(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    uint64_t m = ~0ull;
+    for (int i = 0; i < kThreads / 64; ++i) m = red[i] < m ? red[i] : m;
+    return m;
+}
+
+__global__ __launch_bounds__(kThreads) void k_plan(
+    int layer, const int32_t* __restrict__ ids, const float* __restrict__ w,
+    const uint8_t* __restrict__ x, int x_bytes, int T, int k, int E, int C,
+    int32_t* __restrict__ g_slot_key, int64_t* __restrict__ g_slot_stamp,
+    int32_t* __restrict__ key2slot, DevState* __restrict__ st, DevPlan* __restrict__ dp,
+    DevPlan* __restrict__ hp, int32_t* __restrict__ h_ids, float* __restrict__ h_w,
+    uint8_t* __restrict__ h_x) {
+    extern __shared__ int64_t smem64[];
+    int64_t* s_stamp = smem64;                    // [C]
+    int32_t* s_key = (int32_t*)(smem64 + C);      // [C]
+    __shared__ int cnt[kMaxE];
+    __shared__ int kind[kMaxE];  // 0 unrouted, 1 hit, 2 miss
+    __shared__ int slot_of[kMaxE];
+    __shared__ int red[kThreads / 64];
+    __shared__ uint64_t red64[kThreads / 64];
+    __shared__ int s_err;
+    __shared__ long long s_clock, s_credit;
+    __shared__ int s_m, s_h, s_q, s_qfill;
+    __shared__ int fill_e[kMaxE];
+
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
+    if (tid == 0) s_err = 0;
+    for (int s = tid; s < C; s += kThreads) {
+        s_key[s] = g_slot_key[s];
+        s_stamp[s] = g_slot_stamp[s];
+    }
+    __syncthreads();
+
+    // token counts per expert; ids must be in range and distinct per token
+    for (int p = tid; p < T * k; p += kThreads) {
+        int e = ids[p];
+        if (e < 0 || e >= E) {
+            s_err = 1;
+            continue;
+        }
+        int t = p / k, j = p - t * k;
+        for (int jj = 0; jj < j; ++jj)
+            if (ids[t * k + jj] == e) s_err = 2;
+        atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    if (s_err) {
+        if (tid == 0) {
+            int seq = st->seq + 1;
+            st->seq = seq;
+            dp->pad = s_err;
+            hp->pad = s_err;
+            dp->seq = seq;
+            __threadfence_system();
+            __hip_atomic_store(&hp->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+        return;
+    }
+    if (tid == 0) s_clock = st->clock + 1;
+    __syncthreads();
+    const int64_t clock = s_clock;
+
+    // hits and misses
+    for (int e = tid; e < E; e += kThreads) {
+        int kd = 0, sl = -1;
+        if (cnt[e] > 0) {
+            int key = layer * E + e;
+            int s = key2slot[key];
+            if (s >= 0) {
+                kd = 1;
+                sl = s;
+                s_stamp[s] = clock;
+            } else {
+                kd = 2;
+            }
+        }
+        kind[e] = kd;
+        slot_of[e] = sl;
+    }
+    __syncthreads();
+
+    // counts (E <= kThreads: one expert per thread)
+    int my_e = tid < E ? tid : -1;
+    int is_hit = (my_e >= 0 && kind[my_e] == 1) ? 1 : 0;
+    int is_miss = (my_e >= 0 && kind[my_e] == 2) ? 1 : 0;
+    int2 hs = block_scan(is_hit, red);
+    if (is_hit) {
+        dp->hit_e[hs.x] = hp->hit_e[hs.x] = my_e;
+        dp->hit_slot[hs.x] = hp->hit_slot[hs.x] = slot_of[my_e];
+    }
+    int m = block_sum(is_miss, red);
+    if (tid == 0) {
+        s_h = hs.y;
+        s_m = m;
+        long long c = st->credit, bp = st->bp, bh = st->bh;
+        long long q = (c + (long long)m * bp) / bh;
+        if (q > m) q = m;
+        long long c2 = c + (long long)m * bp - q * bh;
+        if (c2 > bh - 1) c2 = bh - 1;
+        s_credit = c2;
+        s_q = (int)q;
+        int room = C - hs.y;
+        s_qfill = (int)(q < room ? q : room);
+    }
+    __syncthreads();
+    const int q_fill = s_qfill;
+
+    // rank misses by (count desc, id asc)
+    if (is_miss) {
+        int c0 = cnt[my_e], r = 0;
+        for (int e = 0; e < E; ++e)
+            if (kind[e] == 2 && (cnt[e] > c0 || (cnt[e] == c0 && e < my_e))) ++r;
+        if (r < q_fill) {
+            fill_e[r] = my_e;
+            dp->fill_e[r] = hp->fill_e[r] = my_e;
+        } else {
+            dp->host_e[r - q_fill] = hp->host_e[r - q_fill] = my_e;
+        }
+    }
+
+    // victims among occupied slots not touched this call (stamp < clock)
+    int empty = 0;
+    for (int s = tid; s < C; s += kThreads) empty += (s_key[s] < 0);
+    empty = block_sum(empty, red);
+    int need = q_fill - empty;
+    int n_ev = 0;
+    for (int r = 0; r < need; ++r, ++n_ev) {
+        uint64_t best = ~0ull;
+        for (int s = tid; s < C; s += kThreads) {
+            if (s_key[s] >= 0 && s_stamp[s] < clock) {
+                uint64_t v = ((uint64_t)s_stamp[s] << 24) | (uint64_t)s_key[s];
+                best = v < best ? v : best;
+            }
+        }
+        best = block_min_u64(best, red64);
+        if (best == ~0ull) break;  // unreachable: q_fill <= C - hits
+        int vkey = (int)(best & 0xFFFFFFull);
+        int vslot = key2slot[vkey];
+        __syncthreads();
+        if (tid == 0) {
+            dp->evict_key[r] = hp->evict_key[r] = vkey;
+            key2slot[vkey] = -1;
+            s_key[vslot] = -1;
+        }
+        __syncthreads();
+    }
+
+    // empty slots in ascending order go to the fills in rank order
+    const int per = (C + kThreads - 1) / kThreads;
+    const int s_lo = min(C, tid * per), s_hi = min(C, s_lo + per);
+    int my_empty = 0;
+    for (int s = s_lo; s < s_hi; ++s) my_empty += (s_key[s] < 0);
+    int2 es = block_scan(my_empty, red);
+    int r = es.x;
+    for (int s = s_lo; s < s_hi && r < q_fill; ++s) {
+        if (s_key[s] < 0) {
+            int e = fill_e[r];
+            int key = layer * E + e;
+            s_key[s] = key;
+            s_stamp[s] = clock;
+            key2slot[key] = s;
+            slot_of[e] = s;
+            dp->fill_slot[r] = hp->fill_slot[r] = s;
+            ++r;
+        }
+    }
+    __syncthreads();
+
+    for (int s = tid; s < C; s += kThreads) {
+        g_slot_key[s] = s_key[s];
+        g_slot_stamp[s] = s_stamp[s];
+    }
+    for (int e = tid; e < E; e += kThreads) {
+        dp->e2slot[e] = slot_of[e];
+        dp->count[e] = cnt[e];
+    }
+    const int n_hit = s_h, n_host = s_m - q_fill, n_evict = n_ev;
+    if (tid == 0) {
+        dp->pad = 0;
+        dp->layer = layer;
+        dp->T = T;
+        dp->k = k;
+        dp->m = s_m;
+        dp->q = s_q;
+        dp->q_fill = q_fill;
+        dp->n_hit = n_hit;
+        dp->n_host = n_host;
+        dp->n_evict = n_evict;
+        dp->clock = clock;
+        dp->credit = s_credit;
+        st->clock = clock;
+        st->credit = s_credit;
+    }
+    __syncthreads();  // dp lists complete (same workgroup)
+
+    // host mirror: lists were written alongside the device copy; add ids, w, x
+    if (h_ids && h_w) {
+        for (int p = tid; p < T * k; p += kThreads) {
+            h_ids[p] = ids[p];
+            h_w[p] = w[p];
+        }
+    }
+    if (h_x && n_host > 0) {
+        const uint4* xs = (const uint4*)x;
+        uint4* xd = (uint4*)h_x;
+        for (int i = tid; i < x_bytes / 16; i += kThreads) xd[i] = xs[i];
+    }
+    if (tid == 0) {
+        hp->pad = 0;
+        hp->layer = layer;
+        hp->T = T;
+        hp->k = k;
+        hp->m = s_m;
+        hp->q = s_q;
+        hp->q_fill = q_fill;
+        hp->n_hit = n_hit;
+        hp->n_host = n_host;
+        hp->n_evict = n_evict;
+        hp->clock = clock;
+        hp->credit = s_credit;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int seq = st->seq + 1;
+        st->seq = seq;
+        dp->seq = seq;
+        __threadfence_system();
+        __hip_atomic_store(&hp->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+}
+
+}  // namespace
+
+constexpr int kMaxSlotsLds = 8192;
+
+int plan_max_slots() { return kMaxSlotsLds; }
+
+hipError_t launch_plan(int layer, const int32_t* ids, const float* w, const void* x,
+                       size_t x_bytes, int T, int k, int E, int64_t C, int32_t* slot_key,
+                       int64_t* slot_stamp, int32_t* key2slot, DevState* st, DevPlan* d_plan,
+                       DevPlan* h_plan, int32_t* h_ids, float* h_w, void* h_x, hipStream_t s) {
+    static bool attr_set = false;
+    size_t lds = 12 * (size_t)C;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_plan,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           12 * kMaxSlotsLds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    k_plan<<<1, kThreads, lds, s>>>(layer, ids, w, (const uint8_t*)x, (int)x_bytes, T, k, E,
+                                    (int)C, slot_key, slot_stamp, key2slot, st, d_plan, h_plan,
+                                    h_ids, h_w, (uint8_t*)h_x);
+    return hipGetLastError();
+}
+
+}  // namespace eo

@@ -1,0 +1,231 @@
+/*
+ * eo.h — MoE expert-layer forward over a device-resident LRU expert cache,
+ * backed by an expert pool in pinned host memory, on one AMD MI355X (gfx950).
+ *
+ * The method (FreeToken, "Efficient Edge-Native MoE Serving with
+ * Bandwidth-Adaptive Execution"; zhichai.net article, section 2):
+ *   route -> look up the expert cache -> plan the misses -> fill over PCIe or
+ *   execute on the host cores -> grouped SwiGLU expert FFN -> weighted combine.
+ * Decode (Decode paragraph): of the m cache misses of a layer call,
+ * q* = m * B_P / B_H are filled over PCIe into the cache, the rest run on the
+ * host cores from host memory; B_P and B_H are measured on the machine.
+ * Cache (LRU paragraph): one global LRU over all layers' experts.
+ * Prefill (Prefill paragraph): whole layers stream over PCIe with double
+ * buffering; layer l+1's experts are copied while layer l computes.
+ *
+ * Conventions for every call:
+ *   - Returns eo_status; never throws. On failure eo_last_error() holds a
+ *     message (thread-local, valid until the next call on that thread).
+ *   - "device" pointers are HIP device memory owned by the caller; "host"
+ *     pointers are ordinary host memory owned by the caller unless stated.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Step calls are asynchronous and ordered on that stream; results in
+ *     caller buffers are valid once the stream has reached that point.
+ *   - Asynchronous device errors surface at the next call or at eo_sync() as
+ *     EO_ERR_HIP.
+ *   - An engine is used from one host thread at a time.
+ * Tensor layouts are row-major. Activations are bf16 (act_bf16 = 1) or fp32.
+ */
+#ifndef EO_H
+#define EO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EO_OK = 0,
+    EO_ERR_INVALID_ARG = -1,
+    EO_ERR_OOM = -2,
+    EO_ERR_HIP = -3,
+    EO_ERR_STATE = -4,
+    EO_ERR_UNSUPPORTED = -5
+} eo_status;
+
+/* Expert weight storage formats (juejin.cn overview, section 5: MXFP4, NVFP4,
+ * FP8 and BF16; fp32 for small test models). Packed expert block, hidden H,
+ * intermediate I; W13 = [W_gate; W_up] (2I rows of H), W2 = W_down (H rows of
+ * I); quantisation blocks run along rows; two fp4 codes per byte, the even
+ * element in the low nibble:
+ *   FP32 : W13 f32 | W2 f32
+ *   BF16 : W13 bf16 | W2 bf16
+ *   MXFP4: W13 e2m1 | W2 e2m1 | W13 e8m0 per 32 | W2 e8m0 per 32
+ *   NVFP4: W13 e2m1 | W2 e2m1 | W13 e4m3 per 16 | W2 e4m3 per 16 | f32 g_gate, g_up, g_down
+ *   FP8  : W13 e4m3fn | W2 e4m3fn | f32 scale per W13 row | f32 scale per W2 row
+ * Values: MXFP4 e2m1 * 2^(e8m0-127); NVFP4 (e2m1 * e4m3) * g; FP8 e4m3 * s_row. */
+typedef enum { EO_W_FP32 = 0, EO_W_BF16 = 1, EO_W_MXFP4 = 2, EO_W_NVFP4 = 3, EO_W_FP8 = 4 } eo_wfmt;
+
+typedef struct {
+    int32_t layers;         /* MoE layers L */
+    int32_t experts;        /* routed experts per layer E (<= 1024) */
+    int32_t top_k;          /* experts per token k (<= 16, <= E) */
+    int32_t hidden;         /* H, multiple of 64 */
+    int32_t inter;          /* I, multiple of 64 */
+    int32_t shared_experts; /* 0 or 1 always-on shared expert per layer (device-resident) */
+    int32_t wfmt;           /* eo_wfmt */
+    int32_t act_bf16;       /* 1: activations bf16 (needs wfmt != FP32); 0: fp32 (needs wfmt == FP32) */
+    int64_t cache_slots;    /* C: device expert-cache capacity in experts (>= 0) */
+    int32_t max_tokens;     /* largest T of any step call */
+    int32_t host_threads;   /* host-core expert routine threads; 0 = hardware concurrency, capped at 16 */
+    int32_t device;         /* HIP device ordinal */
+} eo_config;
+
+typedef struct eo_engine eo_engine;
+
+/* Largest E for which plans are reported (eo_plan_host arrays). */
+#define EO_MAX_EXPERTS 1024
+
+/* Plan of the last lookup call (zhichai.net article, section 2, Decode
+ * paragraph). Lists hold the experts of `layer`. */
+typedef struct {
+    int32_t layer;
+    int32_t m;          /* misses */
+    int32_t q;          /* misses the bandwidth split sends to PCIe */
+    int32_t q_fill;     /* of those, filled (q clamped by free capacity C - hits) */
+    int32_t n_hit, n_host, n_evict, pad_;
+    int64_t clock;      /* lookup calls so far (the LRU clock) */
+    int64_t credit;     /* split remainder after this call, 0 <= credit < B_H */
+    int32_t hit_expert[EO_MAX_EXPERTS], hit_slot[EO_MAX_EXPERTS];   /* expert id ascending */
+    int32_t fill_expert[EO_MAX_EXPERTS], fill_slot[EO_MAX_EXPERTS]; /* rank order */
+    int32_t host_expert[EO_MAX_EXPERTS];                              /* rank order */
+    int32_t evicted_key[EO_MAX_EXPERTS];                              /* key = layer*E + expert */
+} eo_plan_host;
+
+typedef struct {
+    int64_t lookups, hits, misses, fills, host_experts;
+    int64_t pcie_bytes;  /* bytes copied host->device by fills and prefill streaming */
+    int64_t host_bytes;  /* expert bytes read by the host-core routine */
+    int64_t prefill_layers;
+} eo_stats;
+
+/* Create an engine on cfg->device: allocates the pinned host expert pool
+ * (L*E blocks, each padded to 4 KiB), C device cache slots, the shared experts,
+ * router copies, plan buffers, a copy stream and the host thread pool. The pool
+ * and the shared experts start zeroed, the cache empty, B_P = B_H = 1.
+ * Errors: INVALID_ARG (shape limits above), UNSUPPORTED (format / activation
+ * combination), OOM (pinned or device allocation failed), HIP. */
+eo_status eo_create(const eo_config* cfg, eo_engine** out);
+
+/* Frees everything the engine owns; waits for its outstanding work. */
+eo_status eo_destroy(eo_engine* e);
+
+/* Host address and size of one pool entry (pinned memory owned by the
+ * engine, valid until eo_destroy). The caller writes the packed expert block
+ * there before the first forward call that may need it. */
+eo_status eo_pool_expert(eo_engine* e, int32_t layer, int32_t expert, void** host_ptr,
+                         uint64_t* bytes);
+
+/* Copy one layer's shared-expert block (host bytes, `bytes` must equal the
+ * expert block size) to its device home. Synchronous. */
+eo_status eo_set_shared_expert(eo_engine* e, int32_t layer, const void* host_block,
+                               uint64_t bytes);
+
+/* Copy router weights R_l, fp32 [E, H] host, to the device. Synchronous. */
+eo_status eo_set_router(eo_engine* e, int32_t layer, const float* host_w);
+
+/* Measure B_P (one expert host->device copy into a cache slot) and B_H (the
+ * host-core expert routine over one expert at T = 1, with the engine's thread
+ * count), each the median of several timed runs over different experts,
+ * floored to integer MB/s, and use them for the miss split (zhichai.net
+ * article, section 2, Decode paragraph: measured on the machine with real
+ * tensor shapes). Overwrites cache slot 0's bytes; resets the cache to empty
+ * and the split credit to 0. Either output pointer may be NULL. */
+eo_status eo_measure_bandwidth(eo_engine* e, uint32_t* bp_mbps, uint32_t* bh_mbps);
+
+/* Set B_P and B_H (MB/s, both > 0) directly; clips the credit below B_H. */
+eo_status eo_set_bandwidth(eo_engine* e, uint32_t bp_mbps, uint32_t bh_mbps);
+
+/* ---- step calls (stream-ordered; x, ids, w, y are device pointers) ---- */
+
+/* Router: z = x . R_l^T in fp32 (64 strided fused multiply-add chains, then an
+ * xor butterfly), top-k by (z desc, id asc), w = softmax over the k selected.
+ * forced_ids (device [T,k] or NULL): take these ids in this order (routing
+ * trace replay) and return the softmax of z at them. ids: int32 [T,k];
+ * w: fp32 [T,k]. */
+eo_status eo_route(eo_engine* e, int32_t layer, const void* x, int32_t T,
+                   const int32_t* forced_ids, int32_t* ids, float* w, void* stream);
+
+/* Cache lookup, LRU update and miss plan for the distinct experts in ids
+ * [T,k] (one LRU clock tick). Runs on the device; the plan is kept by the
+ * engine for eo_fill / eo_host_execute / eo_expert_ffn_combine and returned by
+ * eo_last_plan. Split: q = min(m, floor((c + m*B_P)/B_H)),
+ * c <- min(c + m*B_P - q*B_H, B_H - 1), q_fill = min(q, C - hits); misses
+ * ranked by (tokens desc, id asc); victims by (stamp asc, key asc) among slots
+ * not touched by this call; freed and empty slots go to fills in slot order;
+ * host-executed misses are not inserted. */
+eo_status eo_lookup_plan(eo_engine* e, int32_t layer, const int32_t* ids, int32_t T,
+                         void* stream);
+
+/* Issue the last plan's fills (pinned pool -> cache slot) on the engine's copy
+ * stream and make `stream` wait for them. Waits on the host for the plan.
+ * EO_ERR_STATE without a pending plan. */
+eo_status eo_fill(eo_engine* e, void* stream);
+
+/* Run the last plan's host-list experts on the host cores for the tokens
+ * routed to them (x, ids, w as passed to the lookup: x device [T,H]) and stage
+ * their weighted sum for the next eo_expert_ffn_combine. Waits on the host for
+ * the plan and blocks while the host routine runs. */
+eo_status eo_host_execute(eo_engine* e, const void* x, const int32_t* ids, const float* w,
+                          void* stream);
+
+/* Device part of the layer for the last plan: permute tokens by expert,
+ * grouped SwiGLU FFN on the resident experts (decode: dequant-GEMV), the
+ * shared expert, and the weighted combine plus any staged host results:
+ * y fp32 [T,H] = sum_j w[t,j] * FFN_{e_j}(x_t) + FFN_shared(x_t).
+ * No residual. Consumes the plan. */
+eo_status eo_expert_ffn_combine(eo_engine* e, int32_t layer, const void* x, const int32_t* ids,
+                                const float* w, float* y, void* stream);
+
+/* All of the above for one layer: y fp32 [T,H] (no residual). */
+eo_status eo_moe_layer(eo_engine* e, int32_t layer, const void* x, float* y, int32_t T,
+                       const int32_t* forced_ids, void* stream);
+
+/* One decode step through all layers, in place: x_inout [T,H] (activation
+ * dtype) becomes x + sum over layers of the MoE outputs (x_{l+1} = x_l + y_l,
+ * stored in the activation dtype). forced_ids: device [L, T, k] or NULL. */
+eo_status eo_decode_step(eo_engine* e, void* x_inout, int32_t T, const int32_t* forced_ids,
+                         void* stream);
+
+/* Prefill of T tokens (T <= max_tokens) through all layers, in place, with
+ * full-layer double-buffered streaming of each layer's E experts from the
+ * pool (the cache is neither read nor updated). double_buffer = 0 serialises
+ * copy and compute (ablation). */
+eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t double_buffer,
+                     void* stream);
+
+/* Optional per-layer capture for tests, device buffers written by
+ * eo_decode_step / eo_prefill (NULL disables): x_in [L, T, H] layer inputs
+ * (activation dtype), y [L, T, H] fp32 MoE outputs, ids [L, T, k], w [L, T, k].
+ * Capacity is given in tokens per layer. */
+eo_status eo_set_capture(eo_engine* e, void* x_in, float* y, int32_t* ids, float* w,
+                         int32_t tokens_per_layer);
+
+/* ---- introspection ---- */
+/* Slot table and counters (host buffers of C entries each). Synchronous. */
+eo_status eo_cache_snapshot(eo_engine* e, int32_t* slot_key, int64_t* slot_stamp, int64_t* clock,
+                            int64_t* credit);
+/* The last lookup's plan. Synchronous. */
+eo_status eo_last_plan(eo_engine* e, eo_plan_host* out);
+/* Dequantise one pool expert with the device decoder: out_host fp32
+ * [W_gate (I*H) | W_up (I*H) | W_down (H*I)]. Synchronous. */
+eo_status eo_dequant(eo_engine* e, int32_t layer, int32_t expert, float* out_host);
+eo_status eo_stats_get(eo_engine* e, eo_stats* out);
+/* Device time of the last eo_prefill's expert GEMMs and of decode expert
+ * GEMVs since the last reset, from HIP events on the compute stream:
+ * ms totals and launch counts. reset != 0 clears after reading. */
+eo_status eo_kernel_times(eo_engine* e, double* gemv_ms, int64_t* gemv_launches,
+                          double* gemm_ms, int64_t* gemm_launches, int32_t reset);
+/* Enable (1) or disable (0) the per-launch timing events behind eo_kernel_times. */
+eo_status eo_set_timing(eo_engine* e, int32_t enable);
+/* Size in bytes of one packed expert block (unpadded). */
+uint64_t eo_expert_bytes(int32_t hidden, int32_t inter, int32_t wfmt);
+/* Wait for the engine's streams and the device; report async HIP errors. */
+eo_status eo_sync(eo_engine* e);
+const char* eo_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EO_H */

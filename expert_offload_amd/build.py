@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libeo.so")
 
 HIP_SOURCES = ["engine.hip", "k_router.hip", "k_plan.hip", "k_permute.hip", "k_gemm.hip",
                "k_gemv.hip", "k_dequant.hip"]
-HOST_SOURCES = ["host_ffn.cpp"]
+HOST_SOURCES = ["host_ffn.cpp", "layout.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU instructions are kept out of the device code.

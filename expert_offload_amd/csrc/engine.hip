@@ -55,29 +55,6 @@ struct TimedPair {
 
 }  // namespace
 
-namespace eo {
-
-Layout layout_of(int H, int I, int fmt) {
-    Layout l;
-    const uint64_t n13 = 2ull * I * H, n2 = (uint64_t)H * I;
-    switch (fmt) {
-    case EO_W_FP32: l.d13 = 0; l.d2 = 4 * n13; l.s13 = l.s2 = l.gl = l.bytes = 4 * (n13 + n2); break;
-    case EO_W_BF16: l.d13 = 0; l.d2 = 2 * n13; l.s13 = l.s2 = l.gl = l.bytes = 2 * (n13 + n2); break;
-    case EO_W_MXFP4:
-        l.d13 = 0; l.d2 = n13 / 2; l.s13 = l.d2 + n2 / 2; l.s2 = l.s13 + n13 / 32;
-        l.gl = l.bytes = l.s2 + n2 / 32; break;
-    case EO_W_NVFP4:
-        l.d13 = 0; l.d2 = n13 / 2; l.s13 = l.d2 + n2 / 2; l.s2 = l.s13 + n13 / 16;
-        l.gl = l.s2 + n2 / 16; l.bytes = l.gl + 12; break;
-    case EO_W_FP8:
-        l.d13 = 0; l.d2 = n13; l.s13 = l.d2 + n2; l.s2 = l.s13 + 4 * 2ull * I;
-        l.gl = l.bytes = l.s2 + 4ull * H; break;
-    default: break;
-    }
-    return l;
-}
-
-}  // namespace eo
 
 struct eo_engine {
     eo_config cfg{};
@@ -235,7 +212,7 @@ eo_status wait_plan(eo_engine* e) {
                 return fail(EO_ERR_HIP, std::string("device error while waiting for plan: ") +
                                             hipGetErrorString(he));
             }
-            if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(60)) {
+            if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(20)) {
                 e->plan_pending = false;
                 return fail(EO_ERR_HIP, "timed out waiting for the device plan");
             }

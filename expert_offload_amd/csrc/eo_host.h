@@ -3,6 +3,7 @@
 #pragma once
 
 #include <cstdint>
+#include <functional>
 #include <vector>
 
 #include "../../include/eo.h"
@@ -36,5 +37,7 @@ void host_ffn(ThreadPool* pool, const HostJob& job, std::vector<float>& scratch)
 ThreadPool* threadpool_create(int n);
 void threadpool_destroy(ThreadPool* p);
 int threadpool_size(ThreadPool* p);
+// Run fn(task) for task in [0, ntasks) on the pool (the calling thread included).
+void threadpool_run(ThreadPool* p, int ntasks, const std::function<void(int)>& fn);
 
 }  // namespace eo

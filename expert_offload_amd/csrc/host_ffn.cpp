@@ -27,7 +27,9 @@ namespace eo {
 class ThreadPool {
   public:
     explicit ThreadPool(int n) : n_(std::max(1, n)) {
-        for (int i = 1; i < n_; ++i) workers_.emplace_back([this] { loop(); });
+        // every worker starts from generation 0, the value before any run(): a
+        // worker that is scheduled late must still take part in run() #1
+        for (int i = 1; i < n_; ++i) workers_.emplace_back([this] { loop(0); });
     }
     ~ThreadPool() {
         {
@@ -68,8 +70,7 @@ class ThreadPool {
             (*fn_)(i);
         }
     }
-    void loop() {
-        uint64_t seen = gen_.load(std::memory_order_acquire);
+    void loop(uint64_t seen) {
         for (;;) {
             // spin briefly for low dispatch latency, then sleep
             int spins = 0;
@@ -102,6 +103,9 @@ class ThreadPool {
 ThreadPool* threadpool_create(int n) { return new ThreadPool(n); }
 void threadpool_destroy(ThreadPool* p) { delete p; }
 int threadpool_size(ThreadPool* p) { return p->size(); }
+void threadpool_run(ThreadPool* p, int ntasks, const std::function<void(int)>& fn) {
+    p->run(ntasks, fn);
+}
 
 // ------------------------------------------------------------ decoding
 namespace {

@@ -25,7 +25,8 @@ from . import router as _router
 
 def silu(u: np.ndarray) -> np.ndarray:
     u = np.asarray(u, dtype=np.float64)
-    return u / (1.0 + np.exp(-u))
+    with np.errstate(over="ignore"):  # e^-u -> inf gives the limit silu(u) -> -0
+        return u / (1.0 + np.exp(-u))
 
 
 def ffn(wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, x: np.ndarray) -> np.ndarray:

@@ -1,0 +1,85 @@
+// Test driver for the host-core expert routine and its thread pool (CPU only).
+//   host_driver pool            : create a pool and run at once, many times
+//   host_driver ffn <dir>       : read meta.txt, block.bin, x.bin, ids.bin, w.bin from <dir>,
+//                                 run host_ffn with every routed expert on the host,
+//                                 write y.bin (fp32 [T,H])
+#include <atomic>
+#include <chrono>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <unistd.h>
+#include <vector>
+
+#include "../../expert_offload_amd/csrc/eo_host.h"
+
+static std::vector<char> slurp(const std::string& p) {
+    FILE* f = fopen(p.c_str(), "rb");
+    if (!f) { fprintf(stderr, "cannot open %s\n", p.c_str()); exit(2); }
+    fseek(f, 0, SEEK_END);
+    long n = ftell(f);
+    fseek(f, 0, SEEK_SET);
+    std::vector<char> b(n);
+    if (fread(b.data(), 1, n, f) != (size_t)n) exit(2);
+    fclose(f);
+    return b;
+}
+
+int main(int argc, char** argv) {
+    if (argc >= 2 && !strcmp(argv[1], "pool")) {
+        for (int it = 0; it < 500; ++it) {
+            eo::ThreadPool* p = eo::threadpool_create(8);
+            std::atomic<int> sum{0};
+            std::atomic<bool> done{false};
+            std::thread wd([&] {
+                auto t0 = std::chrono::steady_clock::now();
+                while (!done) {
+                    if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(10)) {
+                        printf("DEADLOCK %d\n", it);
+                        fflush(stdout);
+                        _exit(3);
+                    }
+                    std::this_thread::sleep_for(std::chrono::milliseconds(2));
+                }
+            });
+            eo::threadpool_run(p, 37, [&](int i) { sum += i; });
+            eo::threadpool_run(p, 5, [&](int i) { sum += i; });
+            done = true;
+            wd.join();
+            eo::threadpool_destroy(p);
+            if (sum != 666 + 10) { printf("BAD SUM %d\n", (int)sum); return 4; }
+        }
+        printf("ok\n");
+        return 0;
+    }
+    if (argc >= 3 && !strcmp(argv[1], "ffn")) {
+        std::string d = argv[2];
+        int fmt, H, I, T, k, E, threads;
+        FILE* m = fopen((d + "/meta.txt").c_str(), "r");
+        if (!m || fscanf(m, "%d %d %d %d %d %d %d", &fmt, &H, &I, &T, &k, &E, &threads) != 7) return 2;
+        fclose(m);
+        std::vector<char> blocks = slurp(d + "/blocks.bin"), x = slurp(d + "/x.bin"),
+                          ids = slurp(d + "/ids.bin"), w = slurp(d + "/w.bin");
+        eo::Layout lay = eo::layout_of(H, I, fmt);
+        std::vector<const uint8_t*> table(E);
+        for (int e = 0; e < E; ++e) table[e] = (const uint8_t*)blocks.data() + (size_t)e * lay.bytes;
+        std::vector<float> y((size_t)T * H, 0.0f), scratch;
+        eo::ThreadPool* p = eo::threadpool_create(threads);
+        eo::HostJob jb;
+        jb.fmt = fmt; jb.lay = lay; jb.H = H; jb.I = I; jb.T = T; jb.k = k;
+        jb.x = (const float*)x.data();
+        jb.ids = (const int32_t*)ids.data();
+        jb.w = (const float*)w.data();
+        jb.experts = table.data();
+        jb.y = y.data();
+        eo::host_ffn(p, jb, scratch);
+        eo::threadpool_destroy(p);
+        FILE* o = fopen((d + "/y.bin").c_str(), "wb");
+        fwrite(y.data(), sizeof(float), y.size(), o);
+        fclose(o);
+        return 0;
+    }
+    return 1;
+}

@@ -1,0 +1,233 @@
+"""GPU parity of whole layers, decode steps and prefill for every weight format.
+
+Layer outputs are compared with the oracle within 2e-2 * max|ref| (bf16 / fp4 / fp8
+weights, bf16 activations); router ids must match bit for bit. Multi-layer calls
+capture each layer's input on the device and are checked per layer on that input.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import expert_offload_amd as eo  # noqa: E402
+import synth  # noqa: E402
+from oracle import router as OR  # noqa: E402
+from oracle.residency import Residency  # noqa: E402
+from synth.workload import make_engine  # noqa: E402
+from tests.gpu_util import dev, oracle_layer, rel_err  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+FMTS = ["bf16", "fp8", "mxfp4", "nvfp4"]
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def small_shape(fmt, shared=1, layers=2):
+    return synth.LayerShape(f"small_{fmt}", "test", 512, 16, 4, 256, layers,
+                            synth.FMT_NAMES[fmt], 300, 16 * layers, shared=shared)
+
+
+def bf16_to_f32(t):
+    return synth.bf16_bits_to_f32(t.cpu().numpy().view(np.uint16))
+
+
+def check_layer(shape, seed, layer, x_bits, y_dev, ids_dev=None, rows=None):
+    """Oracle on the given bf16 layer input; compare y (and ids) on `rows`."""
+    xf = synth.bf16_bits_to_f32(x_bits)
+    if rows is not None:
+        xf = xf[rows]
+    R = synth.router_weights(seed, layer, shape.experts, shape.hidden)
+    ids, w, _ = OR.route(xf, R, shape.top_k)
+    if ids_dev is not None:
+        got_ids = ids_dev if rows is None else ids_dev[rows]
+        assert np.array_equal(got_ids, ids), f"layer {layer}: router ids differ"
+    ref = oracle_layer(shape, seed, layer, xf, ids, w)
+    got = y_dev if rows is None else y_dev[rows]
+    err = rel_err(got, ref)
+    assert err <= TOL, f"layer {layer}: rel err {err:.3e}"
+    return err
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("T", [300, 1])
+def test_moe_layer_formats(fmt, T):
+    shape = small_shape(fmt)
+    seed = 3
+    e = make_engine(shape, seed)
+    try:
+        eo.eo_set_bandwidth(e, 100, 100)
+        x = synth.activations(seed, 40 + T, T, shape.hidden, 1.0, True)
+        y = torch.zeros((T, shape.hidden), dtype=torch.float32, device="cuda")
+        for layer in range(shape.layers):
+            eo.eo_moe_layer(e, layer, dev(x.view(np.int16)), y, T, None, _stream())
+            torch.cuda.synchronize()
+            check_layer(shape, seed, layer, x, y.cpu().numpy())
+    finally:
+        eo.eo_destroy(e)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+def test_moe_layer_with_host_execution(fmt):
+    # small cache and B_P << B_H: most misses run in the host routine
+    shape = small_shape(fmt)
+    seed = 4
+    e = make_engine(shape, seed, cache_slots=3)
+    try:
+        eo.eo_set_bandwidth(e, 1, 5)
+        for T in (1, 37):
+            x = synth.activations(seed, 60 + T, T, shape.hidden, 1.0, True)
+            y = torch.zeros((T, shape.hidden), dtype=torch.float32, device="cuda")
+            eo.eo_moe_layer(e, 1, dev(x.view(np.int16)), y, T, None, _stream())
+            torch.cuda.synchronize()
+            check_layer(shape, seed, 1, x, y.cpu().numpy())
+        assert eo.eo_stats_get(e)["host_experts"] > 0
+    finally:
+        eo.eo_destroy(e)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_decode_steps_per_layer(fmt):
+    shape = small_shape(fmt, layers=3)
+    seed = 5
+    L, k, H = shape.layers, shape.top_k, shape.hidden
+    steps = 6
+    e = make_engine(shape, seed, cache_slots=10, max_tokens=1)
+    try:
+        eo.eo_set_bandwidth(e, 2, 3)
+        trace = synth.sticky_zipf_trace(seed, steps, L, shape.experts, k)
+        cx = torch.zeros((L, 1, H), dtype=torch.int16, device="cuda")
+        cy = torch.zeros((L, 1, H), dtype=torch.float32, device="cuda")
+        ci = torch.zeros((L, 1, k), dtype=torch.int32, device="cuda")
+        cw = torch.zeros((L, 1, k), dtype=torch.float32, device="cuda")
+        eo.eo_set_capture(e, cx, cy, ci, cw, 1)
+        res = Residency(10, L, shape.experts, 2, 3)
+        for s in range(steps):
+            x = synth.activations(seed, 100 + s, 1, H, 1.0, True)
+            xd = dev(x.view(np.int16))
+            eo.eo_decode_step(e, xd, 1, dev(trace[s].reshape(L, 1, k)), _stream())
+            torch.cuda.synchronize()
+            xin = cx.cpu().numpy().view(np.uint16)
+            assert np.array_equal(xin[0], x)
+            for l in range(L):
+                assert np.array_equal(ci.cpu().numpy()[l, 0], trace[s, l])
+                xf = synth.bf16_bits_to_f32(xin[l])
+                R = synth.router_weights(seed, l, shape.experts, H)
+                ids, w, _ = OR.route(xf, R, k, trace[s, l][None, :])
+                assert np.max(np.abs(cw.cpu().numpy()[l] - w)) <= 1e-6
+                ref = oracle_layer(shape, seed, l, xf, ids, w)
+                assert rel_err(cy.cpu().numpy()[l], ref) <= TOL, (s, l)
+                res.lookup_plan(l, ids)
+                if l + 1 < L:  # next layer's input is bf16(x + y)
+                    nxt = synth.f32_to_bf16_bits(xf + cy.cpu().numpy()[l])
+                    assert np.array_equal(xin[l + 1], nxt), (s, l)
+        keys = np.zeros(10, dtype=np.int32)
+        stamps = np.zeros(10, dtype=np.int64)
+        eo.eo_cache_snapshot(e, keys, stamps)
+        assert list(keys) == res.snapshot()[0] and list(stamps) == res.snapshot()[1]
+    finally:
+        eo.eo_destroy(e)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("db", [1, 0])
+def test_prefill_per_layer(fmt, db):
+    shape = small_shape(fmt, layers=3)
+    seed = 6
+    L, k, H, T = shape.layers, shape.top_k, shape.hidden, 300
+    e = make_engine(shape, seed, cache_slots=0, max_tokens=T)
+    try:
+        x = synth.activations(seed, 200, T, H, 1.0, True)
+        xd = dev(x.view(np.int16))
+        cx = torch.zeros((L, T, H), dtype=torch.int16, device="cuda")
+        cy = torch.zeros((L, T, H), dtype=torch.float32, device="cuda")
+        ci = torch.zeros((L, T, k), dtype=torch.int32, device="cuda")
+        cw = torch.zeros((L, T, k), dtype=torch.float32, device="cuda")
+        eo.eo_set_capture(e, cx, cy, ci, cw, T)
+        eo.eo_prefill(e, xd, T, db, _stream())
+        torch.cuda.synchronize()
+        xin = cx.cpu().numpy().view(np.uint16)
+        ys = cy.cpu().numpy()
+        ids = ci.cpu().numpy()
+        assert np.array_equal(xin[0], x)
+        for l in range(L):
+            check_layer(shape, seed, l, xin[l], ys[l], ids[l])
+        out = xd.cpu().numpy().view(np.uint16)
+        last = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(xin[L - 1]) + ys[L - 1])
+        assert np.array_equal(out, last)
+        st = eo.eo_stats_get(e)
+        assert st["prefill_layers"] == L and st["lookups"] == 0
+    finally:
+        eo.eo_destroy(e)
+
+
+def test_prefill_streaming_matches_cache_path():
+    # streaming must not change the arithmetic: same layer through the cache path
+    shape = small_shape("bf16", layers=1, shared=0)
+    seed = 7
+    T = 300
+    e = make_engine(shape, seed, cache_slots=shape.experts, max_tokens=T)
+    try:
+        eo.eo_set_bandwidth(e, 9, 9)
+        x = synth.activations(seed, 300, T, shape.hidden, 1.0, True)
+        y1 = torch.zeros((T, shape.hidden), dtype=torch.float32, device="cuda")
+        eo.eo_moe_layer(e, 0, dev(x.view(np.int16)), y1, T, None, _stream())
+        cx = torch.zeros((1, T, shape.hidden), dtype=torch.int16, device="cuda")
+        cy = torch.zeros((1, T, shape.hidden), dtype=torch.float32, device="cuda")
+        ci = torch.zeros((1, T, shape.top_k), dtype=torch.int32, device="cuda")
+        cw = torch.zeros((1, T, shape.top_k), dtype=torch.float32, device="cuda")
+        eo.eo_set_capture(e, cx, cy, ci, cw, T)
+        eo.eo_prefill(e, dev(x.view(np.int16)), T, 1, _stream())
+        torch.cuda.synchronize()
+        assert torch.equal(y1, cy[0])
+    finally:
+        eo.eo_destroy(e)
+
+
+def test_decode_determinism():
+    shape = small_shape("bf16", layers=2)
+    outs = []
+    for _ in range(2):
+        e = make_engine(shape, 8, cache_slots=5, max_tokens=1)
+        try:
+            eo.eo_set_bandwidth(e, 3, 4)
+            tr = synth.sticky_zipf_trace(8, 4, 2, shape.experts, shape.top_k)
+            xd = dev(synth.activations(8, 1, 1, shape.hidden, 1.0, True).view(np.int16))
+            for s in range(4):
+                eo.eo_decode_step(e, xd, 1, dev(tr[s].reshape(2, 1, -1)), _stream())
+            torch.cuda.synchronize()
+            keys = np.zeros(5, dtype=np.int32)
+            stamps = np.zeros(5, dtype=np.int64)
+            st = eo.eo_cache_snapshot(e, keys, stamps)
+            outs.append((xd.cpu().numpy().tobytes(), keys.tobytes(), stamps.tobytes(), st))
+        finally:
+            eo.eo_destroy(e)
+    assert outs[0] == outs[1]
+
+
+def test_invalid_forced_ids_rejected():
+    shape = small_shape("bf16", layers=1)
+    e = make_engine(shape, 9, max_tokens=2, fill_pool=False)
+    try:
+        xd = dev(synth.activations(9, 1, 1, shape.hidden, 1.0, True).view(np.int16))
+        y = torch.zeros((1, shape.hidden), dtype=torch.float32, device="cuda")
+        bad = dev(np.array([[0, 0, 1, 2]], dtype=np.int32))  # repeated id
+        with pytest.raises(eo.EOError) as ei:
+            eo.eo_moe_layer(e, 0, xd, y, 1, bad, _stream())
+        assert ei.value.status == eo.EO_ERR_INVALID_ARG
+        bad = dev(np.array([[0, 99, 1, 2]], dtype=np.int32))  # out of range
+        with pytest.raises(eo.EOError):
+            eo.eo_moe_layer(e, 0, xd, y, 1, bad, _stream())
+        # the engine stays usable
+        good = dev(np.array([[3, 0, 1, 2]], dtype=np.int32))
+        eo.eo_moe_layer(e, 0, xd, y, 1, good, _stream())
+        torch.cuda.synchronize()
+        with pytest.raises(eo.EOError):
+            eo.eo_fill(e, _stream())  # no pending plan
+    finally:
+        eo.eo_destroy(e)

@@ -82,8 +82,7 @@ _SIGS = {
     "eo_last_plan": [_P, ctypes.POINTER(eo_plan_host)],
     "eo_dequant": [_P, _I32, _I32, _P],
     "eo_stats_get": [_P, ctypes.POINTER(eo_stats)],
-    "eo_kernel_times": [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64),
-                        ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64), _I32],
+    "eo_kernel_times": [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64), _I32],
     "eo_set_timing": [_P, _I32],
     "eo_expert_bytes": [_I32, _I32, _I32],
     "eo_sync": [_P],
@@ -251,12 +250,11 @@ def eo_set_timing(e, enable: bool) -> None:
 
 
 def eo_kernel_times(e, reset: bool = False) -> dict:
-    a, b = ctypes.c_double(), ctypes.c_double()
-    na, nb = _I64(), _I64()
-    _check(lib().eo_kernel_times(e, ctypes.byref(a), ctypes.byref(na), ctypes.byref(b),
-                                 ctypes.byref(nb), 1 if reset else 0))
-    return {"gemv_ms": a.value, "gemv_launches": na.value, "gemm_ms": b.value,
-            "gemm_launches": nb.value}
+    ms = (ctypes.c_double * 4)()
+    n = (_I64 * 2)()
+    _check(lib().eo_kernel_times(e, ms, n, 1 if reset else 0))
+    return {"gemv_gate_up_ms": ms[0], "gemv_down_ms": ms[1], "gemm_gate_up_ms": ms[2],
+            "gemm_down_ms": ms[3], "gemv_launches": n[0], "gemm_launches": n[1]}
 
 
 def eo_sync(e) -> None:

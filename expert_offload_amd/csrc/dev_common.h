@@ -11,6 +11,9 @@ namespace eo {
 
 __device__ __forceinline__ float bf16_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Upper half of an fp32: the bf16 with the same value when the low 16 bits are 0.
+__device__ __forceinline__ uint32_t bf_hi(float v) { return __float_as_uint(v) >> 16; }
+
 __device__ __forceinline__ uint32_t f32_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
     u += 0x7FFFu + ((u >> 16) & 1u);

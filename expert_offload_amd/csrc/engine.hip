@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <chrono>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -49,8 +50,8 @@ eo_status fail(eo_status s, const std::string& msg) {
 
 uint64_t round_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
-struct TimedPair {
-    hipEvent_t a, b;
+struct TimedSet {  // events before, between and after a kernel pair
+    hipEvent_t ev[3];
 };
 
 }  // namespace
@@ -115,8 +116,9 @@ struct eo_engine {
     eo_stats stats{};
 
     bool timing = false;
-    std::vector<TimedPair> gemv_ev, gemm_ev, free_ev;
-    double gemv_ms = 0, gemm_ms = 0;
+    int gemv_fast = 1;  // EO_GEMV_FAST=0 selects the generic decode GEMV kernels
+    std::vector<TimedSet> gemv_ev, gemm_ev, free_ev;
+    double kms[4] = {0, 0, 0, 0};  // gemv gate/up, gemv down, gemm1, gemm2
     int64_t gemv_n = 0, gemm_n = 0;
 
     void* cap_x = nullptr;
@@ -128,30 +130,27 @@ struct eo_engine {
 
 namespace {
 
-eo_status get_pair(eo_engine* e, TimedPair* p) {
+eo_status get_set(eo_engine* e, TimedSet* p) {
     if (!e->free_ev.empty()) {
         *p = e->free_ev.back();
         e->free_ev.pop_back();
         return EO_OK;
     }
-    HIPCHK(hipEventCreate(&p->a));
-    HIPCHK(hipEventCreate(&p->b));
+    for (int i = 0; i < 3; ++i) HIPCHK(hipEventCreate(&p->ev[i]));
     return EO_OK;
 }
 
 eo_status harvest_times(eo_engine* e) {
     for (auto* v : {&e->gemv_ev, &e->gemm_ev}) {
+        const int base = v == &e->gemv_ev ? 0 : 2;
         for (auto& p : *v) {
-            HIPCHK(hipEventSynchronize(p.b));
-            float ms = 0;
-            HIPCHK(hipEventElapsedTime(&ms, p.a, p.b));
-            if (v == &e->gemv_ev) {
-                e->gemv_ms += ms;
-                e->gemv_n += 1;
-            } else {
-                e->gemm_ms += ms;
-                e->gemm_n += 1;
-            }
+            HIPCHK(hipEventSynchronize(p.ev[2]));
+            float m0 = 0, m1 = 0;
+            HIPCHK(hipEventElapsedTime(&m0, p.ev[0], p.ev[1]));
+            HIPCHK(hipEventElapsedTime(&m1, p.ev[1], p.ev[2]));
+            e->kms[base] += m0;
+            e->kms[base + 1] += m1;
+            (base == 0 ? e->gemv_n : e->gemm_n) += 1;
             e->free_ev.push_back(p);
         }
         v->clear();
@@ -351,28 +350,26 @@ eo_status do_ffn_device(eo_engine* e, int layer, const void* x, const int32_t* i
                         hipStream_t s) {
     const int T = e->plan_T;
     GroupW gw = slots_gw(e, layer);
-    TimedPair tpair{};
-    if (e->timing) EOCHK(get_pair(e, &tpair));
+    TimedSet ts{};
+    if (e->timing) EOCHK(get_set(e, &ts));
+    hipEvent_t* ev = e->timing ? ts.ev : nullptr;
+    hipEvent_t none[3] = {nullptr, nullptr, nullptr};
     hipError_t he;
     if (T == 1) {
         he = launch_ffn_gemv(e->fmt, e->lay, gw, e->d_plan, ids, w, e->k, e->E, e->shared, e->H,
-                             e->I, x, e->act_bf16, e->d_hgemv, e->d_yparts, s,
-                             e->timing ? tpair.a : nullptr, e->timing ? tpair.b : nullptr);
-        if (e->timing) e->gemv_ev.push_back(tpair);
+                             e->I, x, e->act_bf16, e->d_hgemv, e->d_yparts, s, ev ? ev : none,
+                             e->gemv_fast);
+        if (e->timing) e->gemv_ev.push_back(ts);
     } else {
         EOCHK(ensure_gemm(e, T, s));
         he = launch_permute(ids, e->d_plan->e2slot, 0, T, e->k, e->E, e->shared, x, e->act_bf16,
                             e->H, e->pb, s);
-        if (he == hipSuccess) {
-            if (e->timing) HIPCHK(hipEventRecord(tpair.a, s));
+        if (he == hipSuccess)
             he = launch_ffn_gemm(e->fmt, e->lay, gw, e->E, e->shared, e->H, e->I,
                                  T * e->k + T, e->pb.offsets, e->pb.tile_off, e->pb.x_perm,
-                                 e->d_hbuf, e->pb.perm_pair, ids, w, e->k, T, e->d_opairs, s);
-            if (e->timing) {
-                HIPCHK(hipEventRecord(tpair.b, s));
-                e->gemm_ev.push_back(tpair);
-            }
-        }
+                                 e->d_hbuf, e->pb.perm_pair, ids, w, e->k, T, e->d_opairs, s,
+                                 ev ? ev : none);
+        if (e->timing) e->gemm_ev.push_back(ts);
     }
     if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("ffn launch: ") + hipGetErrorString(he));
     return EO_OK;
@@ -446,10 +443,8 @@ void destroy_all(eo_engine* e) {
                           e->ev_start})
         if (ev) (void)hipEventDestroy(ev);
     for (auto* v : {&e->gemv_ev, &e->gemm_ev, &e->free_ev})
-        for (auto& p : *v) {
-            (void)hipEventDestroy(p.a);
-            (void)hipEventDestroy(p.b);
-        }
+        for (auto& p : *v)
+            for (hipEvent_t ev : p.ev) (void)hipEventDestroy(ev);
     if (e->tp) threadpool_destroy(e->tp);
     delete e;
 }
@@ -539,8 +534,10 @@ eo_status create_impl(const eo_config* cfg, eo_engine* e) {
         HIPCHK(hipEventCreateWithFlags(&e->ev_comp[i], hipEventDisableTiming));
     }
     int nt = cfg->host_threads;
-    if (nt <= 0) nt = std::min(16, (int)std::max(1u, std::thread::hardware_concurrency()));
+    // leave one hardware thread for the engine's own orchestration and the runtime
+    if (nt <= 0) nt = std::max(1, std::min(15, (int)std::thread::hardware_concurrency() - 1));
     e->tp = threadpool_create(nt);
+    if (const char* v = std::getenv("EO_GEMV_FAST")) e->gemv_fast = std::atoi(v) != 0;
     e->bp = e->bh = 1;
     EOCHK(reset_cache(e));
     HIPCHK(hipDeviceSynchronize());
@@ -841,11 +838,9 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t double_buff
         if (he == hipSuccess)
             he = launch_permute(ids, nullptr, 1, T, e->k, e->E, e->shared, x_inout, e->act_bf16,
                                 e->H, e->pb, s);
-        TimedPair tpair{};
-        if (e->timing) {
-            EOCHK(get_pair(e, &tpair));
-            HIPCHK(hipEventRecord(tpair.a, s));
-        }
+        TimedSet ts{};
+        if (e->timing) EOCHK(get_set(e, &ts));
+        hipEvent_t none[3] = {nullptr, nullptr, nullptr};
         if (he == hipSuccess) {
             GroupW gw;
             gw.slots = e->d_staging[b];
@@ -854,12 +849,10 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t double_buff
             gw.shared_w = e->shared ? e->d_shared + (uint64_t)l * e->S_pad : nullptr;
             he = launch_ffn_gemm(e->fmt, e->lay, gw, e->E, e->shared, e->H, e->I, T * e->k + T,
                                  e->pb.offsets, e->pb.tile_off, e->pb.x_perm, e->d_hbuf,
-                                 e->pb.perm_pair, ids, w, e->k, T, e->d_opairs, s);
+                                 e->pb.perm_pair, ids, w, e->k, T, e->d_opairs, s,
+                                 e->timing ? ts.ev : none);
         }
-        if (e->timing) {
-            HIPCHK(hipEventRecord(tpair.b, s));
-            e->gemm_ev.push_back(tpair);
-        }
+        if (e->timing) e->gemm_ev.push_back(ts);
         if (he == hipSuccess)
             he = launch_combine(e->d_opairs, ids, nullptr, 1, e->shared, nullptr, T, e->k, e->H, y,
                                 x_inout, e->act_bf16, s, e->E);
@@ -947,16 +940,17 @@ eo_status eo_set_timing(eo_engine* e, int32_t enable) {
     return EO_OK;
 }
 
-eo_status eo_kernel_times(eo_engine* e, double* gemv_ms, int64_t* gemv_launches, double* gemm_ms,
-                          int64_t* gemm_launches, int32_t reset) {
+eo_status eo_kernel_times(eo_engine* e, double* ms, int64_t* launches, int32_t reset) {
     if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
     EOCHK(harvest_times(e));
-    if (gemv_ms) *gemv_ms = e->gemv_ms;
-    if (gemv_launches) *gemv_launches = e->gemv_n;
-    if (gemm_ms) *gemm_ms = e->gemm_ms;
-    if (gemm_launches) *gemm_launches = e->gemm_n;
+    if (ms)
+        for (int i = 0; i < 4; ++i) ms[i] = e->kms[i];
+    if (launches) {
+        launches[0] = e->gemv_n;
+        launches[1] = e->gemm_n;
+    }
     if (reset) {
-        e->gemv_ms = e->gemm_ms = 0;
+        for (double& v : e->kms) v = 0;
         e->gemv_n = e->gemm_n = 0;
     }
     return EO_OK;

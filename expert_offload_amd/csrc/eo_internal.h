@@ -74,12 +74,12 @@ struct GroupW {
 hipError_t launch_ffn_gemm(int fmt, const Layout& lay, GroupW gw, int E, int has_shared, int H,
                            int I, int P_max, const int32_t* offsets, const int32_t* tile_off,
                            const void* x_perm, void* h_buf, const int32_t* perm_pair,
-                           const int32_t* ids, const float* w, int k, int T, float* o_pairs,
-                           hipStream_t s);
+                           const int32_t* ids, const float* w, int k, int T, void* o_pairs,
+                           hipStream_t s, hipEvent_t* ev /*[3]: before, between, after*/);
 
 // Combine: y[t] = sum_j (resident) o_pairs[t*k+j] + o_pairs[T*k+t] (shared)
 // + y_host[t] (if given). Optional residual: x_out = act(x + y).
-hipError_t launch_combine(const float* o_pairs, const int32_t* ids, const int32_t* e2slot,
+hipError_t launch_combine(const void* o_pairs, const int32_t* ids, const int32_t* e2slot,
                           int all_resident, int has_shared, const float* y_host, int T, int k,
                           int H, float* y, void* x_res, int act_bf16, hipStream_t s, int E);
 
@@ -87,7 +87,8 @@ hipError_t launch_combine(const float* o_pairs, const int32_t* ids, const int32_
 hipError_t launch_ffn_gemv(int fmt, const Layout& lay, GroupW gw, const DevPlan* plan,
                            const int32_t* ids, const float* w, int k, int E, int has_shared,
                            int H, int I, const void* x, int act_bf16, float* h_buf,
-                           float* y_parts, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+                           float* y_parts, hipStream_t s, hipEvent_t* ev /*[3], may be null*/,
+                           int allow_fast);
 // Sum of the GEMV partials (k + shared rows of [H]) plus host results.
 hipError_t launch_gemv_reduce(const float* y_parts, int nparts, const float* y_host, int H,
                               float* y, void* x_res, int act_bf16, hipStream_t s);

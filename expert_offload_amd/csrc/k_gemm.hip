@@ -2,7 +2,8 @@
 //
 // Per expert e with its M_e permuted rows X_e (bf16):
 //   GEMM1: G = X_e . W13^T, h = silu(G_gate) * G_up  -> bf16 [M_e, I]
-//   GEMM2: O = h . W2^T, scaled by the pair's routing weight -> o_pairs (fp32)
+//   GEMM2: O = h . W2^T, scaled by the pair's routing weight -> o_pairs (bf16;
+//          fp32 on the fp32-weight path)
 // on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulate). Weight
 // tiles are decoded into LDS as bf16: bf16 as stored; e4m3 (FP8) and
 // e2m1 * e8m0 (MXFP4) and e2m1 * e4m3 (NVFP4) are exact in bf16, so the only
@@ -19,6 +20,8 @@
 //
 // fp32 weights with fp32 activations (small test models) use a plain VALU
 // kernel with the same grouping and epilogues.
+#include <cstdlib>
+
 #include "dev_common.h"
 #include "eo_internal.h"
 
@@ -30,6 +33,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;  // LDS row stride in bf16
+
+int g_gemm_tiles = 1;  // EO_GEMM_BIG=0 selects the plain 128 x 128 kernel
 
 struct GemmArgs {
     GroupW gw;
@@ -43,7 +48,7 @@ struct GemmArgs {
     const int32_t* perm_pair;
     const float* w;
     int Tk;
-    float* o_pairs;       // GEMM2 output [Tk + T, H]
+    void* o_pairs;        // GEMM2 output [Tk + T, H]: bf16 (MFMA path) or fp32
 };
 
 __device__ __forceinline__ int find_group(const int32_t* tile_off, int G, int tile) {
@@ -60,8 +65,6 @@ __device__ __forceinline__ const uint8_t* group_base(const GroupW& gw, int g, in
     int s = gw.e2slot ? gw.e2slot[g] : g;
     return gw.slots + (uint64_t)s * gw.stride;
 }
-
-__device__ __forceinline__ uint32_t bf_hi(float v) { return __float_as_uint(v) >> 16; }
 
 // Decode 32 fp4 codes (16 bytes) with per-16 multipliers sc0 (elements 0..15)
 // and sc1 (16..31) into 32 bf16 at dst (exact: at most 6 significant bits).
@@ -229,7 +232,8 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
                     if (m0 + row < m_end) {
                         int pair = a.perm_pair[m0 + row];
                         float wp = pair < a.Tk ? a.w[pair] : 1.0f;
-                        a.o_pairs[(size_t)pair * a.H + n] = acc[i][j][v] * sc * wp;
+                        ((uint16_t*)a.o_pairs)[(size_t)pair * a.H + n] =
+                            (uint16_t)f32_bf16_rne(acc[i][j][v] * sc * wp);
                     }
                 }
         }
@@ -301,16 +305,293 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs a, const float* __res
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 int n = n0 + tx + 16 * j;
-                a.o_pairs[(size_t)pair * a.H + n] = acc[i][j] * wp;
+                ((float*)a.o_pairs)[(size_t)pair * a.H + n] = acc[i][j] * wp;
             }
         }
     }
 }
 
+
+// ------------------------------------------------------------------ v3 tiles
+// 128 (rows) x 256 (weight rows) per workgroup, K step 32; wavefront (wm, wn)
+// owns rows wm*64..+64 and 128 weight rows (2 x 4 MFMA 32x32x16 blocks). GEMM1's
+// 256 weight rows are 128 gate rows then the same 128 up rows; a wavefront
+// takes gate columns wn*64..+64 and the matching up columns, so h = silu(g)*u
+// forms in registers. The next K tile's global loads are issued into registers
+// before the current tile's MFMAs; LDS is double-buffered (60 KB) with one
+// barrier per K step, which leaves room for two workgroups (8 wavefronts) per
+// CU. LDS rows are 40 bf16 (80 B): the 16 lanes of each ds_read_b128 quarter
+// hit 16 distinct 16-byte bank groups. The epilogue goes through LDS: scaled
+// bf16 results are written there, then leave as 16-byte row segments; row ->
+// pair index and routing weight are staged once per workgroup.
+constexpr int V3M = 128, V3N = 256, V3K = 32, V3L = V3K + 8;
+constexpr int V3_OUT_LD = V3N + 8;  // epilogue tile row stride (bf16)
+constexpr size_t kV3Pipe = 2 * (V3M + V3N) * V3L * sizeof(uint16_t);     // 61,440 B
+constexpr size_t kV3Out = (size_t)V3M * V3_OUT_LD * sizeof(uint16_t);     // 67,584 B
+constexpr size_t kV3Lds = (kV3Pipe > kV3Out ? kV3Pipe : kV3Out) + 2 * V3M * sizeof(int32_t);
+
 template <int FMT>
-void run_mfma(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s) {
+struct V3Regs {  // one K tile of global data held by a thread
+    uint4 a[2];
+    uint4 b[FMT == EO_W_BF16 ? 4 : (FMT == EO_W_FP8 ? 2 : 1)];
+    uint32_t sc;  // fp4 block scales of this thread's B chunk
+};
+
+template <int FMT, int MODE>
+__device__ __forceinline__ int v3_wrow(const GemmArgs& a, int n0, int i) {
+    if (MODE == 0) return i < 128 ? n0 + i : a.I + n0 + (i - 128);
+    return n0 + i;
+}
+
+template <int FMT, int MODE>
+__device__ __forceinline__ void v3_load(const GemmArgs& a, const uint8_t* wdata,
+                                        const uint8_t* wscal, int m0, int m_end, int n0, int k0,
+                                        int tid, V3Regs<FMT>& r) {
+    const int K = a.K;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {  // A: 128 rows x 32 bf16 = 512 chunks
+        int c = tid + 256 * it, row = c >> 2, seg = c & 3;
+        r.a[it] = (m0 + row < m_end)
+                      ? *(const uint4*)(a.A + (size_t)(m0 + row) * K + k0 + seg * 8)
+                      : make_uint4(0, 0, 0, 0);
+    }
+    if (FMT == EO_W_BF16) {  // B: 256 rows x 32 bf16 = 1024 chunks
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            int c = tid + 256 * it, row = c >> 2, seg = c & 3;
+            r.b[it] = *(const uint4*)((const uint16_t*)wdata +
+                                      (size_t)v3_wrow<FMT, MODE>(a, n0, row) * K + k0 + seg * 8);
+        }
+    } else if (FMT == EO_W_FP8) {  // 256 rows x 32 bytes = 512 chunks
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            int c = tid + 256 * it, row = c >> 1, seg = c & 1;
+            r.b[it] = *(const uint4*)(wdata + (size_t)v3_wrow<FMT, MODE>(a, n0, row) * K + k0 +
+                                      seg * 16);
+        }
+    } else {  // fp4: 256 rows x 16 bytes = 256 chunks, one per thread
+        const int row = tid, wr = v3_wrow<FMT, MODE>(a, n0, row);
+        r.b[0] = *(const uint4*)(wdata + (size_t)wr * (K / 2) + k0 / 2);
+        if (FMT == EO_W_MXFP4)
+            r.sc = wscal[(size_t)wr * (K / 32) + k0 / 32];
+        else
+            r.sc = *(const uint16_t*)(wscal + (size_t)wr * (K / 16) + k0 / 16);
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void v3_store(uint16_t* As, uint16_t* Bs, int tid, const V3Regs<FMT>& r) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        int c = tid + 256 * it, row = c >> 2, seg = c & 3;
+        *(uint4*)(As + row * V3L + seg * 8) = r.a[it];
+    }
+    if (FMT == EO_W_BF16) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            int c = tid + 256 * it, row = c >> 2, seg = c & 3;
+            *(uint4*)(Bs + row * V3L + seg * 8) = r.b[it];
+        }
+    } else if (FMT == EO_W_FP8) {
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            int c = tid + 256 * it, row = c >> 1, seg = c & 1;
+            const uint4 q = r.b[it];
+            uint32_t words[4] = {q.x, q.y, q.z, q.w}, out[8];
+#pragma unroll
+            for (int wi = 0; wi < 4; ++wi) {
+                uint32_t wv = words[wi];
+                out[2 * wi] = bf_hi(e4m3_f32(wv & 0xFF)) | (bf_hi(e4m3_f32((wv >> 8) & 0xFF)) << 16);
+                out[2 * wi + 1] =
+                    bf_hi(e4m3_f32((wv >> 16) & 0xFF)) | (bf_hi(e4m3_f32(wv >> 24)) << 16);
+            }
+            uint4* d = (uint4*)(Bs + row * V3L + seg * 16);
+            d[0] = make_uint4(out[0], out[1], out[2], out[3]);
+            d[1] = make_uint4(out[4], out[5], out[6], out[7]);
+        }
+    } else {
+        float sc0, sc1;
+        if (FMT == EO_W_MXFP4) {
+            sc0 = sc1 = e8m0_f32(r.sc);
+        } else {
+            sc0 = e4m3_f32(r.sc & 0xFF);
+            sc1 = e4m3_f32(r.sc >> 8);
+        }
+        fp4x32_to_lds(r.b[0], sc0, sc1, Bs + tid * V3L);
+    }
+}
+
+template <int FMT, int MODE>
+__global__ __launch_bounds__(256, 2) void k_gemm_v3(GemmArgs a, int nN) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    // pipeline buffer b: A at smem + b*V3M*V3L, B at smem + 2*V3M*V3L + b*V3N*V3L;
+    // after the K loop the same bytes hold the epilogue tile; row info follows.
+    int32_t* s_pair = (int32_t*)((uint8_t*)smem + (kV3Pipe > kV3Out ? kV3Pipe : kV3Out));
+    float* s_wp = (float*)(s_pair + V3M);
+
+    // Tile order: (row tile, weight tile) with the weight tile fastest, so the
+    // nN tiles that share a row tile, and the row tiles of one expert that share
+    // its weights, run back to back. Workgroups are dealt to the 8 XCDs round
+    // robin (id mod 8); each XCD gets one contiguous share of the real tiles, so
+    // that sharing happens in its own L2.
+    const int real = a.tile_off[a.G] * nN;
+    const int per = (real + 7) >> 3;
+    const int logical = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if ((int)(blockIdx.x >> 3) >= per || logical >= real) return;
+    const int tile = logical / nN, ntile = logical - tile * nN;
+    const int g = find_group(a.tile_off, a.G, tile);
+    const int m0 = a.offsets[g] + (tile - a.tile_off[g]) * V3M;
+    const int m_end = a.offsets[g + 1];
+    const uint8_t* wb = group_base(a.gw, g, a.E);
+    const uint8_t* wdata = wb + (MODE == 0 ? a.lay.d13 : a.lay.d2);
+    const uint8_t* wscal = wb + (MODE == 0 ? a.lay.s13 : a.lay.s2);
+    const int n0 = ntile * (MODE == 0 ? 128 : 256);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nk = a.K / V3K;
+
+    if (MODE == 1 && tid < V3M) {
+        int pair = m0 + tid < m_end ? a.perm_pair[m0 + tid] : -1;
+        s_pair[tid] = pair;
+        s_wp[tid] = pair < 0 ? 0.0f : (pair < a.Tk ? a.w[pair] : 1.0f);
+    }
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    auto brow = [&](int j) -> int {  // LDS B row of N block j of this wavefront
+        if (MODE == 0) return (j >> 1) * 128 + wn * 64 + (j & 1) * 32;
+        return wn * 128 + j * 32;
+    };
+
+    V3Regs<FMT> regs;
+    v3_load<FMT, MODE>(a, wdata, wscal, m0, m_end, n0, 0, tid, regs);
+    v3_store<FMT>(smem, smem + 2 * V3M * V3L, tid, regs);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) v3_load<FMT, MODE>(a, wdata, wscal, m0, m_end, n0, (kt + 1) * V3K, tid, regs);
+        const uint16_t* A_ = smem + cur * (V3M * V3L);
+        const uint16_t* B_ = smem + 2 * V3M * V3L + cur * (V3N * V3L);
+#pragma unroll
+        for (int ks = 0; ks < V3K / 16; ++ks) {
+            const int kc = ks * 16 + (lane >> 5) * 8;
+            bf16x8 av[2], bv[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                av[i] = *(const bf16x8*)(A_ + (wm * 64 + i * 32 + (lane & 31)) * V3L + kc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bv[j] = *(const bf16x8*)(B_ + (brow(j) + (lane & 31)) * V3L + kc);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < nk)
+            v3_store<FMT>(smem + (cur ^ 1) * (V3M * V3L),
+                          smem + 2 * V3M * V3L + (cur ^ 1) * (V3N * V3L), tid, regs);
+        __syncthreads();
+    }
+
+    // epilogue: scaled bf16 values into the LDS tile (the pipeline buffers are
+    // free after the last barrier), then 16-byte row segments to global memory
+    uint16_t* ot = smem;
+    const int col = lane & 31;
+    if (MODE == 0) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int c = wn * 64 + jj * 32 + col;  // column within the 128-wide h tile
+            const int n = n0 + c;
+            float sg = 1.0f, su = 1.0f;
+            if (FMT == EO_W_FP8) {
+                sg = ((const float*)wscal)[n];
+                su = ((const float*)wscal)[a.I + n];
+            } else if (FMT == EO_W_NVFP4) {
+                const float* gl = (const float*)(wb + a.lay.gl);
+                sg = gl[0];
+                su = gl[1];
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    float gv = acc[i][jj][v] * sg, uv = acc[i][2 + jj][v] * su;
+                    ot[row * V3_OUT_LD + c] = (uint16_t)f32_bf16_rne(silu_f32(gv) * uv);
+                }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {  // 128 rows x 16 segments of 16 B
+            int cidx = tid + 256 * it, row = cidx >> 4, seg = cidx & 15;
+            if (m0 + row < m_end)
+                *(uint4*)(a.h_out + (size_t)(m0 + row) * a.I + n0 + seg * 8) =
+                    *(const uint4*)(ot + row * V3_OUT_LD + seg * 8);
+        }
+    } else {
+        const float gs = FMT == EO_W_NVFP4 ? ((const float*)(wb + a.lay.gl))[2] : 1.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = wn * 128 + j * 32 + col;
+            const float sc = FMT == EO_W_FP8 ? ((const float*)wscal)[n0 + c] : gs;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    ot[row * V3_OUT_LD + c] = (uint16_t)f32_bf16_rne(acc[i][j][v] * sc * s_wp[row]);
+                }
+        }
+        __syncthreads();
+        uint16_t* op = (uint16_t*)a.o_pairs;
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {  // 128 rows x 32 segments of 16 B
+            int cidx = tid + 256 * it, row = cidx >> 5, seg = cidx & 31;
+            int pair = s_pair[row];
+            if (pair >= 0)
+                *(uint4*)(op + (size_t)pair * a.H + n0 + seg * 8) =
+                    *(const uint4*)(ot + row * V3_OUT_LD + seg * 8);
+        }
+    }
+}
+
+template <int FMT>
+bool run_v3(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hipEvent_t* ev) {
+    if (I % 128 || H % 256) return false;
+    static bool attr = false;
+    if (!attr) {
+        if (hipFuncSetAttribute((const void*)k_gemm_v3<FMT, 0>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kV3Lds) != hipSuccess ||
+            hipFuncSetAttribute((const void*)k_gemm_v3<FMT, 1>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kV3Lds) != hipSuccess)
+            return false;
+        attr = true;
+    }
+    const int n1 = I / 128, n2 = H / 256;
+    auto grid = [&](int nN) { return ((tiles * nN + 7) / 8) * 8; };
+    if (ev[0]) (void)hipEventRecord(ev[0], s);
+    k_gemm_v3<FMT, 0><<<grid(n1), 256, kV3Lds, s>>>(a1, n1);
+    if (ev[1]) (void)hipEventRecord(ev[1], s);
+    k_gemm_v3<FMT, 1><<<grid(n2), 256, kV3Lds, s>>>(a2, n2);
+    if (ev[2]) (void)hipEventRecord(ev[2], s);
+    return true;
+}
+
+template <int FMT>
+void run_mfma(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hipEvent_t* ev) {
+    if (g_gemm_tiles && run_v3<FMT>(a1, a2, tiles, I, H, s, ev)) return;
+    if (ev[0]) (void)hipEventRecord(ev[0], s);
     k_gemm_mfma<FMT, 0><<<dim3(tiles, I / 64), 256, 0, s>>>(a1);
+    if (ev[1]) (void)hipEventRecord(ev[1], s);
     k_gemm_mfma<FMT, 1><<<dim3(tiles, H / 128), 256, 0, s>>>(a2);
+    if (ev[2]) (void)hipEventRecord(ev[2], s);
 }
 
 }  // namespace
@@ -318,9 +599,14 @@ void run_mfma(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s) 
 hipError_t launch_ffn_gemm(int fmt, const Layout& lay, GroupW gw, int E, int has_shared, int H,
                            int I, int P_max, const int32_t* offsets, const int32_t* tile_off,
                            const void* x_perm, void* h_buf, const int32_t* perm_pair,
-                           const int32_t* ids, const float* w, int k, int T, float* o_pairs,
-                           hipStream_t s) {
+                           const int32_t* ids, const float* w, int k, int T, void* o_pairs,
+                           hipStream_t s, hipEvent_t* ev) {
     (void)ids;
+    static bool env_read = false;
+    if (!env_read) {
+        if (const char* v = getenv("EO_GEMM_BIG")) g_gemm_tiles = atoi(v) != 0;
+        env_read = true;
+    }
     const int G = E + (has_shared ? 1 : 0);
     const int tiles = (P_max + kTileM - 1) / kTileM + G;  // upper bound on row tiles
     GemmArgs a1{};
@@ -344,13 +630,16 @@ hipError_t launch_ffn_gemm(int fmt, const Layout& lay, GroupW gw, int E, int has
     a2.A = (const uint16_t*)h_buf;
     switch (fmt) {
     case EO_W_FP32:
+        if (ev[0]) (void)hipEventRecord(ev[0], s);
         k_gemm_f32<0><<<dim3(tiles, I / 32), 256, 0, s>>>(a1, (const float*)x_perm, (float*)h_buf);
+        if (ev[1]) (void)hipEventRecord(ev[1], s);
         k_gemm_f32<1><<<dim3(tiles, H / 64), 256, 0, s>>>(a2, (const float*)h_buf, nullptr);
+        if (ev[2]) (void)hipEventRecord(ev[2], s);
         break;
-    case EO_W_BF16: run_mfma<EO_W_BF16>(a1, a2, tiles, I, H, s); break;
-    case EO_W_FP8: run_mfma<EO_W_FP8>(a1, a2, tiles, I, H, s); break;
-    case EO_W_MXFP4: run_mfma<EO_W_MXFP4>(a1, a2, tiles, I, H, s); break;
-    case EO_W_NVFP4: run_mfma<EO_W_NVFP4>(a1, a2, tiles, I, H, s); break;
+    case EO_W_BF16: run_mfma<EO_W_BF16>(a1, a2, tiles, I, H, s, ev); break;
+    case EO_W_FP8: run_mfma<EO_W_FP8>(a1, a2, tiles, I, H, s, ev); break;
+    case EO_W_MXFP4: run_mfma<EO_W_MXFP4>(a1, a2, tiles, I, H, s, ev); break;
+    case EO_W_NVFP4: run_mfma<EO_W_NVFP4>(a1, a2, tiles, I, H, s, ev); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -247,12 +247,244 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ y
     }
 }
 
+
+// ------------------------------------------------------------------ fast path
+// For bf16 activations and the shapes instantiated below: gate/up kernel
+// (h written as bf16) then down kernel. Each lane group of G lanes owns R rows
+// and NC 16-byte chunks per row; all loads of a wavefront are issued before its
+// arithmetic, so each lane keeps R * NC * 16 bytes in flight. bf16 products
+// use v_dot2_f32_bf16; fp4 codes become bf16 pairs with the scaled convert
+// (MXFP4: times 2^(e8m0-127), exact; NVFP4: unscaled, then the two e4m3 block
+// scales on the partial sums).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x2_t as_bf2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
+
+__device__ __forceinline__ float dot8(uint4 w, uint4 x, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w.x), as_bf2(x.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w.y), as_bf2(x.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w.z), as_bf2(x.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w.w), as_bf2(x.w), acc, false);
+    return acc;
+}
+
+// 8 fp4 codes of one 32-bit word (two per byte, low nibble first) times x.
+template <int B>
+__device__ __forceinline__ float fp4_byte(uint32_t w, float sc, uint32_t xw, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, B),
+                                           as_bf2(xw), acc, false);
+}
+__device__ __forceinline__ float fp4_word(uint32_t w, float sc, uint4 x, float acc) {
+    acc = fp4_byte<0>(w, sc, x.x, acc);
+    acc = fp4_byte<1>(w, sc, x.y, acc);
+    acc = fp4_byte<2>(w, sc, x.z, acc);
+    acc = fp4_byte<3>(w, sc, x.w, acc);
+    return acc;
+}
+
+__device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t two) {
+    return bf_hi(e4m3_f32(two & 0xFF)) | (bf_hi(e4m3_f32((two >> 8) & 0xFF)) << 16);
+}
+
+template <int FMT> struct FastC;  // bf16 x elements per chunk, x uint4 per chunk
+template <> struct FastC<EO_W_BF16> { static constexpr int n = 8, xq = 1; };
+template <> struct FastC<EO_W_FP8> { static constexpr int n = 16, xq = 2; };
+template <> struct FastC<EO_W_MXFP4> { static constexpr int n = 32, xq = 4; };
+template <> struct FastC<EO_W_NVFP4> { static constexpr int n = 32, xq = 4; };
+
+template <int FMT>
+__device__ __forceinline__ const uint8_t* row_ptr(const uint8_t* data, int row, int K) {
+    if (FMT == EO_W_BF16) return data + (size_t)row * K * 2;
+    if (FMT == EO_W_FP8) return data + (size_t)row * K;
+    return data + (size_t)row * (K / 2);
+}
+
+// Partial dots of R weight rows with the bf16 vector x over this lane's chunks
+// c = gl + G*i (i < NC); block scales are applied, row/tensor scales are not.
+template <int FMT, int G, int NC, int R>
+__device__ __forceinline__ void rows_dot(const uint8_t* data, const uint8_t* scal, int K,
+                                         const int (&rows)[R], const uint16_t* x, int gl,
+                                         float (&out)[R]) {
+    constexpr int XQ = FastC<FMT>::xq, N = FastC<FMT>::n;
+    uint4 wq[R][NC];
+    uint4 xq[NC][XQ];
+    uint32_t sq[R][NC];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < NC; ++i)
+            wq[r][i] = *(const uint4*)(row_ptr<FMT>(data, rows[r], K) + (size_t)(gl + G * i) * 16);
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+#pragma unroll
+        for (int q = 0; q < XQ; ++q) xq[i][q] = *(const uint4*)(x + (size_t)(gl + G * i) * N + 8 * q);
+    if (FMT == EO_W_MXFP4 || FMT == EO_W_NVFP4) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+                const int c = gl + G * i;
+                if (FMT == EO_W_MXFP4)
+                    sq[r][i] = scal[(size_t)rows[r] * (K / 32) + c];
+                else
+                    sq[r][i] = *(const uint16_t*)(scal + (size_t)rows[r] * (K / 16) + 2 * c);
+            }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const uint4 w = wq[r][i];
+            if (FMT == EO_W_BF16) {
+                acc = dot8(w, xq[i][0], acc);
+            } else if (FMT == EO_W_FP8) {
+                acc = dot8(make_uint4(e4m3x2_bf16(w.x), e4m3x2_bf16(w.x >> 16),
+                                      e4m3x2_bf16(w.y), e4m3x2_bf16(w.y >> 16)), xq[i][0], acc);
+                acc = dot8(make_uint4(e4m3x2_bf16(w.z), e4m3x2_bf16(w.z >> 16),
+                                      e4m3x2_bf16(w.w), e4m3x2_bf16(w.w >> 16)), xq[i][1], acc);
+            } else if (FMT == EO_W_MXFP4) {
+                const float sc = e8m0_f32(sq[r][i]);
+                acc = fp4_word(w.x, sc, xq[i][0], acc);
+                acc = fp4_word(w.y, sc, xq[i][1], acc);
+                acc = fp4_word(w.z, sc, xq[i][2], acc);
+                acc = fp4_word(w.w, sc, xq[i][3], acc);
+            } else {  // NVFP4: exact e2m1 values, then the two e4m3 block scales
+                float a0 = fp4_word(w.x, 1.0f, xq[i][0], 0.0f);
+                a0 = fp4_word(w.y, 1.0f, xq[i][1], a0);
+                float a1 = fp4_word(w.z, 1.0f, xq[i][2], 0.0f);
+                a1 = fp4_word(w.w, 1.0f, xq[i][3], a1);
+                acc = fmaf(a0, e4m3_f32(sq[r][i] & 0xFF), acc);
+                acc = fmaf(a1, e4m3_f32(sq[r][i] >> 8), acc);
+            }
+        }
+        out[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int s = G / 2; s >= 1; s >>= 1) out[r] += __shfl_xor(out[r], s, 64);
+}
+
+template <int FMT, int GA, int NCA, int RA>
+__global__ __launch_bounds__(256) void k_gemv_gu(GemvArgs a, uint16_t* __restrict__ hb, int nA_per) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = blockIdx.x / nA_per, blk = blockIdx.x % nA_per;
+    const uint8_t* wb = expert_base(a, j);
+    if (!wb) return;
+    const int grp = lane / GA, gl = lane % GA;
+    const int r0 = ((blk * 4 + wave) * (64 / GA) + grp) * RA;
+    int rows[2 * RA];
+#pragma unroll
+    for (int r = 0; r < RA; ++r) {
+        rows[r] = r0 + r;
+        rows[RA + r] = a.I + r0 + r;
+    }
+    float out[2 * RA];
+    rows_dot<FMT, GA, NCA, 2 * RA>(wb + a.lay.d13, wb + a.lay.s13, a.H, rows, (const uint16_t*)a.x,
+                                   gl, out);
+    if (gl == 0) {
+        float sg = 1.0f, su = 1.0f;
+        const float* rs = (const float*)(wb + a.lay.s13);
+        if (FMT == EO_W_NVFP4) {
+            const float* g = (const float*)(wb + a.lay.gl);
+            sg = g[0];
+            su = g[1];
+        }
+#pragma unroll
+        for (int r = 0; r < RA; ++r) {
+            float g = out[r] * (FMT == EO_W_FP8 ? rs[r0 + r] : sg);
+            float u = out[RA + r] * (FMT == EO_W_FP8 ? rs[a.I + r0 + r] : su);
+            hb[(size_t)j * a.I + r0 + r] = (uint16_t)f32_bf16_rne(silu_f32(g) * u);
+        }
+    }
+}
+
+template <int FMT, int GB, int NCB, int RB>
+__global__ __launch_bounds__(256) void k_gemv_dn(GemvArgs a, const uint16_t* __restrict__ hb,
+                                                 int nB_per) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = blockIdx.x / nB_per, blk = blockIdx.x % nB_per;
+    const int grp = lane / GB, gl = lane % GB;
+    const int o0 = ((blk * 4 + wave) * (64 / GB) + grp) * RB;
+    const uint8_t* wb = expert_base(a, j);
+    if (!wb) {
+        if (gl == 0)
+#pragma unroll
+            for (int r = 0; r < RB; ++r) a.yp[(size_t)j * a.H + o0 + r] = 0.0f;
+        return;
+    }
+    int rows[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) rows[r] = o0 + r;
+    float out[RB];
+    rows_dot<FMT, GB, NCB, RB>(wb + a.lay.d2, wb + a.lay.s2, a.I, rows, hb + (size_t)j * a.I, gl,
+                               out);
+    if (gl == 0) {
+        const float wj = j < a.k ? a.w[j] : 1.0f;
+        const float* rs = (const float*)(wb + a.lay.s2);
+        const float gs = FMT == EO_W_NVFP4 ? ((const float*)(wb + a.lay.gl))[2] : 1.0f;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            float v = out[r] * (FMT == EO_W_FP8 ? rs[o0 + r] : gs);
+            a.yp[(size_t)j * a.H + o0 + r] = v * wj;
+        }
+    }
+}
+
+// Lanes per row G and chunks per lane NC for a row of `nch` chunks.
+bool split_rows(int nch, int* G, int* NC) {
+    for (int g = 64; g >= 4; g >>= 1)
+        if (nch % g == 0) {
+            *G = g;
+            *NC = nch / g;
+            return true;
+        }
+    return false;
+}
+
+template <int FMT, int GA, int NCA, int RA, int GB, int NCB, int RB>
+hipError_t run_fast(const GemvArgs& a, uint16_t* hb, hipStream_t s, hipEvent_t* ev) {
+    const int rowsA = 4 * (64 / GA) * RA, rowsB = 4 * (64 / GB) * RB;
+    if (a.I % rowsA || a.H % rowsB) return hipErrorNotSupported;
+    const int nA_per = a.I / rowsA, nB_per = a.H / rowsB;
+    if (ev[0]) (void)hipEventRecord(ev[0], s);
+    k_gemv_gu<FMT, GA, NCA, RA><<<a.nexp * nA_per, 256, 0, s>>>(a, hb, nA_per);
+    if (ev[1]) (void)hipEventRecord(ev[1], s);
+    k_gemv_dn<FMT, GB, NCB, RB><<<a.nexp * nB_per, 256, 0, s>>>(a, hb, nB_per);
+    if (ev[2]) (void)hipEventRecord(ev[2], s);
+    return hipGetLastError();
+}
+
+// Shapes with a tuned instantiation: (GA, NCA) from H, (GB, NCB) from I.
+template <int FMT>
+hipError_t fast_dispatch(const GemvArgs& a, uint16_t* hb, hipStream_t s, hipEvent_t* ev) {
+    constexpr int N = FastC<FMT>::n;
+    int GA, NCA, GB, NCB;
+    if (a.H % N || a.I % N || !split_rows(a.H / N, &GA, &NCA) || !split_rows(a.I / N, &GB, &NCB))
+        return hipErrorNotSupported;
+#define EO_FAST(ga, nca, ra, gb, ncb, rb)                         \
+    if (GA == ga && NCA == nca && GB == gb && NCB == ncb)         \
+        return run_fast<FMT, ga, nca, ra, gb, ncb, rb>(a, hb, s, ev);
+    EO_FAST(64, 4, 2, 32, 3, 2)  // bf16 H 2048, I 768
+    EO_FAST(64, 1, 4, 32, 1, 4)  // bf16 H 512, I 256
+    EO_FAST(32, 1, 4, 16, 1, 4)  // fp8 H 512, I 256
+    EO_FAST(64, 2, 4, 64, 1, 4)  // fp4 H 4096, I 2048
+    EO_FAST(64, 3, 2, 64, 1, 4)  // fp4 H 6144, I 2048
+    EO_FAST(16, 1, 4, 8, 1, 4)   // fp4 H 512, I 256
+    EO_FAST(64, 2, 2, 32, 3, 2)  // fp8 H 2048, I 768
+    EO_FAST(64, 1, 4, 8, 3, 4)   // fp4 H 2048, I 768
+#undef EO_FAST
+    return hipErrorNotSupported;
+}
+
 template <int FMT, bool XBF16>
-void run(const GemvArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    if (ev0) (void)hipEventRecord(ev0, s);
+void run(const GemvArgs& a, hipStream_t s, hipEvent_t* ev) {
+    if (ev[0]) (void)hipEventRecord(ev[0], s);
     k_gemv_up<FMT, XBF16><<<dim3(a.I / (4 * kRowsA), a.nexp), 256, 0, s>>>(a);
+    if (ev[1]) (void)hipEventRecord(ev[1], s);
     k_gemv_down<FMT><<<dim3(a.H / (4 * kRowsB), a.nexp), 256, 0, s>>>(a);
-    if (ev1) (void)hipEventRecord(ev1, s);
+    if (ev[2]) (void)hipEventRecord(ev[2], s);
 }
 
 }  // namespace
@@ -260,7 +492,7 @@ void run(const GemvArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
 hipError_t launch_ffn_gemv(int fmt, const Layout& lay, GroupW gw, const DevPlan* plan,
                            const int32_t* ids, const float* w, int k, int E, int has_shared,
                            int H, int I, const void* x, int act_bf16, float* h_buf,
-                           float* y_parts, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+                           float* y_parts, hipStream_t s, hipEvent_t* ev, int allow_fast) {
     GemvArgs a{};
     a.gw = gw;
     a.lay = lay;
@@ -275,16 +507,28 @@ hipError_t launch_ffn_gemv(int fmt, const Layout& lay, GroupW gw, const DevPlan*
     a.x = x;
     a.h = h_buf;
     a.yp = y_parts;
+    if (allow_fast && act_bf16 && fmt != EO_W_FP32) {
+        hipError_t he = hipErrorNotSupported;
+        uint16_t* hb = (uint16_t*)h_buf;
+        switch (fmt) {
+        case EO_W_BF16: he = fast_dispatch<EO_W_BF16>(a, hb, s, ev); break;
+        case EO_W_FP8: he = fast_dispatch<EO_W_FP8>(a, hb, s, ev); break;
+        case EO_W_MXFP4: he = fast_dispatch<EO_W_MXFP4>(a, hb, s, ev); break;
+        case EO_W_NVFP4: he = fast_dispatch<EO_W_NVFP4>(a, hb, s, ev); break;
+        default: break;
+        }
+        if (he != hipErrorNotSupported) return he;
+    }
     if (fmt == EO_W_FP32) {
         if (act_bf16) return hipErrorInvalidValue;
-        run<EO_W_FP32, false>(a, s, ev0, ev1);
+        run<EO_W_FP32, false>(a, s, ev);
     } else {
         if (!act_bf16) return hipErrorInvalidValue;
         switch (fmt) {
-        case EO_W_BF16: run<EO_W_BF16, true>(a, s, ev0, ev1); break;
-        case EO_W_FP8: run<EO_W_FP8, true>(a, s, ev0, ev1); break;
-        case EO_W_MXFP4: run<EO_W_MXFP4, true>(a, s, ev0, ev1); break;
-        case EO_W_NVFP4: run<EO_W_NVFP4, true>(a, s, ev0, ev1); break;
+        case EO_W_BF16: run<EO_W_BF16, true>(a, s, ev); break;
+        case EO_W_FP8: run<EO_W_FP8, true>(a, s, ev); break;
+        case EO_W_MXFP4: run<EO_W_MXFP4, true>(a, s, ev); break;
+        case EO_W_NVFP4: run<EO_W_NVFP4, true>(a, s, ev); break;
         default: return hipErrorInvalidValue;
         }
     }

@@ -6,7 +6,8 @@
 // expert (papers.ananclaw.com explainer, "core method" section 4, names it as
 // an architecture axis) is one more group holding every token. After the
 // grouped FFN, each pair's weighted output sits at o_pairs[t*k + j] (shared:
-// o_pairs[T*k + t]) and the combine sums a token's rows in fixed j order.
+// o_pairs[T*k + t]; bf16 with bf16 activations, else fp32) and the combine sums
+// a token's rows in fixed j order in fp32.
 #include "dev_common.h"
 #include "eo_internal.h"
 
@@ -130,8 +131,19 @@ __global__ __launch_bounds__(256) void k_shared_rows(int T, int Tk, const int32_
     for (int c = lane; c < row_bytes / 16; c += 64) out[c] = src[c];
 }
 
+// Four consecutive pair outputs as fp32 (bf16 storage with bf16 activations).
 template <bool BF16>
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o_pairs,
+__device__ __forceinline__ float4 pair4(const void* o_pairs, size_t row, int H, int h4) {
+    if (BF16) {
+        uint2 v = ((const uint2*)((const uint16_t*)o_pairs + row * H))[h4];
+        return make_float4(bf16_f32(v.x & 0xFFFFu), bf16_f32(v.x >> 16), bf16_f32(v.y & 0xFFFFu),
+                           bf16_f32(v.y >> 16));
+    }
+    return ((const float4*)((const float*)o_pairs + row * H))[h4];
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_combine(const void* __restrict__ o_pairs,
                                                  const int32_t* __restrict__ ids,
                                                  const int32_t* __restrict__ e2slot,
                                                  int all_resident, int has_shared,
@@ -145,11 +157,11 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o_pai
     for (int j = 0; j < k; ++j) {
         int e = ids[(size_t)t * k + j];
         if (!pair_resident(e2slot, all_resident, e, E)) continue;
-        float4 v = ((const float4*)(o_pairs + ((size_t)t * k + j) * H))[h4];
+        float4 v = pair4<BF16>(o_pairs, (size_t)t * k + j, H, h4);
         acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
     if (has_shared) {
-        float4 v = ((const float4*)(o_pairs + ((size_t)T * k + t) * H))[h4];
+        float4 v = pair4<BF16>(o_pairs, (size_t)T * k + t, H, h4);
         acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
     if (y_host) {
@@ -210,7 +222,7 @@ hipError_t launch_permute(const int32_t* ids, const int32_t* e2slot, int all_res
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* o_pairs, const int32_t* ids, const int32_t* e2slot,
+hipError_t launch_combine(const void* o_pairs, const int32_t* ids, const int32_t* e2slot,
                           int all_resident, int has_shared, const float* y_host, int T, int k,
                           int H, float* y, void* x_res, int act_bf16, hipStream_t s, int E) {
     dim3 grid((H / 4 + 255) / 256, T);

@@ -61,14 +61,14 @@ typedef struct {
     int32_t layers;         /* MoE layers L */
     int32_t experts;        /* routed experts per layer E (<= 1024) */
     int32_t top_k;          /* experts per token k (<= 16, <= E) */
-    int32_t hidden;         /* H, multiple of 64 */
+    int32_t hidden;         /* H, multiple of 128 */
     int32_t inter;          /* I, multiple of 64 */
     int32_t shared_experts; /* 0 or 1 always-on shared expert per layer (device-resident) */
     int32_t wfmt;           /* eo_wfmt */
     int32_t act_bf16;       /* 1: activations bf16 (needs wfmt != FP32); 0: fp32 (needs wfmt == FP32) */
     int64_t cache_slots;    /* C: device expert-cache capacity in experts (>= 0) */
     int32_t max_tokens;     /* largest T of any step call */
-    int32_t host_threads;   /* host-core expert routine threads; 0 = hardware concurrency, capped at 16 */
+    int32_t host_threads;   /* host-core expert routine threads; 0 = hardware threads - 1, at most 15 */
     int32_t device;         /* HIP device ordinal */
 } eo_config;
 
@@ -102,8 +102,9 @@ typedef struct {
 
 /* Create an engine on cfg->device: allocates the pinned host expert pool
  * (L*E blocks, each padded to 4 KiB), C device cache slots, the shared experts,
- * router copies, plan buffers, a copy stream and the host thread pool. The pool
- * and the shared experts start zeroed, the cache empty, B_P = B_H = 1.
+ * router copies, plan buffers, a copy stream and the host thread pool. Pool
+ * contents are undefined until written; shared experts and routers start
+ * zeroed, the cache empty, B_P = B_H = 1.
  * Errors: INVALID_ARG (shape limits above), UNSUPPORTED (format / activation
  * combination), OOM (pinned or device allocation failed), HIP. */
 eo_status eo_create(const eo_config* cfg, eo_engine** out);
@@ -212,11 +213,14 @@ eo_status eo_last_plan(eo_engine* e, eo_plan_host* out);
  * [W_gate (I*H) | W_up (I*H) | W_down (H*I)]. Synchronous. */
 eo_status eo_dequant(eo_engine* e, int32_t layer, int32_t expert, float* out_host);
 eo_status eo_stats_get(eo_engine* e, eo_stats* out);
-/* Device time of the last eo_prefill's expert GEMMs and of decode expert
- * GEMVs since the last reset, from HIP events on the compute stream:
- * ms totals and launch counts. reset != 0 clears after reading. */
-eo_status eo_kernel_times(eo_engine* e, double* gemv_ms, int64_t* gemv_launches,
-                          double* gemm_ms, int64_t* gemm_launches, int32_t reset);
+/* Device time of the expert FFN kernels since the last reset, from HIP events
+ * recorded on the compute stream around each kernel while timing is enabled:
+ * ms[0] decode GEMV gate/up kernel, ms[1] decode GEMV down kernel, ms[2] grouped
+ * GEMM gate/up (+SwiGLU) kernel, ms[3] grouped GEMM down kernel (totals);
+ * launches[0] decode GEMV pairs, launches[1] grouped GEMM pairs. Either pointer
+ * may be NULL; reset != 0 clears after reading. Synchronises on the events. */
+eo_status eo_kernel_times(eo_engine* e, double* ms /*[4]*/, int64_t* launches /*[2]*/,
+                          int32_t reset);
 /* Enable (1) or disable (0) the per-launch timing events behind eo_kernel_times. */
 eo_status eo_set_timing(eo_engine* e, int32_t enable);
 /* Size in bytes of one packed expert block (unpadded). */

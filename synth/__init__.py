@@ -29,8 +29,7 @@ P_EXPERT, P_SHARED, P_ROUTER, P_ACT, P_TRACE = 1, 2, 3, 4, 5
 def build(force: bool = False) -> str:
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + f".tmp{os.getpid()}"
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC,
-                               "-lm"])
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 

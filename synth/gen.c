@@ -23,6 +23,9 @@
  *     fp8  : W13 e4m3 [2I,H] | W2 e4m3 [H,I] | W13 f32 row scale [2I] | W2 f32 row scale [H]
  *   Two fp4 codes share a byte, the even element in the low nibble.
  *
+ * Single-threaded: callers parallelise over experts (ctypes releases the GIL),
+ * so no thread team lingers after generation.
+ *
  * Quantisers (generator side, round-half-to-even, saturating):
  *   mxfp4: shared exponent floor(log2 amax_block) - 2 (OCP MX v1.0), stored as e8m0.
  *   nvfp4: g = amax_tensor / (448*6); block scale e4m3(amax_block / (6 g)).
@@ -81,7 +84,6 @@ static void normal_block(uint32_t seed, uint32_t purpose, uint32_t c1, uint32_t 
 static void normal_fill(uint32_t seed, uint32_t purpose, uint32_t c1, uint32_t c2, uint32_t c3,
                         double sigma, int64_t n, float* out) {
     int64_t nblk = (n + 3) / 4;
-#pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < nblk; ++b) {
         float z[4];
         normal_block(seed, purpose, c1, c2, c3, (uint32_t)b, z);
@@ -106,7 +108,6 @@ static uint16_t f32_to_bf16_rne(float f) {
 }
 
 void synth_f32_to_bf16(const float* in, uint16_t* out, int64_t n) {
-#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16_rne(in[i]);
 }
 
@@ -179,7 +180,6 @@ static float amax_f32(const float* v, int64_t n) {
  * according to fmt. `g` is the tensor's nvfp4 global scale. */
 static void quantise_rows(const float* w, int64_t rows, int64_t K, int fmt, float g,
                           uint8_t* data, uint8_t* scales) {
-#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         const float* row = w + r * K;
         if (fmt == FMT_FP32) {

@@ -6,7 +6,9 @@ oracle never imports this module.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import ctypes
+import os
 
 import numpy as np
 
@@ -32,13 +34,20 @@ def make_engine(shape: LayerShape, seed: int = 0, cache_slots: int | None = None
                 blk = expert_block(seed, l, 0, shape.hidden, shape.inter, shape.fmt,
                                    purpose=P_SHARED)
                 eo.eo_set_shared_expert(e, l, blk, blk.size)
-            if fill_pool:
-                for x in range(shape.experts):
-                    write_pool_expert(e, shape, seed, l, x)
+        if fill_pool:
+            write_pool(e, shape, seed, L)
     except Exception:
         eo.eo_destroy(e)
         raise
     return e
+
+
+def write_pool(e: int, shape: LayerShape, seed: int, layers: int, workers: int = 0) -> None:
+    """All pool entries, generated in parallel (one expert per task)."""
+    workers = workers or min(16, os.cpu_count() or 1)
+    jobs = [(l, x) for l in range(layers) for x in range(shape.experts)]
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(lambda lx: write_pool_expert(e, shape, seed, *lx), jobs))
 
 
 def write_pool_expert(e: int, shape: LayerShape, seed: int, layer: int, expert: int) -> None:

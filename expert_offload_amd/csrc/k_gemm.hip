@@ -34,7 +34,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;  // LDS row stride in bf16
 
-int g_gemm_tiles = 1;  // EO_GEMM_BIG=0 selects the plain 128 x 128 kernel
+// 2: bf16 weights use the async-ring kernel (v4), other formats v3; 1: v3 for all;
+// 0: the plain 128 x 128 kernel. EO_GEMM_PATH overrides.
+int g_gemm_tiles = 2;
 
 struct GemmArgs {
     GroupW gw;
@@ -584,8 +586,205 @@ bool run_v3(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hi
     return true;
 }
 
+// ------------------------------------------------------------------ v4 (bf16)
+// Same tiles and epilogue as v3, but the K loop is a 3-stage ring filled by
+// direct-to-LDS loads (global_load_lds_dwordx4): two K tiles are in flight
+// while the third is multiplied, and no VGPRs carry the tiles. Each load
+// instruction of a wavefront fills 1 KB of LDS in lane order, so rows are
+// unpadded (64 B = 4 segments of 16 B for K step 32) and a lane loads the
+// global segment that belongs in its slot: segment s of row r sits in slot
+// s ^ ((r >> 2) & 3). With that XOR swizzle the 16 lanes of each ds_read_b128
+// quarter (16 rows, one logical segment) hit 16 distinct 16-byte bank groups.
+// Barriers are raw s_barrier with explicit vmcnt waits, so outstanding tile
+// loads are not drained at each K step.
+constexpr int V4S = 3;                                   // stages
+constexpr size_t kV4Stage = (size_t)(V3M + V3N) * 64;     // 24 KB
+constexpr size_t kV4Pipe = V4S * kV4Stage;                // 72 KB
+constexpr size_t kV4Lds = (kV4Pipe > kV3Out ? kV4Pipe : kV3Out) + 2 * V3M * sizeof(int32_t);
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int swz(int row, int seg) { return seg ^ ((row >> 2) & 3); }
+
+template <int MODE>
+__device__ __forceinline__ void v4_issue(const GemmArgs& a, const uint16_t* wdata, int m0,
+                                         int m_end, int n0, int k0, uint8_t* stage, int wave,
+                                         int lane) {
+    const int K = a.K;
+    const int lrow = lane >> 2, slot = lane & 3;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {  // A: 8 x 1 KB, rows (it*4 + wave)*16 ..
+        const int row = (it * 4 + wave) * 16 + lrow;
+        const int gr = min(m0 + row, m_end - 1);
+        const uint16_t* src = a.A + (size_t)gr * K + k0 + swz(row, slot) * 8;
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + (it * 4 + wave) * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {  // B: 16 x 1 KB
+        const int row = (it * 4 + wave) * 16 + lrow;
+        const int wr = MODE == 0 ? (row < 128 ? n0 + row : a.I + n0 + row - 128) : n0 + row;
+        const uint16_t* src = wdata + (size_t)wr * K + k0 + swz(row, slot) * 8;
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + V3M * 64 + (it * 4 + wave) * 1024),
+                                         16, 0, 0);
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void k_gemm_v4(GemmArgs a, int nN) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    uint8_t* sb = (uint8_t*)smem;
+    int32_t* s_pair = (int32_t*)(sb + (kV4Pipe > kV3Out ? kV4Pipe : kV3Out));
+    float* s_wp = (float*)(s_pair + V3M);
+
+    const int real = a.tile_off[a.G] * nN;
+    const int per = (real + 7) >> 3;
+    const int logical = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if ((int)(blockIdx.x >> 3) >= per || logical >= real) return;
+    const int tile = logical / nN, ntile = logical - tile * nN;
+    const int g = find_group(a.tile_off, a.G, tile);
+    const int m0 = a.offsets[g] + (tile - a.tile_off[g]) * V3M;
+    const int m_end = a.offsets[g + 1];
+    const uint8_t* wb = group_base(a.gw, g, a.E);
+    const uint16_t* wdata = (const uint16_t*)(wb + (MODE == 0 ? a.lay.d13 : a.lay.d2));
+    const int n0 = ntile * (MODE == 0 ? 128 : 256);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nk = a.K / V3K;
+
+    if (MODE == 1 && tid < V3M) {
+        int pair = m0 + tid < m_end ? a.perm_pair[m0 + tid] : -1;
+        s_pair[tid] = pair;
+        s_wp[tid] = pair < 0 ? 0.0f : (pair < a.Tk ? a.w[pair] : 1.0f);
+    }
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    v4_issue<MODE>(a, wdata, m0, m_end, n0, 0, sb, wave, lane);
+    if (nk > 1) v4_issue<MODE>(a, wdata, m0, m_end, n0, V3K, sb + kV4Stage, wave, lane);
+
+    int arow[2], aseg[2][2];  // A rows read by this lane and their swizzled slots
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        arow[i] = wm * 64 + i * 32 + (lane & 31);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) aseg[i][ks] = swz(arow[i], 2 * ks + (lane >> 5));
+    }
+    int brow_[4], bseg[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        brow_[j] = (MODE == 0 ? (j >> 1) * 128 + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32) +
+                   (lane & 31);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) bseg[j][ks] = swz(brow_[j], 2 * ks + (lane >> 5));
+    }
+
+    for (int kt = 0; kt < nk; ++kt) {
+        // this thread's 6 loads of tile kt are done once at most the 6 of
+        // tile kt+1 are outstanding; the barrier makes every thread's visible
+        if (kt + 1 < nk)
+            __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6), expcnt/lgkmcnt not waited
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        if (kt + 2 < nk)
+            v4_issue<MODE>(a, wdata, m0, m_end, n0, (kt + 2) * V3K, sb + ((kt + 2) % V4S) * kV4Stage,
+                           wave, lane);
+        const uint8_t* st = sb + (kt % V4S) * kV4Stage;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 av[2], bv[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) av[i] = *(const bf16x8*)(st + arow[i] * 64 + aseg[i][ks] * 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bv[j] = *(const bf16x8*)(st + V3M * 64 + brow_[j] * 64 + bseg[j][ks] * 16);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    __syncthreads();  // all tile loads landed and all LDS reads done: reuse as the epilogue tile
+
+    uint16_t* ot = smem;
+    const int col = lane & 31;
+    if (MODE == 0) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int c = wn * 64 + jj * 32 + col;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    ot[row * V3_OUT_LD + c] =
+                        (uint16_t)f32_bf16_rne(silu_f32(acc[i][jj][v]) * acc[i][2 + jj][v]);
+                }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            int cidx = tid + 256 * it, row = cidx >> 4, seg = cidx & 15;
+            if (m0 + row < m_end)
+                *(uint4*)(a.h_out + (size_t)(m0 + row) * a.I + n0 + seg * 8) =
+                    *(const uint4*)(ot + row * V3_OUT_LD + seg * 8);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = wn * 128 + j * 32 + col;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    ot[row * V3_OUT_LD + c] = (uint16_t)f32_bf16_rne(acc[i][j][v] * s_wp[row]);
+                }
+        }
+        __syncthreads();
+        uint16_t* op = (uint16_t*)a.o_pairs;
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            int cidx = tid + 256 * it, row = cidx >> 5, seg = cidx & 31;
+            int pair = s_pair[row];
+            if (pair >= 0)
+                *(uint4*)(op + (size_t)pair * a.H + n0 + seg * 8) =
+                    *(const uint4*)(ot + row * V3_OUT_LD + seg * 8);
+        }
+    }
+}
+
+bool run_v4(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hipEvent_t* ev) {
+    if (I % 128 || H % 256 || H % V3K || I % V3K) return false;
+    static bool attr = false;
+    if (!attr) {
+        if (hipFuncSetAttribute((const void*)k_gemm_v4<0>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kV4Lds) != hipSuccess ||
+            hipFuncSetAttribute((const void*)k_gemm_v4<1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kV4Lds) != hipSuccess)
+            return false;
+        attr = true;
+    }
+    const int n1 = I / 128, n2 = H / 256;
+    auto grid = [&](int nN) { return ((tiles * nN + 7) / 8) * 8; };
+    if (ev[0]) (void)hipEventRecord(ev[0], s);
+    k_gemm_v4<0><<<grid(n1), 256, kV4Lds, s>>>(a1, n1);
+    if (ev[1]) (void)hipEventRecord(ev[1], s);
+    k_gemm_v4<1><<<grid(n2), 256, kV4Lds, s>>>(a2, n2);
+    if (ev[2]) (void)hipEventRecord(ev[2], s);
+    return true;
+}
+
 template <int FMT>
 void run_mfma(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hipEvent_t* ev) {
+    if (FMT == EO_W_BF16 && g_gemm_tiles >= 2 && run_v4(a1, a2, tiles, I, H, s, ev)) return;
     if (g_gemm_tiles && run_v3<FMT>(a1, a2, tiles, I, H, s, ev)) return;
     if (ev[0]) (void)hipEventRecord(ev[0], s);
     k_gemm_mfma<FMT, 0><<<dim3(tiles, I / 64), 256, 0, s>>>(a1);
@@ -604,7 +803,7 @@ hipError_t launch_ffn_gemm(int fmt, const Layout& lay, GroupW gw, int E, int has
     (void)ids;
     static bool env_read = false;
     if (!env_read) {
-        if (const char* v = getenv("EO_GEMM_BIG")) g_gemm_tiles = atoi(v) != 0;
+        if (const char* v = getenv("EO_GEMM_PATH")) g_gemm_tiles = atoi(v);
         env_read = true;
     }
     const int G = E + (has_shared ? 1 : 0);

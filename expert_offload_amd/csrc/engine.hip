@@ -50,8 +50,8 @@ eo_status fail(eo_status s, const std::string& msg) {
 
 uint64_t round_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
-struct TimedSet {  // events before, between and after a kernel pair
-    hipEvent_t ev[3];
+struct TimedSet {  // start/stop events stamped on each kernel of a pair
+    hipEvent_t ev[4];
 };
 
 }  // namespace
@@ -136,7 +136,7 @@ eo_status get_set(eo_engine* e, TimedSet* p) {
         e->free_ev.pop_back();
         return EO_OK;
     }
-    for (int i = 0; i < 3; ++i) HIPCHK(hipEventCreate(&p->ev[i]));
+    for (int i = 0; i < 4; ++i) HIPCHK(hipEventCreate(&p->ev[i]));
     return EO_OK;
 }
 
@@ -144,10 +144,10 @@ eo_status harvest_times(eo_engine* e) {
     for (auto* v : {&e->gemv_ev, &e->gemm_ev}) {
         const int base = v == &e->gemv_ev ? 0 : 2;
         for (auto& p : *v) {
-            HIPCHK(hipEventSynchronize(p.ev[2]));
+            HIPCHK(hipEventSynchronize(p.ev[3]));
             float m0 = 0, m1 = 0;
             HIPCHK(hipEventElapsedTime(&m0, p.ev[0], p.ev[1]));
-            HIPCHK(hipEventElapsedTime(&m1, p.ev[1], p.ev[2]));
+            HIPCHK(hipEventElapsedTime(&m1, p.ev[2], p.ev[3]));
             e->kms[base] += m0;
             e->kms[base + 1] += m1;
             (base == 0 ? e->gemv_n : e->gemm_n) += 1;
@@ -353,12 +353,31 @@ eo_status do_ffn_device(eo_engine* e, int layer, const void* x, const int32_t* i
     TimedSet ts{};
     if (e->timing) EOCHK(get_set(e, &ts));
     hipEvent_t* ev = e->timing ? ts.ev : nullptr;
-    hipEvent_t none[3] = {nullptr, nullptr, nullptr};
+    hipEvent_t none[4] = {nullptr, nullptr, nullptr, nullptr};
     hipError_t he;
     if (T == 1) {
+        // the host holds the plan and (mirrored) the token's ids and weights:
+        // hand the kernels their weight pointers instead of device lookups
+        GemvExperts gx{};
+        if (e->mirrored && e->plan_ready) {
+            const eo_plan_host& p = e->last_plan;
+            gx.valid = 1;
+            for (int j = 0; j < e->k; ++j) {
+                const int ex = e->h_ids[j];
+                int slot = -1;
+                for (int i = 0; i < p.n_hit && slot < 0; ++i)
+                    if (p.hit_expert[i] == ex) slot = p.hit_slot[i];
+                for (int i = 0; i < p.q_fill && slot < 0; ++i)
+                    if (p.fill_expert[i] == ex) slot = p.fill_slot[i];
+                gx.base[j] = slot < 0 ? nullptr : e->d_slots + (uint64_t)slot * e->S_pad;
+                gx.w[j] = e->h_w[j];
+            }
+            gx.base[e->k] = gw.shared_w;
+            gx.w[e->k] = 1.0f;
+        }
         he = launch_ffn_gemv(e->fmt, e->lay, gw, e->d_plan, ids, w, e->k, e->E, e->shared, e->H,
                              e->I, x, e->act_bf16, e->d_hgemv, e->d_yparts, s, ev ? ev : none,
-                             e->gemv_fast);
+                             e->gemv_fast, gx.valid ? &gx : nullptr);
         if (e->timing) e->gemv_ev.push_back(ts);
     } else {
         EOCHK(ensure_gemm(e, T, s));
@@ -840,7 +859,7 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t double_buff
                                 e->H, e->pb, s);
         TimedSet ts{};
         if (e->timing) EOCHK(get_set(e, &ts));
-        hipEvent_t none[3] = {nullptr, nullptr, nullptr};
+        hipEvent_t none[4] = {nullptr, nullptr, nullptr, nullptr};
         if (he == hipSuccess) {
             GroupW gw;
             gw.slots = e->d_staging[b];

@@ -75,7 +75,8 @@ hipError_t launch_ffn_gemm(int fmt, const Layout& lay, GroupW gw, int E, int has
                            int I, int P_max, const int32_t* offsets, const int32_t* tile_off,
                            const void* x_perm, void* h_buf, const int32_t* perm_pair,
                            const int32_t* ids, const float* w, int k, int T, void* o_pairs,
-                           hipStream_t s, hipEvent_t* ev /*[3]: before, between, after*/);
+                           hipStream_t s,
+                           hipEvent_t* ev /*[4]: start/stop of each kernel, entries may be null*/);
 
 // Combine: y[t] = sum_j (resident) o_pairs[t*k+j] + o_pairs[T*k+t] (shared)
 // + y_host[t] (if given). Optional residual: x_out = act(x + y).
@@ -84,11 +85,19 @@ hipError_t launch_combine(const void* o_pairs, const int32_t* ids, const int32_t
                           int H, float* y, void* x_res, int act_bf16, hipStream_t s, int E);
 
 // Decode GEMV path (T == 1): phase A gate/up -> h, phase B down with weights.
+// When the host already knows the plan and the routing of the token it passes
+// each slot's weight base (null: host-executed) and routing weight directly.
+struct GemvExperts {
+    int valid;
+    const uint8_t* base[kMaxK + 1];
+    float w[kMaxK + 1];
+};
 hipError_t launch_ffn_gemv(int fmt, const Layout& lay, GroupW gw, const DevPlan* plan,
                            const int32_t* ids, const float* w, int k, int E, int has_shared,
                            int H, int I, const void* x, int act_bf16, float* h_buf,
-                           float* y_parts, hipStream_t s, hipEvent_t* ev /*[3], may be null*/,
-                           int allow_fast);
+                           float* y_parts, hipStream_t s,
+                           hipEvent_t* ev /*[4]: start/stop of each kernel, entries may be null*/,
+                           int allow_fast, const GemvExperts* ex /*may be null*/);
 // Sum of the GEMV partials (k + shared rows of [H]) plus host results.
 hipError_t launch_gemv_reduce(const float* y_parts, int nparts, const float* y_host, int H,
                               float* y, void* x_res, int act_bf16, hipStream_t s);

@@ -20,6 +20,8 @@
 //
 // fp32 weights with fp32 activations (small test models) use a plain VALU
 // kernel with the same grouping and epilogues.
+#include <hip/hip_ext.h>
+
 #include <cstdlib>
 
 #include "dev_common.h"
@@ -578,11 +580,10 @@ bool run_v3(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hi
     }
     const int n1 = I / 128, n2 = H / 256;
     auto grid = [&](int nN) { return ((tiles * nN + 7) / 8) * 8; };
-    if (ev[0]) (void)hipEventRecord(ev[0], s);
-    k_gemm_v3<FMT, 0><<<grid(n1), 256, kV3Lds, s>>>(a1, n1);
-    if (ev[1]) (void)hipEventRecord(ev[1], s);
-    k_gemm_v3<FMT, 1><<<grid(n2), 256, kV3Lds, s>>>(a2, n2);
-    if (ev[2]) (void)hipEventRecord(ev[2], s);
+    hipExtLaunchKernelGGL(k_gemm_v3<FMT, 0>, dim3(grid(n1)), dim3(256), (uint32_t)kV3Lds, s,
+                          ev[0], ev[1], 0, a1, n1);
+    hipExtLaunchKernelGGL(k_gemm_v3<FMT, 1>, dim3(grid(n2)), dim3(256), (uint32_t)kV3Lds, s,
+                          ev[2], ev[3], 0, a2, n2);
     return true;
 }
 
@@ -774,11 +775,10 @@ bool run_v4(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hi
     }
     const int n1 = I / 128, n2 = H / 256;
     auto grid = [&](int nN) { return ((tiles * nN + 7) / 8) * 8; };
-    if (ev[0]) (void)hipEventRecord(ev[0], s);
-    k_gemm_v4<0><<<grid(n1), 256, kV4Lds, s>>>(a1, n1);
-    if (ev[1]) (void)hipEventRecord(ev[1], s);
-    k_gemm_v4<1><<<grid(n2), 256, kV4Lds, s>>>(a2, n2);
-    if (ev[2]) (void)hipEventRecord(ev[2], s);
+    hipExtLaunchKernelGGL(k_gemm_v4<0>, dim3(grid(n1)), dim3(256), (uint32_t)kV4Lds, s, ev[0],
+                          ev[1], 0, a1, n1);
+    hipExtLaunchKernelGGL(k_gemm_v4<1>, dim3(grid(n2)), dim3(256), (uint32_t)kV4Lds, s, ev[2],
+                          ev[3], 0, a2, n2);
     return true;
 }
 
@@ -786,11 +786,10 @@ template <int FMT>
 void run_mfma(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hipEvent_t* ev) {
     if (FMT == EO_W_BF16 && g_gemm_tiles >= 2 && run_v4(a1, a2, tiles, I, H, s, ev)) return;
     if (g_gemm_tiles && run_v3<FMT>(a1, a2, tiles, I, H, s, ev)) return;
-    if (ev[0]) (void)hipEventRecord(ev[0], s);
-    k_gemm_mfma<FMT, 0><<<dim3(tiles, I / 64), 256, 0, s>>>(a1);
-    if (ev[1]) (void)hipEventRecord(ev[1], s);
-    k_gemm_mfma<FMT, 1><<<dim3(tiles, H / 128), 256, 0, s>>>(a2);
-    if (ev[2]) (void)hipEventRecord(ev[2], s);
+    hipExtLaunchKernelGGL(k_gemm_mfma<FMT, 0>, dim3(tiles, I / 64), dim3(256), 0, s, ev[0], ev[1],
+                          0, a1);
+    hipExtLaunchKernelGGL(k_gemm_mfma<FMT, 1>, dim3(tiles, H / 128), dim3(256), 0, s, ev[2], ev[3],
+                          0, a2);
 }
 
 }  // namespace
@@ -829,11 +828,10 @@ hipError_t launch_ffn_gemm(int fmt, const Layout& lay, GroupW gw, int E, int has
     a2.A = (const uint16_t*)h_buf;
     switch (fmt) {
     case EO_W_FP32:
-        if (ev[0]) (void)hipEventRecord(ev[0], s);
-        k_gemm_f32<0><<<dim3(tiles, I / 32), 256, 0, s>>>(a1, (const float*)x_perm, (float*)h_buf);
-        if (ev[1]) (void)hipEventRecord(ev[1], s);
-        k_gemm_f32<1><<<dim3(tiles, H / 64), 256, 0, s>>>(a2, (const float*)h_buf, nullptr);
-        if (ev[2]) (void)hipEventRecord(ev[2], s);
+        hipExtLaunchKernelGGL(k_gemm_f32<0>, dim3(tiles, I / 32), dim3(256), 0, s, ev[0], ev[1],
+                              0, a1, (const float*)x_perm, (float*)h_buf);
+        hipExtLaunchKernelGGL(k_gemm_f32<1>, dim3(tiles, H / 64), dim3(256), 0, s, ev[2], ev[3], 0,
+                              a2, (const float*)h_buf, (float*)nullptr);
         break;
     case EO_W_BF16: run_mfma<EO_W_BF16>(a1, a2, tiles, I, H, s, ev); break;
     case EO_W_FP8: run_mfma<EO_W_FP8>(a1, a2, tiles, I, H, s, ev); break;

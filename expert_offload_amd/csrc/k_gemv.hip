@@ -10,6 +10,10 @@
 //   phase B: y_j = w_j * W_down h_j                               (fp32 [H])
 // followed by a reduction over j in fixed order (plus host-executed results).
 // Experts the plan sends to the host are skipped here (phase B writes zeros).
+#include <hip/hip_ext.h>
+
+#include <cstdlib>
+
 #include "dev_common.h"
 #include "eo_internal.h"
 
@@ -29,6 +33,7 @@ struct GemvArgs {
     const void* x;
     float* h;      // [nexp, I]
     float* yp;     // [nexp, H]
+    GemvExperts ex;  // when ex.valid: weight base and routing weight per slot j
 };
 
 // Elements per 16-byte weight chunk.
@@ -133,6 +138,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Resolve expert j of this decode call: weight base, or null if host-executed.
 __device__ __forceinline__ const uint8_t* expert_base(const GemvArgs& a, int j) {
+    if (a.ex.valid) return a.ex.base[j];
     if (j == a.k) return a.gw.shared_w;
     int e = a.ids[j];
     if (e < 0 || e >= a.E) return nullptr;
@@ -421,7 +427,7 @@ __global__ __launch_bounds__(256) void k_gemv_dn(GemvArgs a, const uint16_t* __r
     rows_dot<FMT, GB, NCB, RB>(wb + a.lay.d2, wb + a.lay.s2, a.I, rows, hb + (size_t)j * a.I, gl,
                                out);
     if (gl == 0) {
-        const float wj = j < a.k ? a.w[j] : 1.0f;
+        const float wj = a.ex.valid ? a.ex.w[j] : (j < a.k ? a.w[j] : 1.0f);
         const float* rs = (const float*)(wb + a.lay.s2);
         const float gs = FMT == EO_W_NVFP4 ? ((const float*)(wb + a.lay.gl))[2] : 1.0f;
 #pragma unroll
@@ -431,6 +437,8 @@ __global__ __launch_bounds__(256) void k_gemv_dn(GemvArgs a, const uint16_t* __r
         }
     }
 }
+
+int g_gemv_variant = -1;  // EO_GEMV_VARIANT selects a tuning variant (0 = default)
 
 // Lanes per row G and chunks per lane NC for a row of `nch` chunks.
 bool split_rows(int nch, int* G, int* NC) {
@@ -448,11 +456,10 @@ hipError_t run_fast(const GemvArgs& a, uint16_t* hb, hipStream_t s, hipEvent_t* 
     const int rowsA = 4 * (64 / GA) * RA, rowsB = 4 * (64 / GB) * RB;
     if (a.I % rowsA || a.H % rowsB) return hipErrorNotSupported;
     const int nA_per = a.I / rowsA, nB_per = a.H / rowsB;
-    if (ev[0]) (void)hipEventRecord(ev[0], s);
-    k_gemv_gu<FMT, GA, NCA, RA><<<a.nexp * nA_per, 256, 0, s>>>(a, hb, nA_per);
-    if (ev[1]) (void)hipEventRecord(ev[1], s);
-    k_gemv_dn<FMT, GB, NCB, RB><<<a.nexp * nB_per, 256, 0, s>>>(a, hb, nB_per);
-    if (ev[2]) (void)hipEventRecord(ev[2], s);
+    hipExtLaunchKernelGGL(k_gemv_gu<FMT, GA, NCA, RA>, dim3(a.nexp * nA_per), dim3(256), 0, s,
+                          ev[0], ev[1], 0, a, hb, nA_per);
+    hipExtLaunchKernelGGL(k_gemv_dn<FMT, GB, NCB, RB>, dim3(a.nexp * nB_per), dim3(256), 0, s,
+                          ev[2], ev[3], 0, a, (const uint16_t*)hb, nB_per);
     return hipGetLastError();
 }
 
@@ -466,7 +473,16 @@ hipError_t fast_dispatch(const GemvArgs& a, uint16_t* hb, hipStream_t s, hipEven
 #define EO_FAST(ga, nca, ra, gb, ncb, rb)                         \
     if (GA == ga && NCA == nca && GB == gb && NCB == ncb)         \
         return run_fast<FMT, ga, nca, ra, gb, ncb, rb>(a, hb, s, ev);
-    EO_FAST(64, 4, 2, 32, 3, 2)  // bf16 H 2048, I 768
+    if (FMT == EO_W_BF16 && GA == 64 && NCA == 4 && GB == 32 && NCB == 3) {
+        switch (g_gemv_variant) {  // rows per lane group (gate/up, down); tuning sweep
+        case 2: return run_fast<FMT, 64, 4, 4, 32, 3, 4>(a, hb, s, ev);
+        case 3: return run_fast<FMT, 64, 4, 1, 32, 3, 2>(a, hb, s, ev);
+        case 4: return run_fast<FMT, 64, 4, 2, 32, 3, 4>(a, hb, s, ev);
+        case 5: return run_fast<FMT, 64, 4, 2, 32, 3, 2>(a, hb, s, ev);
+        default: break;
+        }
+    }
+    EO_FAST(64, 4, 1, 32, 3, 1)  // bf16 H 2048, I 768
     EO_FAST(64, 1, 4, 32, 1, 4)  // bf16 H 512, I 256
     EO_FAST(32, 1, 4, 16, 1, 4)  // fp8 H 512, I 256
     EO_FAST(64, 2, 4, 64, 1, 4)  // fp4 H 4096, I 2048
@@ -480,11 +496,10 @@ hipError_t fast_dispatch(const GemvArgs& a, uint16_t* hb, hipStream_t s, hipEven
 
 template <int FMT, bool XBF16>
 void run(const GemvArgs& a, hipStream_t s, hipEvent_t* ev) {
-    if (ev[0]) (void)hipEventRecord(ev[0], s);
-    k_gemv_up<FMT, XBF16><<<dim3(a.I / (4 * kRowsA), a.nexp), 256, 0, s>>>(a);
-    if (ev[1]) (void)hipEventRecord(ev[1], s);
-    k_gemv_down<FMT><<<dim3(a.H / (4 * kRowsB), a.nexp), 256, 0, s>>>(a);
-    if (ev[2]) (void)hipEventRecord(ev[2], s);
+    hipExtLaunchKernelGGL(k_gemv_up<FMT, XBF16>, dim3(a.I / (4 * kRowsA), a.nexp), dim3(256), 0,
+                          s, ev[0], ev[1], 0, a);
+    hipExtLaunchKernelGGL(k_gemv_down<FMT>, dim3(a.H / (4 * kRowsB), a.nexp), dim3(256), 0, s,
+                          ev[2], ev[3], 0, a);
 }
 
 }  // namespace
@@ -492,7 +507,8 @@ void run(const GemvArgs& a, hipStream_t s, hipEvent_t* ev) {
 hipError_t launch_ffn_gemv(int fmt, const Layout& lay, GroupW gw, const DevPlan* plan,
                            const int32_t* ids, const float* w, int k, int E, int has_shared,
                            int H, int I, const void* x, int act_bf16, float* h_buf,
-                           float* y_parts, hipStream_t s, hipEvent_t* ev, int allow_fast) {
+                           float* y_parts, hipStream_t s, hipEvent_t* ev, int allow_fast,
+                           const GemvExperts* ex) {
     GemvArgs a{};
     a.gw = gw;
     a.lay = lay;
@@ -507,6 +523,11 @@ hipError_t launch_ffn_gemv(int fmt, const Layout& lay, GroupW gw, const DevPlan*
     a.x = x;
     a.h = h_buf;
     a.yp = y_parts;
+    if (ex) a.ex = *ex;
+    if (g_gemv_variant < 0) {
+        const char* v = getenv("EO_GEMV_VARIANT");
+        g_gemv_variant = v ? atoi(v) : 0;
+    }
     if (allow_fast && act_bf16 && fmt != EO_W_FP32) {
         hipError_t he = hipErrorNotSupported;
         uint16_t* hb = (uint16_t*)h_buf;

@@ -213,8 +213,9 @@ eo_status eo_last_plan(eo_engine* e, eo_plan_host* out);
  * [W_gate (I*H) | W_up (I*H) | W_down (H*I)]. Synchronous. */
 eo_status eo_dequant(eo_engine* e, int32_t layer, int32_t expert, float* out_host);
 eo_status eo_stats_get(eo_engine* e, eo_stats* out);
-/* Device time of the expert FFN kernels since the last reset, from HIP events
- * recorded on the compute stream around each kernel while timing is enabled:
+/* Device time of the expert FFN kernels since the last reset, from HIP start/stop
+ * events attached to each kernel launch on the compute stream while timing is
+ * enabled (hipExtLaunchKernel: the events take the kernel's own start and end):
  * ms[0] decode GEMV gate/up kernel, ms[1] decode GEMV down kernel, ms[2] grouped
  * GEMM gate/up (+SwiGLU) kernel, ms[3] grouped GEMM down kernel (totals);
  * launches[0] decode GEMV pairs, launches[1] grouped GEMM pairs. Either pointer

@@ -69,6 +69,8 @@ struct eo_engine {
     uint8_t* d_slots = nullptr;
     uint8_t* d_shared = nullptr;
     float* d_router = nullptr;
+    float* d_router_t = nullptr;  // per-chain layout [L][E][64][H/64]
+    uint16_t* d_xt = nullptr;     // [max_tokens][64][H/64] bf16 scratch
     int32_t* d_slot_key = nullptr;
     int64_t* d_slot_stamp = nullptr;
     int32_t* d_key2slot = nullptr;
@@ -414,8 +416,9 @@ eo_status do_combine(eo_engine* e, const int32_t* ids, float* y, void* x_res, hi
 eo_status moe_layer_impl(eo_engine* e, int layer, const void* x, float* y, int T,
                          const int32_t* forced, int32_t* ids, float* w, void* x_res,
                          hipStream_t s) {
-    hipError_t he = launch_route(x, e->act_bf16, e->d_router + (size_t)layer * e->E * e->H, T,
-                                 e->E, e->H, e->k, forced, ids, w, e->d_z, s);
+    const size_t roff = (size_t)layer * e->E * e->H;
+    hipError_t he = launch_route(x, e->act_bf16, e->d_router + roff, e->d_router_t + roff, T,
+                                 e->E, e->H, e->k, forced, ids, w, e->d_z, e->d_xt, s);
     if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("route: ") + hipGetErrorString(he));
     EOCHK(do_plan(e, layer, ids, w, x, T, s));
     EOCHK(do_fill(e, s));
@@ -450,7 +453,8 @@ void destroy_all(eo_engine* e) {
         if (p) (void)hipHostFree(p);
     auto fr = [](void* p) { if (p) (void)hipFree(p); };
     auto fh = [](void* p) { if (p) (void)hipHostFree(p); };
-    fr(e->d_slots); fr(e->d_shared); fr(e->d_router); fr(e->d_slot_key); fr(e->d_slot_stamp);
+    fr(e->d_slots); fr(e->d_shared); fr(e->d_router); fr(e->d_router_t); fr(e->d_xt);
+    fr(e->d_slot_key); fr(e->d_slot_stamp);
     fr(e->d_key2slot); fr(e->d_state); fr(e->d_plan); fr(e->d_ids); fr(e->d_w); fr(e->d_z);
     fr(e->d_y); fr(e->d_hgemv); fr(e->d_yparts); fr(e->d_yhost);
     fr(e->pb.counts); fr(e->pb.offsets); fr(e->pb.tile_off); fr(e->pb.perm_pair);
@@ -519,6 +523,10 @@ eo_status create_impl(const eo_config* cfg, eo_engine* e) {
     }
     EOCHK(dmalloc(&e->d_router, sizeof(float) * e->L * e->E * e->H));
     HIPCHK(hipMemset(e->d_router, 0, sizeof(float) * e->L * e->E * e->H));
+    EOCHK(dmalloc(&e->d_router_t, sizeof(float) * e->L * e->E * e->H));
+    HIPCHK(hipMemset(e->d_router_t, 0, sizeof(float) * e->L * e->E * e->H));
+    if (e->act_bf16 && cfg->max_tokens >= 32 && e->H % 512 == 0)
+        EOCHK(dmalloc(&e->d_xt, sizeof(uint16_t) * (size_t)cfg->max_tokens * e->H));
     EOCHK(dmalloc(&e->d_slot_key, sizeof(int32_t) * e->C));
     EOCHK(dmalloc(&e->d_slot_stamp, sizeof(int64_t) * e->C));
     EOCHK(dmalloc(&e->d_key2slot, sizeof(int32_t) * e->L * e->E));
@@ -638,6 +646,15 @@ eo_status eo_set_router(eo_engine* e, int32_t layer, const float* host_w) {
     HIPCHK(hipSetDevice(e->cfg.device));
     HIPCHK(hipMemcpy(e->d_router + (size_t)layer * e->E * e->H, host_w,
                      sizeof(float) * e->E * e->H, hipMemcpyHostToDevice));
+    // per-chain copy: Rt[e][i][j] = R[e][i + 64 j]
+    const int J = e->H / 64;
+    std::vector<float> rt((size_t)e->E * e->H);
+    for (int x = 0; x < e->E; ++x)
+        for (int i = 0; i < 64; ++i)
+            for (int j = 0; j < J; ++j)
+                rt[((size_t)x * 64 + i) * J + j] = host_w[(size_t)x * e->H + i + 64 * j];
+    HIPCHK(hipMemcpy(e->d_router_t + (size_t)layer * e->E * e->H, rt.data(),
+                     sizeof(float) * e->E * e->H, hipMemcpyHostToDevice));
     return EO_OK;
 }
 
@@ -741,8 +758,10 @@ eo_status eo_route(eo_engine* e, int32_t layer, const void* x, int32_t T, const 
     EOCHK(check_layer(e, layer));
     EOCHK(check_T(e, T));
     if (!x || !ids || !w) return fail(EO_ERR_INVALID_ARG, "null pointer");
-    hipError_t he = launch_route(x, e->act_bf16, e->d_router + (size_t)layer * e->E * e->H, T, e->E,
-                                 e->H, e->k, forced_ids, ids, w, e->d_z, (hipStream_t)stream);
+    const size_t roff = (size_t)layer * e->E * e->H;
+    hipError_t he = launch_route(x, e->act_bf16, e->d_router + roff, e->d_router_t + roff, T, e->E,
+                                 e->H, e->k, forced_ids, ids, w, e->d_z, e->d_xt,
+                                 (hipStream_t)stream);
     if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("route: ") + hipGetErrorString(he));
     return EO_OK;
 }
@@ -852,8 +871,9 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t double_buff
             w = e->cap_w + (size_t)l * e->cap_T * e->k;
             y = e->cap_y + (size_t)l * e->cap_T * e->H;
         }
-        hipError_t he = launch_route(x_inout, e->act_bf16, e->d_router + (size_t)l * e->E * e->H, T,
-                                     e->E, e->H, e->k, nullptr, ids, w, e->d_z, s);
+        const size_t roff = (size_t)l * e->E * e->H;
+        hipError_t he = launch_route(x_inout, e->act_bf16, e->d_router + roff, e->d_router_t + roff,
+                                     T, e->E, e->H, e->k, nullptr, ids, w, e->d_z, e->d_xt, s);
         if (he == hipSuccess)
             he = launch_permute(ids, nullptr, 1, T, e->k, e->E, e->shared, x_inout, e->act_bf16,
                                 e->H, e->pb, s);

@@ -37,9 +37,11 @@ struct DevState {
 
 // ---------------------------------------------------------------- launches
 // Router (fixed-order fp32 logits, top-k, softmax).
-hipError_t launch_route(const void* x, int act_bf16, const float* R, int T, int E, int H, int k,
-                        const int32_t* forced, int32_t* ids, float* w, float* z_scratch,
-                        hipStream_t s);
+// Rt: R laid out per chain ([E][64][H/64]) and xT: scratch for x laid out the
+// same way ([T][64][H/64] bf16); both optional (then the direct kernel runs).
+hipError_t launch_route(const void* x, int act_bf16, const float* R, const float* Rt, int T,
+                        int E, int H, int k, const int32_t* forced, int32_t* ids, float* w,
+                        float* z_scratch, uint16_t* xT, hipStream_t s);
 
 // Lookup + LRU + miss plan, single workgroup; writes plan to d_plan and a
 // mirror (header, lists, ids, w and, when x_mirror != null, x) to host memory.

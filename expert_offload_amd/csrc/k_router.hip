@@ -141,17 +141,104 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ z, int T
     }
 }
 
+// ---------------------------------------------------------------- many tokens
+// Same accumulation order, with the operands laid out per chain: chain i of
+// row r is stored contiguously (xT[t][i][j] = x[t][i + 64 j], Rt[e][i][j] =
+// R[e][i + 64 j]), so lane i reads 8 (x) or 4 (R) consecutive steps j with one
+// 16-byte load instead of one element per load. The FMAs still run j = 0, 1, ...
+// in order from +0, and the butterfly is unchanged, so z is bit-identical.
+constexpr int kTT2 = 8, kEE2 = 8;
+
+__global__ __launch_bounds__(64) void k_chain_transpose(const uint16_t* __restrict__ x, int H,
+                                                        uint16_t* __restrict__ xT) {
+    const int t = blockIdx.x, i = threadIdx.x, J = H / 64;
+    const uint16_t* xr = x + (size_t)t * H;
+    uint16_t* dst = xT + ((size_t)t * 64 + i) * J;
+    for (int j0 = 0; j0 < J; j0 += 8) {
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            w[q] = (uint32_t)xr[i + 64 * (j0 + 2 * q)] | ((uint32_t)xr[i + 64 * (j0 + 2 * q + 1)] << 16);
+        *(uint4*)(dst + j0) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_logits_chains(const uint16_t* __restrict__ xT,
+                                                       const float* __restrict__ Rt, int T, int E,
+                                                       int H, float* __restrict__ z) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * kTT2;
+    const int e0 = (blockIdx.y * 4 + wave) * kEE2;
+    const int J = H / 64;
+    float acc[kTT2][kEE2];
+#pragma unroll
+    for (int a = 0; a < kTT2; ++a)
+#pragma unroll
+        for (int b = 0; b < kEE2; ++b) acc[a][b] = 0.0f;
+    const uint16_t* xp[kTT2];
+#pragma unroll
+    for (int a = 0; a < kTT2; ++a) xp[a] = xT + ((size_t)min(t0 + a, T - 1) * 64 + lane) * J;
+    const float* rp[kEE2];
+#pragma unroll
+    for (int b = 0; b < kEE2; ++b) rp[b] = Rt + ((size_t)(e0 + b) * 64 + lane) * J;
+    for (int j0 = 0; j0 < J; j0 += 8) {
+        float xv[kTT2][8];
+#pragma unroll
+        for (int a = 0; a < kTT2; ++a) {
+            uint4 q = *(const uint4*)(xp[a] + j0);
+            uint32_t wds[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                xv[a][2 * c] = bf16_f32(wds[c] & 0xFFFFu);
+                xv[a][2 * c + 1] = bf16_f32(wds[c] >> 16);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < kEE2; ++b) {
+            float4 r0 = *(const float4*)(rp[b] + j0), r1 = *(const float4*)(rp[b] + j0 + 4);
+            float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+                for (int a = 0; a < kTT2; ++a) acc[a][b] = __builtin_fmaf(xv[a][jj], rv[jj], acc[a][b]);
+        }
+    }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+#pragma unroll
+        for (int a = 0; a < kTT2; ++a)
+#pragma unroll
+            for (int b = 0; b < kEE2; ++b) acc[a][b] = acc[a][b] + __shfl_xor(acc[a][b], s, 64);
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int a = 0; a < kTT2; ++a)
+            if (t0 + a < T)
+#pragma unroll
+                for (int b = 0; b < kEE2; ++b) z[(size_t)(t0 + a) * E + e0 + b] = acc[a][b];
+    }
+}
+
 }  // namespace
 
-hipError_t launch_route(const void* x, int act_bf16, const float* R, int T, int E, int H, int k,
-                        const int32_t* forced, int32_t* ids, float* w, float* g_z,
-                        hipStream_t s) {
+bool route_chains_ok(int T, int E, int H, int act_bf16) {
+    return act_bf16 && T >= 32 && H % 512 == 0 && E % (4 * kEE2) == 0;
+}
+
+hipError_t launch_route(const void* x, int act_bf16, const float* R, const float* Rt, int T,
+                        int E, int H, int k, const int32_t* forced, int32_t* ids, float* w,
+                        float* g_z, uint16_t* xT, hipStream_t s) {
     if (T <= 0) return hipSuccess;
-    dim3 grid((T + kTT - 1) / kTT, (E + 4 * kEE - 1) / (4 * kEE));
-    if (act_bf16)
-        k_logits<true><<<grid, 256, 0, s>>>(x, R, T, E, H, g_z);
-    else
-        k_logits<false><<<grid, 256, 0, s>>>(x, R, T, E, H, g_z);
+    if (Rt && xT && route_chains_ok(T, E, H, act_bf16)) {
+        k_chain_transpose<<<T, 64, 0, s>>>((const uint16_t*)x, H, xT);
+        k_logits_chains<<<dim3((T + kTT2 - 1) / kTT2, E / (4 * kEE2)), 256, 0, s>>>(xT, Rt, T, E, H, g_z);
+    } else {
+        dim3 grid((T + kTT - 1) / kTT, (E + 4 * kEE - 1) / (4 * kEE));
+        if (act_bf16)
+            k_logits<true><<<grid, 256, 0, s>>>(x, R, T, E, H, g_z);
+        else
+            k_logits<false><<<grid, 256, 0, s>>>(x, R, T, E, H, g_z);
+    }
     k_topk<<<(T + 3) / 4, 256, 0, s>>>(g_z, T, E, k, forced, ids, w);
     return hipGetLastError();
 }

@@ -9,7 +9,8 @@
  *
  * Random numbers: Philox4x32-10, the counter-based generator of Salmon, Moraes,
  * Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC'11), written
- * from its published definition. Normals come from the Box-Muller transform.
+ * from its published definition. Normals come from the inverse normal CDF
+ * (Acklam's rational approximation) of one uniform each.
  *
  * Expert block layout (one routed or shared expert, hidden H, intermediate I):
  *   W13 = [W_gate ; W_up], 2I rows of H elements (row r < I is gate row r,
@@ -62,23 +63,44 @@ void synth_philox4x32_10(const uint32_t* ctr, const uint32_t* key, uint32_t* out
     philox4x32_10(ctr, key, out);
 }
 
-/* Element i of stream (seed, purpose, c1, c2, c3): Philox block i/4 with
- * counter {i/4, c1, c2, c3} and key {seed, purpose}; the block's four words
- * give two Box-Muller pairs. */
+/* Inverse of the standard normal CDF: P. J. Acklam's rational approximation
+ * (relative error below 1.2e-9), central region and tails. */
+static double inv_norm_cdf(double p) {
+    static const double a[6] = {-3.969683028665376e+01, 2.209460984245205e+02,
+                                -2.759285104469687e+02, 1.383577518672690e+02,
+                                -3.066479806614716e+01, 2.506628277459239e+00};
+    static const double b[5] = {-5.447609879822406e+01, 1.615858368580409e+02,
+                                -1.556989798598866e+02, 6.680131188771972e+01,
+                                -1.328068155288572e+01};
+    static const double c[6] = {-7.784894002430293e-03, -3.223964580411365e-01,
+                                -2.400758277161838e+00, -2.549732539343734e+00,
+                                4.374664141464968e+00, 2.938163982698783e+00};
+    static const double d[4] = {7.784695709041462e-03, 3.224671290700398e-01,
+                                2.445134137142996e+00, 3.754408661907416e+00};
+    const double plow = 0.02425;
+    if (p < plow) {
+        double q = sqrt(-2.0 * log(p));
+        return (((((c[0] * q + c[1]) * q + c[2]) * q + c[3]) * q + c[4]) * q + c[5]) /
+               ((((d[0] * q + d[1]) * q + d[2]) * q + d[3]) * q + 1.0);
+    }
+    if (p > 1.0 - plow) {
+        double q = sqrt(-2.0 * log(1.0 - p));
+        return -(((((c[0] * q + c[1]) * q + c[2]) * q + c[3]) * q + c[4]) * q + c[5]) /
+               ((((d[0] * q + d[1]) * q + d[2]) * q + d[3]) * q + 1.0);
+    }
+    double q = p - 0.5, r = q * q;
+    return (((((a[0] * r + a[1]) * r + a[2]) * r + a[3]) * r + a[4]) * r + a[5]) * q /
+           (((((b[0] * r + b[1]) * r + b[2]) * r + b[3]) * r + b[4]) * r + 1.0);
+}
+
+/* Element i of stream (seed, purpose, c1, c2, c3): word i%4 of Philox block i/4
+ * with counter {i/4, c1, c2, c3} and key {seed, purpose}, as a uniform in (0,1)
+ * (32-bit grid, offset by half a step), mapped through the inverse normal CDF. */
 static void normal_block(uint32_t seed, uint32_t purpose, uint32_t c1, uint32_t c2, uint32_t c3,
                          uint32_t blk, float z[4]) {
     uint32_t ctr[4] = {blk, c1, c2, c3}, key[2] = {seed, purpose}, w[4];
     philox4x32_10(ctr, key, w);
-    const float two_pi = 6.28318530717958647692f;
-    for (int p = 0; p < 2; ++p) {
-        /* uniforms in (0, 1): 24-bit grid, offset by half a step */
-        float u1 = ((float)(w[2 * p] >> 8) + 0.5f) * (1.0f / 16777216.0f);
-        float u2 = ((float)(w[2 * p + 1] >> 8) + 0.5f) * (1.0f / 16777216.0f);
-        float r = sqrtf(-2.0f * logf(u1)), s, c;
-        sincosf(two_pi * u2, &s, &c);
-        z[2 * p] = r * c;
-        z[2 * p + 1] = r * s;
-    }
+    for (int j = 0; j < 4; ++j) z[j] = (float)inv_norm_cdf(((double)w[j] + 0.5) * (1.0 / 4294967296.0));
 }
 
 static void normal_fill(uint32_t seed, uint32_t purpose, uint32_t c1, uint32_t c2, uint32_t c3,
@@ -135,9 +157,15 @@ static uint32_t encode_minifloat(double q, int mbits, int emin, int bias) {
     return ((uint32_t)(e + bias) << mbits) | mant;
 }
 
-static uint8_t e2m1_code(double v) { /* v already divided by its scale */
-    double q = round_minifloat(fabs(v), 1, 0, 6.0);
-    return (uint8_t)((signbit(v) ? 0x8u : 0u) | encode_minifloat(q, 1, 0, 1));
+/* e2m1 code of v (already divided by its scale), round half to even, saturating:
+ * the midpoints of 0, .5, 1, 1.5, 2, 3, 4, 6 are .25, .75, 1.25, 1.75, 2.5, 3.5, 5;
+ * a tie goes to the even code (0, 1.0, 2.0, 4.0), hence > before odd codes and
+ * >= before even ones. */
+static uint8_t e2m1_code(double v) {
+    double m = fabs(v);
+    uint32_t c = (m > 0.25) + (m >= 0.75) + (m > 1.25) + (m >= 1.75) + (m > 2.5) + (m >= 3.5) +
+                 (m > 5.0);
+    return (uint8_t)((signbit(v) ? 0x8u : 0u) | c);
 }
 
 static uint8_t e4m3_code(double v) {
@@ -200,9 +228,10 @@ static void quantise_rows(const float* w, int64_t rows, int64_t K, int fmt, floa
                 if (se < -127) se = -127;
                 if (se > 127) se = 127;
                 scales[r * (K / 32) + b] = (uint8_t)(se + 127);
+                const double inv = ldexp(1.0, -se); /* exact power of two */
                 for (int i = 0; i < 32; i += 2) {
-                    uint8_t lo = e2m1_code(ldexp((double)row[32 * b + i], -se));
-                    uint8_t hi = e2m1_code(ldexp((double)row[32 * b + i + 1], -se));
+                    uint8_t lo = e2m1_code((double)row[32 * b + i] * inv);
+                    uint8_t hi = e2m1_code((double)row[32 * b + i + 1] * inv);
                     o[(32 * b + i) / 2] = (uint8_t)(lo | (hi << 4));
                 }
             }

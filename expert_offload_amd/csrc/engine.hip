@@ -89,6 +89,7 @@ struct eo_engine {
     float* d_w = nullptr;
     float* d_z = nullptr;
     float* d_y = nullptr;
+    void* d_u = nullptr;  // [max_tokens, H] layer input (RMS-normalised residual)
     float* d_hgemv = nullptr;
     float* d_yparts = nullptr;
     float* d_yhost = nullptr;
@@ -456,7 +457,7 @@ void destroy_all(eo_engine* e) {
     fr(e->d_slots); fr(e->d_shared); fr(e->d_router); fr(e->d_router_t); fr(e->d_xt);
     fr(e->d_slot_key); fr(e->d_slot_stamp);
     fr(e->d_key2slot); fr(e->d_state); fr(e->d_plan); fr(e->d_ids); fr(e->d_w); fr(e->d_z);
-    fr(e->d_y); fr(e->d_hgemv); fr(e->d_yparts); fr(e->d_yhost);
+    fr(e->d_y); fr(e->d_u); fr(e->d_hgemv); fr(e->d_yparts); fr(e->d_yhost);
     fr(e->pb.counts); fr(e->pb.offsets); fr(e->pb.tile_off); fr(e->pb.perm_pair);
     fr(e->pb.chunk_cnt); fr(e->pb.x_perm); fr(e->d_hbuf); fr(e->d_opairs);
     fr(e->d_staging[0]); fr(e->d_staging[1]);
@@ -549,6 +550,7 @@ eo_status create_impl(const eo_config* cfg, eo_engine* e) {
     EOCHK(dmalloc(&e->d_w, sizeof(float) * Tm * e->k));
     EOCHK(dmalloc(&e->d_z, sizeof(float) * Tm * e->E));
     EOCHK(dmalloc(&e->d_y, sizeof(float) * Tm * e->H));
+    EOCHK(dmalloc(&e->d_u, (size_t)e->act_size * Tm * e->H));
     EOCHK(dmalloc(&e->d_hgemv, sizeof(float) * (e->k + 1) * e->I));
     EOCHK(dmalloc(&e->d_yparts, sizeof(float) * (e->k + 1) * e->H));
     EOCHK(dmalloc(&e->d_yhost, sizeof(float) * Tm * e->H));
@@ -821,14 +823,16 @@ eo_status eo_decode_step(eo_engine* e, void* x_inout, int32_t T, const int32_t* 
         int32_t* ids = e->d_ids;
         float* w = e->d_w;
         float* y = e->d_y;
+        hipError_t he = launch_rmsnorm(x_inout, e->d_u, T, e->H, e->act_bf16, s);
+        if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("rmsnorm: ") + hipGetErrorString(he));
         if (cap) {
             HIPCHK(hipMemcpyAsync((uint8_t*)e->cap_x + (size_t)l * e->cap_T * e->H * e->act_size,
-                                  x_inout, xb, hipMemcpyDeviceToDevice, s));
+                                  e->d_u, xb, hipMemcpyDeviceToDevice, s));
             ids = e->cap_ids + (size_t)l * e->cap_T * e->k;
             w = e->cap_w + (size_t)l * e->cap_T * e->k;
             y = e->cap_y + (size_t)l * e->cap_T * e->H;
         }
-        EOCHK(moe_layer_impl(e, l, x_inout, y, T, forced, ids, w, x_inout, s));
+        EOCHK(moe_layer_impl(e, l, e->d_u, y, T, forced, ids, w, x_inout, s));
     }
     if (e->timing) EOCHK(harvest_times(e));
     return EO_OK;
@@ -864,18 +868,20 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t double_buff
         int32_t* ids = e->d_ids;
         float* w = e->d_w;
         float* y = nullptr;
+        hipError_t he = launch_rmsnorm(x_inout, e->d_u, T, e->H, e->act_bf16, s);
+        if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("rmsnorm: ") + hipGetErrorString(he));
         if (cap) {
             HIPCHK(hipMemcpyAsync((uint8_t*)e->cap_x + (size_t)l * e->cap_T * e->H * e->act_size,
-                                  x_inout, xb, hipMemcpyDeviceToDevice, s));
+                                  e->d_u, xb, hipMemcpyDeviceToDevice, s));
             ids = e->cap_ids + (size_t)l * e->cap_T * e->k;
             w = e->cap_w + (size_t)l * e->cap_T * e->k;
             y = e->cap_y + (size_t)l * e->cap_T * e->H;
         }
         const size_t roff = (size_t)l * e->E * e->H;
-        hipError_t he = launch_route(x_inout, e->act_bf16, e->d_router + roff, e->d_router_t + roff,
-                                     T, e->E, e->H, e->k, nullptr, ids, w, e->d_z, e->d_xt, s);
+        he = launch_route(e->d_u, e->act_bf16, e->d_router + roff, e->d_router_t + roff, T, e->E,
+                          e->H, e->k, nullptr, ids, w, e->d_z, e->d_xt, s);
         if (he == hipSuccess)
-            he = launch_permute(ids, nullptr, 1, T, e->k, e->E, e->shared, x_inout, e->act_bf16,
+            he = launch_permute(ids, nullptr, 1, T, e->k, e->E, e->shared, e->d_u, e->act_bf16,
                                 e->H, e->pb, s);
         TimedSet ts{};
         if (e->timing) EOCHK(get_set(e, &ts));

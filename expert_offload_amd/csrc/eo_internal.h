@@ -106,6 +106,8 @@ hipError_t launch_gemv_reduce(const float* y_parts, int nparts, const float* y_h
 
 // Residual add: x = act(x + y), T*H elements.
 hipError_t launch_residual(void* x, const float* y, int64_t n, int act_bf16, hipStream_t s);
+// u [T,H] = RMS-normalised rows of r (activation dtype, 16-byte aligned rows).
+hipError_t launch_rmsnorm(const void* r, void* u, int T, int H, int act_bf16, hipStream_t s);
 
 // Debug dequant of one expert block to fp32 (device decoder).
 hipError_t launch_dequant(int fmt, const Layout& lay, const uint8_t* blk, int H, int I, float* out,

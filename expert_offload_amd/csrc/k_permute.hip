@@ -1,4 +1,5 @@
-// Token permutation by expert, weighted combine and residual.
+// Token permutation by expert, weighted combine, residual and the RMS
+// normalisation that turns the residual stream into a layer's input.
 //
 // Grouped expert execution needs each expert's tokens contiguous: the (token,
 // slot) pairs whose expert is device-resident are grouped by expert, stable in
@@ -199,7 +200,70 @@ __global__ __launch_bounds__(256) void k_residual(void* __restrict__ x, const fl
     }
 }
 
+// Layer input from the residual stream: u = r / sqrt(mean(r^2) + 1e-6), one
+// block per token. The sum of squares is taken in fp32 in a fixed order (per
+// lane, then a butterfly within each wavefront, then the wavefronts in order),
+// so the result does not depend on scheduling; u is rounded to the storage type.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_rmsnorm(const void* __restrict__ r, void* __restrict__ u,
+                                                 int H) {
+    __shared__ float part[4];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const int nv = BF16 ? H / 8 : H / 4;  // 16-byte vectors per row
+    const uint4* rv = (const uint4*)((const uint8_t*)r + (size_t)t * H * (BF16 ? 2 : 4));
+    uint4* uv = (uint4*)((uint8_t*)u + (size_t)t * H * (BF16 ? 2 : 4));
+    float ss = 0.0f;
+    for (int c = tid; c < nv; c += 256) {
+        uint4 v = rv[c];
+        if (BF16) {
+            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float a = bf16_f32(w[i] & 0xFFFFu), b = bf16_f32(w[i] >> 16);
+                ss = fmaf(a, a, ss);
+                ss = fmaf(b, b, ss);
+            }
+        } else {
+            float f[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                          __uint_as_float(v.w)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ss = fmaf(f[i], f[i], ss);
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    if ((tid & 63) == 0) part[tid >> 6] = ss;
+    __syncthreads();
+    const float tot = ((part[0] + part[1]) + part[2]) + part[3];
+    const float inv = 1.0f / sqrtf(tot / (float)H + 1e-6f);
+    for (int c = tid; c < nv; c += 256) {
+        uint4 v = rv[c];
+        if (BF16) {
+            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                w[i] = f32_bf16_rne(bf16_f32(w[i] & 0xFFFFu) * inv) |
+                       (f32_bf16_rne(bf16_f32(w[i] >> 16) * inv) << 16);
+            uv[c] = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+            uv[c] = make_uint4(__float_as_uint(__uint_as_float(v.x) * inv),
+                               __float_as_uint(__uint_as_float(v.y) * inv),
+                               __float_as_uint(__uint_as_float(v.z) * inv),
+                               __float_as_uint(__uint_as_float(v.w) * inv));
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_rmsnorm(const void* r, void* u, int T, int H, int act_bf16, hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    if (act_bf16)
+        k_rmsnorm<true><<<T, 256, 0, s>>>(r, u, H);
+    else
+        k_rmsnorm<false><<<T, 256, 0, s>>>(r, u, H);
+    return hipGetLastError();
+}
 
 hipError_t launch_permute(const int32_t* ids, const int32_t* e2slot, int all_resident, int T,
                           int k, int E, int has_shared, const void* x, int act_bf16, int H,

@@ -183,13 +183,16 @@ eo_status eo_expert_ffn_combine(eo_engine* e, int32_t layer, const void* x, cons
 eo_status eo_moe_layer(eo_engine* e, int32_t layer, const void* x, float* y, int32_t T,
                        const int32_t* forced_ids, void* stream);
 
-/* One decode step through all layers, in place: x_inout [T,H] (activation
- * dtype) becomes x + sum over layers of the MoE outputs (x_{l+1} = x_l + y_l,
- * stored in the activation dtype). forced_ids: device [L, T, k] or NULL. */
+/* One decode step through all layers, in place. x_inout [T,H] (activation
+ * dtype) is the residual stream r: layer l takes u_l = r_l / sqrt(mean(r_l^2)
+ * + 1e-6) per token (stored in the activation dtype; a parameter-free RMS
+ * normalisation, as in pre-norm transformer blocks) and r_{l+1} = r_l + y_l(u_l)
+ * (stored in the activation dtype). forced_ids: device [L, T, k] or NULL. */
 eo_status eo_decode_step(eo_engine* e, void* x_inout, int32_t T, const int32_t* forced_ids,
                          void* stream);
 
-/* Prefill of T tokens (T <= max_tokens) through all layers, in place, with
+/* Prefill of T tokens (T <= max_tokens) through all layers, in place (the
+ * same residual stream and normalisation as eo_decode_step), with
  * full-layer double-buffered streaming of each layer's E experts from the
  * pool (the cache is neither read nor updated). double_buffer = 0 serialises
  * copy and compute (ablation). */
@@ -197,7 +200,7 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t double_buff
                      void* stream);
 
 /* Optional per-layer capture for tests, device buffers written by
- * eo_decode_step / eo_prefill (NULL disables): x_in [L, T, H] layer inputs
+ * eo_decode_step / eo_prefill (NULL disables): x_in [L, T, H] layer inputs u_l
  * (activation dtype), y [L, T, H] fp32 MoE outputs, ids [L, T, k], w [L, T, k].
  * Capacity is given in tokens per layer. */
 eo_status eo_set_capture(eo_engine* e, void* x_in, float* y, int32_t* ids, float* w,

@@ -45,3 +45,23 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
 def oracle_layer(shape, seed, layer, x_f32, ids, w):
     return OM.layer_output(x_f32, ids, w, oracle_expert_fn(shape, seed, layer),
                            oracle_shared(shape, seed, layer))
+
+
+def check_residual_stream(x0_bits: np.ndarray, xin_bits: np.ndarray, ys: np.ndarray) -> np.ndarray:
+    """Multi-layer calls with bf16 activations: x0 [T,H] is the residual stream's
+    start, xin [L,T,H] the captured layer inputs, ys [L,T,H] the captured fp32
+    layer outputs. The stream is stored in bf16 after each layer (the device adds
+    in fp32, then rounds to nearest even, replayed here exactly); each layer input
+    must be the oracle's RMS-normalised stream within one bf16 unit in the last
+    place (the device normalises in fp32, the oracle in fp64).
+    Returns the expected bf16 bits of the stream after the last layer."""
+    r = np.asarray(x0_bits, dtype=np.uint16)
+    for l in range(xin_bits.shape[0]):
+        rf = synth.bf16_bits_to_f32(r)
+        ref = OM.layer_input(rf, True)
+        got = synth.bf16_bits_to_f32(xin_bits[l]).astype(np.float64)
+        ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(ref), 1e-30))[1] - 8)
+        assert np.all(np.abs(got - ref) <= ulp), f"layer {l}: normalised input off by > 1 ulp"
+        assert np.mean(got == ref) >= 0.98, f"layer {l}: too many 1-ulp differences"
+        r = synth.f32_to_bf16_bits(rf + ys[l])
+    return r

@@ -2,7 +2,9 @@
 
 Layer outputs are compared with the oracle within 2e-2 * max|ref| (bf16 / fp4 / fp8
 weights, bf16 activations); router ids must match bit for bit. Multi-layer calls
-capture each layer's input on the device and are checked per layer on that input.
+capture each layer's input on the device and are checked per layer on that input;
+the residual stream linking the layers is replayed from the captured outputs and
+each captured input checked against the oracle's normalisation of it.
 """
 import dataclasses
 
@@ -16,7 +18,7 @@ import synth  # noqa: E402
 from oracle import router as OR  # noqa: E402
 from oracle.residency import Residency  # noqa: E402
 from synth.workload import make_engine  # noqa: E402
-from tests.gpu_util import dev, oracle_layer, rel_err  # noqa: E402
+from tests.gpu_util import check_residual_stream, dev, oracle_layer, rel_err  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -113,7 +115,8 @@ def test_decode_steps_per_layer(fmt):
             eo.eo_decode_step(e, xd, 1, dev(trace[s].reshape(L, 1, k)), _stream())
             torch.cuda.synchronize()
             xin = cx.cpu().numpy().view(np.uint16)
-            assert np.array_equal(xin[0], x)
+            rL = check_residual_stream(x, xin, cy.cpu().numpy())
+            assert np.array_equal(xd.cpu().numpy().view(np.uint16), rL)
             for l in range(L):
                 assert np.array_equal(ci.cpu().numpy()[l, 0], trace[s, l])
                 xf = synth.bf16_bits_to_f32(xin[l])
@@ -123,9 +126,6 @@ def test_decode_steps_per_layer(fmt):
                 ref = oracle_layer(shape, seed, l, xf, ids, w)
                 assert rel_err(cy.cpu().numpy()[l], ref) <= TOL, (s, l)
                 res.lookup_plan(l, ids)
-                if l + 1 < L:  # next layer's input is bf16(x + y)
-                    nxt = synth.f32_to_bf16_bits(xf + cy.cpu().numpy()[l])
-                    assert np.array_equal(xin[l + 1], nxt), (s, l)
         keys = np.zeros(10, dtype=np.int32)
         stamps = np.zeros(10, dtype=np.int64)
         eo.eo_cache_snapshot(e, keys, stamps)
@@ -154,12 +154,10 @@ def test_prefill_per_layer(fmt, db):
         xin = cx.cpu().numpy().view(np.uint16)
         ys = cy.cpu().numpy()
         ids = ci.cpu().numpy()
-        assert np.array_equal(xin[0], x)
+        rL = check_residual_stream(x, xin, ys)
         for l in range(L):
             check_layer(shape, seed, l, xin[l], ys[l], ids[l])
-        out = xd.cpu().numpy().view(np.uint16)
-        last = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(xin[L - 1]) + ys[L - 1])
-        assert np.array_equal(out, last)
+        assert np.array_equal(xd.cpu().numpy().view(np.uint16), rL)
         st = eo.eo_stats_get(e)
         assert st["prefill_layers"] == L and st["lookups"] == 0
     finally:
@@ -175,16 +173,50 @@ def test_prefill_streaming_matches_cache_path():
     try:
         eo.eo_set_bandwidth(e, 9, 9)
         x = synth.activations(seed, 300, T, shape.hidden, 1.0, True)
-        y1 = torch.zeros((T, shape.hidden), dtype=torch.float32, device="cuda")
-        eo.eo_moe_layer(e, 0, dev(x.view(np.int16)), y1, T, None, _stream())
         cx = torch.zeros((1, T, shape.hidden), dtype=torch.int16, device="cuda")
         cy = torch.zeros((1, T, shape.hidden), dtype=torch.float32, device="cuda")
         ci = torch.zeros((1, T, shape.top_k), dtype=torch.int32, device="cuda")
         cw = torch.zeros((1, T, shape.top_k), dtype=torch.float32, device="cuda")
         eo.eo_set_capture(e, cx, cy, ci, cw, T)
         eo.eo_prefill(e, dev(x.view(np.int16)), T, 1, _stream())
+        # the layer's own input (the normalised stream) through the cache path
+        y1 = torch.zeros((T, shape.hidden), dtype=torch.float32, device="cuda")
+        eo.eo_moe_layer(e, 0, cx[0].clone(), y1, T, None, _stream())
         torch.cuda.synchronize()
         assert torch.equal(y1, cy[0])
+    finally:
+        eo.eo_destroy(e)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "nvfp4"])
+def test_decode_stack_against_oracle_chain(fmt):
+    # three layers on forced expert ids: the oracle runs the whole residual
+    # stream itself (normalise, route weights, layer, residual) from x0 alone
+    shape = small_shape(fmt, layers=3)
+    seed = 12
+    L, k, H = shape.layers, shape.top_k, shape.hidden
+    e = make_engine(shape, seed, cache_slots=20, max_tokens=1)
+    try:
+        eo.eo_set_bandwidth(e, 5, 7)
+        trace = synth.sticky_zipf_trace(seed, 3, L, shape.experts, k)
+        from oracle import moe as OM
+        from tests.gpu_util import oracle_expert_fn, oracle_shared
+        layers = None
+        for s in range(3):
+            x = synth.activations(seed, 700 + s, 1, H, 2.0, True)
+            xd = dev(x.view(np.int16))
+            eo.eo_decode_step(e, xd, 1, dev(trace[s].reshape(L, 1, k)), _stream())
+            torch.cuda.synchronize()
+            if layers is None:
+                layers = [[synth.router_weights(seed, l, shape.experts, H), k,
+                           oracle_expert_fn(shape, seed, l), oracle_shared(shape, seed, l), None]
+                          for l in range(L)]
+            for l in range(L):
+                layers[l][4] = trace[s, l][None, :]
+            rL, _ = OM.stack_forward(synth.bf16_bits_to_f32(x), [tuple(v) for v in layers], True)
+            got = synth.bf16_bits_to_f32(xd.cpu().numpy().view(np.uint16))
+            err = rel_err(got, rL)
+            assert err <= TOL, f"step {s}: rel err {err:.3e}"
     finally:
         eo.eo_destroy(e)
 

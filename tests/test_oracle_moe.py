@@ -81,3 +81,55 @@ def test_layer_output_invariant_to_slot_order():
     Y1 = moe.layer_output(X, ids, w, expert)
     Y2 = moe.layer_output(X, ids[:, perm], w[:, perm], expert)
     assert np.max(np.abs(Y1 - Y2)) <= 1e-13 * np.max(np.abs(Y1))
+
+
+def test_rmsnorm_pins():
+    rng = np.random.default_rng(9)
+    r = rng.standard_normal((5, 256)) * np.array([[0.01], [1.0], [7.0], [300.0], [2.0]])
+    u = moe.rmsnorm(r)
+    # unit mean square (up to eps), direction kept, scale invariant
+    assert np.allclose(np.mean(u * u, axis=1), 1.0 / (1.0 + moe.RMS_EPS / np.mean(r * r, axis=1)))
+    assert np.allclose(u / np.linalg.norm(u, axis=1, keepdims=True),
+                       r / np.linalg.norm(r, axis=1, keepdims=True), rtol=1e-14)
+    # scale invariant once eps is negligible (mean square 1 vs 9: eps/ms = 1e-6)
+    assert np.allclose(moe.rmsnorm(3.0 * r[1:2]), moe.rmsnorm(r[1:2]), rtol=1e-6, atol=0)
+    # hand-worked: (3, 4) has mean square 12.5
+    assert np.allclose(moe.rmsnorm(np.array([3.0, 4.0])), np.array([3.0, 4.0]) / np.sqrt(12.5 + 1e-6))
+    assert np.array_equal(moe.rmsnorm(np.zeros(4)), np.zeros(4))
+
+
+def test_round_bf16_against_torch_and_ties():
+    rng = np.random.default_rng(4)
+    # fp32-representable inputs: torch's fp32 -> bf16 conversion rounds once
+    v = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(moe.round_bf16(v.astype(np.float64)), ref)
+    # ties go to even: 1 + 2^-8 sits halfway between 1 and 1 + 2^-7
+    assert moe.round_bf16(np.array([1 + 2.0**-8]))[0] == 1.0
+    assert moe.round_bf16(np.array([1 + 3 * 2.0**-8]))[0] == 1 + 2.0**-6
+    # just above a tie rounds up (fp64 input, no intermediate fp32 rounding)
+    assert moe.round_bf16(np.array([1 + 2.0**-8 + 2.0**-40]))[0] == 1 + 2.0**-7
+    assert moe.round_bf16(np.array([-1.5, 0.0]))[1] == 0.0
+
+
+def test_stack_forward_matches_explicit_chain():
+    # two layers written out by hand from the primitives, forced and routed ids
+    H, I, E, k, T = 64, 32, 8, 2, 5
+    ex = [_tiny_experts(H, I, E, F.BF16, seed=11, layer=l) for l in range(2)]
+    R = [synth.router_weights(11, l, E, H) for l in range(2)]
+    X0 = synth.bf16_bits_to_f32(synth.activations(11, 0, T, H, 3.0, True)).astype(np.float64)
+    forced = np.array([[1, 4]] * T, dtype=np.int32)
+    rL, tr = moe.stack_forward(X0, [(R[0], k, ex[0], None, None), (R[1], k, ex[1], None, forced)],
+                               True)
+    u0 = moe.round_bf16(X0 / np.sqrt(np.mean(X0 ** 2, axis=1, keepdims=True) + 1e-6))
+    assert np.array_equal(tr[0][0], u0)
+    ids0, w0, _ = router.route(u0.astype(np.float32), R[0], k)
+    assert np.array_equal(tr[0][1], ids0)
+    r1 = moe.round_bf16(X0 + moe.layer_output(u0, ids0, w0, ex[0]))
+    u1 = moe.round_bf16(r1 / np.sqrt(np.mean(r1 ** 2, axis=1, keepdims=True) + 1e-6))
+    assert np.array_equal(tr[1][0], u1) and np.array_equal(tr[1][1], forced)
+    _, w1, _ = router.route(u1.astype(np.float32), R[1], k, forced)
+    assert np.array_equal(rL, moe.round_bf16(r1 + moe.layer_output(u1, forced, w1, ex[1])))
+    # every stored value is a bf16 value; the inputs are normalised
+    assert np.array_equal(moe.round_bf16(rL), rL)
+    assert np.allclose(np.mean(tr[1][0] ** 2, axis=1), 1.0, rtol=1e-2)

@@ -16,7 +16,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libeo.so")
 
 HIP_SOURCES = ["engine.hip", "k_router.hip", "k_plan.hip", "k_permute.hip", "k_gemm.hip",
-               "k_gemv.hip", "k_dequant.hip"]
+               "k_gemv.hip", "k_dequant.hip", "k_fill.hip"]
 HOST_SOURCES = ["host_ffn.cpp", "layout.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -65,7 +65,9 @@ struct eo_engine {
     int64_t C = 0;
     int act_size = 4;
 
-    std::vector<uint8_t*> pool;  // per layer, E * S_pad pinned bytes
+    std::vector<uint8_t*> pool;      // per layer, E * S_pad pinned bytes
+    std::vector<uint8_t*> pool_dev;  // the same, as device-visible addresses
+    bool fill_sdma = false;          // EO_FILL_SDMA=1: fills by hipMemcpyAsync (ablation)
     uint8_t* d_slots = nullptr;
     uint8_t* d_shared = nullptr;
     float* d_router = nullptr;
@@ -90,10 +92,13 @@ struct eo_engine {
     float* d_z = nullptr;
     float* d_y = nullptr;
     void* d_u = nullptr;  // [max_tokens, H] layer input (RMS-normalised residual)
+    uint16_t* d_r = nullptr;  // [2, H] residual stream of the one-token decode step
+    bool fused_entry = true;  // EO_FUSED_ENTRY=0: separate norm / router / top-k kernels
     float* d_hgemv = nullptr;
     float* d_yparts = nullptr;
     float* d_yhost = nullptr;
-    float* h_yhost = nullptr;
+    float* h_yhost = nullptr;      // mapped, coherent
+    float* h_yhost_dev = nullptr;
     std::vector<float> xf;  // host fp32 copy of x for the host routine
     std::vector<float> host_scratch;
 
@@ -245,17 +250,19 @@ eo_status wait_plan(eo_engine* e) {
     e->stats.lookups += 1;
     e->stats.hits += p.n_hit;
     e->stats.misses += p.m;
+    e->stats.fills += p.q_fill;
+    e->stats.pcie_bytes += (int64_t)p.q_fill * (int64_t)e->S;
     e->plan_ready = true;
     return EO_OK;
 }
 
 eo_status do_plan(eo_engine* e, int layer, const int32_t* ids, const float* w, const void* x,
-                  int T, hipStream_t s) {
+                  int T, hipStream_t s, PlanRoute rt = PlanRoute{nullptr, nullptr, nullptr, nullptr}) {
     const size_t xb = (size_t)T * e->H * e->act_size;
     hipError_t he = launch_plan(layer, ids, w ? w : nullptr, x, xb, T, e->k, e->E, e->C,
                                 e->d_slot_key, e->d_slot_stamp, e->d_key2slot, e->d_state,
                                 e->d_plan, e->h_plan_dev, w ? e->h_ids_dev : nullptr,
-                                w ? e->h_w_dev : nullptr, x ? e->h_x_dev : nullptr, s);
+                                w ? e->h_w_dev : nullptr, x ? e->h_x_dev : nullptr, s, rt);
     if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("plan launch: ") + hipGetErrorString(he));
     e->plan_seq += 1;
     e->plan_pending = true;
@@ -267,7 +274,17 @@ eo_status do_plan(eo_engine* e, int layer, const int32_t* ids, const float* w, c
     return EO_OK;
 }
 
+// Fills of the pending plan, queued on s behind the plan kernel: the fill kernel
+// reads the fill list from device memory, so nothing waits for the host.
 eo_status do_fill(eo_engine* e, hipStream_t s) {
+    if (!e->plan_pending) return fail(EO_ERR_STATE, "no pending plan (call eo_lookup_plan first)");
+    if (e->C == 0) return EO_OK;
+    if (!e->fill_sdma) {
+        hipError_t he = launch_fill(e->d_plan, e->pool_dev[e->plan_layer], e->d_slots, e->S,
+                                    e->S_pad, s);
+        if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("fill: ") + hipGetErrorString(he));
+        return EO_OK;
+    }
     EOCHK(wait_plan(e));
     const eo_plan_host& p = e->last_plan;
     if (p.q_fill == 0) return EO_OK;
@@ -279,8 +296,6 @@ eo_status do_fill(eo_engine* e, hipStream_t s) {
     }
     HIPCHK(hipEventRecord(e->ev_fill, e->copy_stream));
     HIPCHK(hipStreamWaitEvent(s, e->ev_fill, 0));
-    e->stats.fills += p.q_fill;
-    e->stats.pcie_bytes += (int64_t)p.q_fill * (int64_t)e->S;
     return EO_OK;
 }
 
@@ -327,12 +342,15 @@ eo_status do_host(eo_engine* e, const void* x, const int32_t* ids, const float* 
     jb.T = T;
     jb.k = k;
     jb.x = e->xf.data();
+    jb.xb = e->act_bf16 ? (const uint16_t*)hx : nullptr;
     jb.ids = hids;
     jb.w = hw;
     jb.experts = table.data();
     jb.y = e->h_yhost;
     host_ffn(e->tp, jb, e->host_scratch);
-    HIPCHK(hipMemcpyAsync(e->d_yhost, e->h_yhost, sizeof(float) * T * H, hipMemcpyHostToDevice, s));
+    // one token: the combine reads the mapped host result directly
+    if (T > 1)
+        HIPCHK(hipMemcpyAsync(e->d_yhost, e->h_yhost, sizeof(float) * T * H, hipMemcpyHostToDevice, s));
     e->host_staged = true;
     e->stats.host_experts += p.n_host;
     e->stats.host_bytes += (int64_t)p.n_host * (int64_t)e->S;
@@ -399,7 +417,7 @@ eo_status do_ffn_device(eo_engine* e, int layer, const void* x, const int32_t* i
 
 eo_status do_combine(eo_engine* e, const int32_t* ids, float* y, void* x_res, hipStream_t s) {
     const int T = e->plan_T;
-    const float* yh = e->host_staged ? e->d_yhost : nullptr;
+    const float* yh = e->host_staged ? (T == 1 ? e->h_yhost_dev : e->d_yhost) : nullptr;
     hipError_t he;
     if (T == 1)
         he = launch_gemv_reduce(e->d_yparts, e->k + e->shared, yh, e->H, y, x_res, e->act_bf16, s);
@@ -426,6 +444,58 @@ eo_status moe_layer_impl(eo_engine* e, int layer, const void* x, float* y, int T
     EOCHK(do_ffn_device(e, layer, x, ids, w, s));
     EOCHK(do_host(e, x, ids, w, s));
     return do_combine(e, ids, y, x_res, s);
+}
+
+// One token through all layers with the fused layer entry: per layer, one
+// kernel applies the previous layer's result to the residual stream,
+// normalises and computes the logits; the plan kernel selects the experts,
+// then fill, GEMV and host execution as in moe_layer_impl. The previous
+// layer's partial outputs are summed by the next entry (the last layer's by a
+// final reduce into x_inout). The stream ping-pongs between two rows of d_r.
+eo_status decode_one_token(eo_engine* e, uint16_t* x_inout, const int32_t* forced_ids,
+                           hipStream_t s) {
+    const int H = e->H, k = e->k, nparts = e->k + e->shared;
+    const bool cap = e->cap_y && 1 <= e->cap_T;
+    const float* prev_host = nullptr;
+    for (int l = 0; l < e->L; ++l) {
+        int32_t* ids = e->d_ids;
+        float* w = e->d_w;
+        EntryArgs a;
+        a.r_in = l == 0 ? x_inout : e->d_r + (size_t)((l - 1) & 1) * H;
+        a.r_out = e->d_r + (size_t)(l & 1) * H;
+        a.parts = l > 0 ? e->d_yparts : nullptr;
+        a.nparts = l > 0 ? nparts : 0;
+        a.y_host = prev_host;
+        a.y_out = (cap && l > 0) ? e->cap_y + (size_t)(l - 1) * e->cap_T * H : nullptr;
+        a.u = (uint16_t*)e->d_u;
+        a.Rt = e->d_router_t + (size_t)l * e->E * H;
+        a.z = e->d_z;
+        a.E = e->E;
+        a.H = H;
+        hipError_t he = launch_entry(a, s);
+        if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("layer entry: ") + hipGetErrorString(he));
+        if (cap) {
+            HIPCHK(hipMemcpyAsync((uint8_t*)e->cap_x + (size_t)l * e->cap_T * H * 2, e->d_u,
+                                  (size_t)H * 2, hipMemcpyDeviceToDevice, s));
+            ids = e->cap_ids + (size_t)l * e->cap_T * k;
+            w = e->cap_w + (size_t)l * e->cap_T * k;
+        }
+        PlanRoute rt{e->d_z, forced_ids ? forced_ids + (size_t)l * k : nullptr, ids, w};
+        EOCHK(do_plan(e, l, ids, w, e->d_u, 1, s, rt));
+        EOCHK(do_fill(e, s));
+        EOCHK(do_ffn_device(e, l, e->d_u, ids, w, s));
+        EOCHK(do_host(e, e->d_u, ids, w, s));
+        prev_host = e->host_staged ? e->h_yhost_dev : nullptr;
+        // the plan is consumed here; its outputs are summed by the next entry
+        e->plan_pending = false;
+        e->plan_ready = false;
+        e->host_staged = false;
+    }
+    float* y_last = cap ? e->cap_y + (size_t)(e->L - 1) * e->cap_T * H : nullptr;
+    hipError_t he = launch_gemv_reduce(e->d_yparts, nparts, prev_host, H, y_last, x_inout, 1, s,
+                                       e->d_r + (size_t)((e->L - 1) & 1) * H);
+    if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("combine: ") + hipGetErrorString(he));
+    return EO_OK;
 }
 
 eo_status reset_cache(eo_engine* e) {
@@ -457,7 +527,7 @@ void destroy_all(eo_engine* e) {
     fr(e->d_slots); fr(e->d_shared); fr(e->d_router); fr(e->d_router_t); fr(e->d_xt);
     fr(e->d_slot_key); fr(e->d_slot_stamp);
     fr(e->d_key2slot); fr(e->d_state); fr(e->d_plan); fr(e->d_ids); fr(e->d_w); fr(e->d_z);
-    fr(e->d_y); fr(e->d_u); fr(e->d_hgemv); fr(e->d_yparts); fr(e->d_yhost);
+    fr(e->d_y); fr(e->d_u); fr(e->d_r); fr(e->d_hgemv); fr(e->d_yparts); fr(e->d_yhost);
     fr(e->pb.counts); fr(e->pb.offsets); fr(e->pb.tile_off); fr(e->pb.perm_pair);
     fr(e->pb.chunk_cnt); fr(e->pb.x_perm); fr(e->d_hbuf); fr(e->d_opairs);
     fr(e->d_staging[0]); fr(e->d_staging[1]);
@@ -516,7 +586,11 @@ eo_status create_impl(const eo_config* cfg, eo_engine* e) {
     HIPCHK(hipSetDevice(cfg->device));
 
     e->pool.assign(e->L, nullptr);
-    for (int l = 0; l < e->L; ++l) EOCHK(hmalloc(&e->pool[l], e->E * e->S_pad, hipHostMallocDefault));
+    e->pool_dev.assign(e->L, nullptr);
+    for (int l = 0; l < e->L; ++l) {
+        EOCHK(hmalloc(&e->pool[l], e->E * e->S_pad, hipHostMallocDefault));
+        HIPCHK(hipHostGetDevicePointer((void**)&e->pool_dev[l], e->pool[l], 0));
+    }
     EOCHK(dmalloc(&e->d_slots, e->C * e->S_pad));
     if (e->shared) {
         EOCHK(dmalloc(&e->d_shared, (size_t)e->L * e->S_pad));
@@ -551,10 +625,12 @@ eo_status create_impl(const eo_config* cfg, eo_engine* e) {
     EOCHK(dmalloc(&e->d_z, sizeof(float) * Tm * e->E));
     EOCHK(dmalloc(&e->d_y, sizeof(float) * Tm * e->H));
     EOCHK(dmalloc(&e->d_u, (size_t)e->act_size * Tm * e->H));
+    EOCHK(dmalloc(&e->d_r, sizeof(uint16_t) * 2 * e->H));
     EOCHK(dmalloc(&e->d_hgemv, sizeof(float) * (e->k + 1) * e->I));
     EOCHK(dmalloc(&e->d_yparts, sizeof(float) * (e->k + 1) * e->H));
     EOCHK(dmalloc(&e->d_yhost, sizeof(float) * Tm * e->H));
-    EOCHK(hmalloc(&e->h_yhost, sizeof(float) * Tm * e->H, hipHostMallocDefault));
+    EOCHK(hmalloc(&e->h_yhost, sizeof(float) * Tm * e->H, mflags));
+    HIPCHK(hipHostGetDevicePointer((void**)&e->h_yhost_dev, e->h_yhost, 0));
     HIPCHK(hipStreamCreateWithFlags(&e->copy_stream, hipStreamNonBlocking));
     HIPCHK(hipEventCreateWithFlags(&e->ev_fill, hipEventDisableTiming));
     HIPCHK(hipEventCreateWithFlags(&e->ev_start, hipEventDisableTiming));
@@ -567,6 +643,8 @@ eo_status create_impl(const eo_config* cfg, eo_engine* e) {
     if (nt <= 0) nt = std::max(1, std::min(15, (int)std::thread::hardware_concurrency() - 1));
     e->tp = threadpool_create(nt);
     if (const char* v = std::getenv("EO_GEMV_FAST")) e->gemv_fast = std::atoi(v) != 0;
+    if (const char* v = std::getenv("EO_FILL_SDMA")) e->fill_sdma = std::atoi(v) != 0;
+    if (const char* v = std::getenv("EO_FUSED_ENTRY")) e->fused_entry = std::atoi(v) != 0;
     e->bp = e->bh = 1;
     EOCHK(reset_cache(e));
     HIPCHK(hipDeviceSynchronize());
@@ -708,7 +786,9 @@ eo_status eo_measure_bandwidth(eo_engine* e, uint32_t* bp_out, uint32_t* bh_out)
     (void)hipEventDestroy(b);
     if (tmp) (void)hipFree(tmp);
     // host routine over one expert at T = 1
-    std::vector<float> x(e->H, 0.01f), y(e->H);
+    // x = 0.01 (as stored in the activation dtype: bf16 0x3C24 = 0.010009765625)
+    std::vector<float> x(e->H, e->act_bf16 ? 0.010009765625f : 0.01f), y(e->H);
+    std::vector<uint16_t> xb(e->H, 0x3C24);
     std::vector<const uint8_t*> table(e->E, nullptr);
     int32_t ids[kMaxK];
     float w[kMaxK];
@@ -732,6 +812,7 @@ eo_status eo_measure_bandwidth(eo_engine* e, uint32_t* bp_out, uint32_t* bh_out)
         jb.T = 1;
         jb.k = e->k;
         jb.x = x.data();
+        jb.xb = e->act_bf16 ? xb.data() : nullptr;
         jb.ids = ids;
         jb.w = w;
         jb.experts = table.data();
@@ -816,6 +897,11 @@ eo_status eo_decode_step(eo_engine* e, void* x_inout, int32_t T, const int32_t* 
     EOCHK(check_T(e, T));
     if (!aligned16(x_inout)) return fail(EO_ERR_INVALID_ARG, "x must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
+    if (T == 1 && e->fused_entry && entry_ok(e->E, e->H, e->act_bf16)) {
+        EOCHK(decode_one_token(e, (uint16_t*)x_inout, forced_ids, s));
+        if (e->timing) EOCHK(harvest_times(e));
+        return EO_OK;
+    }
     const size_t xb = (size_t)T * e->H * e->act_size;
     const bool cap = e->cap_y && T <= e->cap_T;
     for (int l = 0; l < e->L; ++l) {

@@ -28,12 +28,16 @@ struct HostJob {
     Layout lay;
     int H, I, T, k;
     const float* x;                 // [T,H] fp32
+    const uint16_t* xb = nullptr;   // [T,H] the same values as bf16 bits, when they are bf16
     const int32_t* ids;             // [T,k]
     const float* w;                 // [T,k]
     const uint8_t* const* experts;  // pool block per expert id (null: not host-executed)
     float* y;                       // [T,H] accumulated (zeroed by the caller)
 };
 void host_ffn(ThreadPool* pool, const HostJob& job, std::vector<float>& scratch);
+// True when host_ffn takes the AVX512_BF16 route for bf16 experts (CPU support,
+// unless the environment sets EO_HOST_ISA=avx2).
+bool host_ffn_uses_avx512bf16();
 ThreadPool* threadpool_create(int n);
 void threadpool_destroy(ThreadPool* p);
 int threadpool_size(ThreadPool* p);

@@ -43,12 +43,49 @@ hipError_t launch_route(const void* x, int act_bf16, const float* R, const float
                         int E, int H, int k, const int32_t* forced, int32_t* ids, float* w,
                         float* z_scratch, uint16_t* xT, hipStream_t s);
 
+// Layer entry of one token in the stacked decode step (bf16 activations):
+// r_out = bf16(r_in + sum_j parts[j] + y_host) (r_in copied when there are no
+// parts), u = bf16(r_out / sqrt(mean(r_out^2) + 1e-6)), z[e] = router logit of
+// u in the fixed chain order from the per-chain router Rt [E][64][H/64].
+// y_out (optional) receives the summed parts. r_out must not alias r_in when
+// parts are given. Needs entry_ok(E, H, act_bf16).
+struct EntryArgs {
+    const uint16_t* r_in;
+    uint16_t* r_out;
+    const float* parts;  // [nparts][H] or null
+    int nparts;
+    const float* y_host;  // [H] or null (device-visible)
+    float* y_out;         // [H] or null
+    uint16_t* u;          // [H]
+    const float* Rt;
+    float* z;  // [E]
+    int E, H;
+};
+bool entry_ok(int E, int H, int act_bf16);
+hipError_t launch_entry(const EntryArgs& a, hipStream_t s);
+
 // Lookup + LRU + miss plan, single workgroup; writes plan to d_plan and a
 // mirror (header, lists, ids, w and, when x_mirror != null, x) to host memory.
+// With rt.z (one token only), the kernel first selects the token's experts
+// from the logits z [E] (forced ids if given) and writes them to rt.ids_out /
+// rt.w_out; ids and w are then ignored.
+struct PlanRoute {
+    const float* z;
+    const int32_t* forced;
+    int32_t* ids_out;
+    float* w_out;
+};
 hipError_t launch_plan(int layer, const int32_t* ids, const float* w, const void* x,
                        size_t x_bytes, int T, int k, int E, int64_t C, int32_t* slot_key,
                        int64_t* slot_stamp, int32_t* key2slot, DevState* st, DevPlan* d_plan,
-                       DevPlan* h_plan, int32_t* h_ids, float* h_w, void* h_x, hipStream_t s);
+                       DevPlan* h_plan, int32_t* h_ids, float* h_w, void* h_x, hipStream_t s,
+                       PlanRoute rt = PlanRoute{nullptr, nullptr, nullptr, nullptr});
+
+// Fill: copy the plan's q_fill experts from the layer's pool (device-visible
+// pointer to pinned host memory, E * S_pad bytes) into their slots. Reads the
+// fill list from d_plan; no host synchronisation.
+hipError_t launch_fill(const DevPlan* plan, const uint8_t* pool_layer_dev, uint8_t* slots,
+                       uint64_t S, uint64_t S_pad, hipStream_t s);
 
 // Permute: group the (token, k) pairs whose expert is resident by expert,
 // stable in pair order; the shared expert (when present) is group E holding
@@ -100,9 +137,11 @@ hipError_t launch_ffn_gemv(int fmt, const Layout& lay, GroupW gw, const DevPlan*
                            float* y_parts, hipStream_t s,
                            hipEvent_t* ev /*[4]: start/stop of each kernel, entries may be null*/,
                            int allow_fast, const GemvExperts* ex /*may be null*/);
-// Sum of the GEMV partials (k + shared rows of [H]) plus host results.
+// Sum of the GEMV partials (k + shared rows of [H]) plus host results; with
+// x_res, x_res = act(x_in + y) (x_in null: in place).
 hipError_t launch_gemv_reduce(const float* y_parts, int nparts, const float* y_host, int H,
-                              float* y, void* x_res, int act_bf16, hipStream_t s);
+                              float* y, void* x_res, int act_bf16, hipStream_t s,
+                              const void* x_in = nullptr);
 
 // Residual add: x = act(x + y), T*H elements.
 hipError_t launch_residual(void* x, const float* y, int64_t n, int act_bf16, hipStream_t s);

@@ -14,6 +14,7 @@
 #include <atomic>
 #include <cmath>
 #include <condition_variable>
+#include <cstdlib>
 #include <cstring>
 #include <functional>
 #include <mutex>
@@ -222,7 +223,61 @@ float dot_bf16(const uint16_t* w, const float* x, int K) {
     return s;
 }
 
+// ---------------------------------------------------------- AVX-512 BF16
+// bf16 weights against bf16 activations with the bf16 pair dot product
+// (vdpbf16ps: 32 products per instruction, fp32 accumulation). Used when the
+// CPU has AVX512_BF16; the SwiGLU output h is rounded to bf16 (nearest even)
+// before the down projection, as on the device.
+#define EO_AVX512BF16 __attribute__((target("avx512f,avx512bw,avx512vl,avx512bf16")))
+
+EO_AVX512BF16 inline __m512bh as_bh(__m512i v) { return (__m512bh)v; }
+
+// Two rows of K (K % 128 == 0) against one vector.
+EO_AVX512BF16 void dot2_bf16_avx512(const uint16_t* a, const uint16_t* b, const uint16_t* x,
+                                    int K, float* ra, float* rb) {
+    __m512 a0 = _mm512_setzero_ps(), a1 = _mm512_setzero_ps();
+    __m512 b0 = _mm512_setzero_ps(), b1 = _mm512_setzero_ps();
+    for (int i = 0; i < K; i += 64) {
+        __m512i x0 = _mm512_loadu_si512(x + i), x1 = _mm512_loadu_si512(x + i + 32);
+        a0 = _mm512_dpbf16_ps(a0, as_bh(_mm512_loadu_si512(a + i)), as_bh(x0));
+        a1 = _mm512_dpbf16_ps(a1, as_bh(_mm512_loadu_si512(a + i + 32)), as_bh(x1));
+        b0 = _mm512_dpbf16_ps(b0, as_bh(_mm512_loadu_si512(b + i)), as_bh(x0));
+        b1 = _mm512_dpbf16_ps(b1, as_bh(_mm512_loadu_si512(b + i + 32)), as_bh(x1));
+    }
+    *ra = _mm512_reduce_add_ps(_mm512_add_ps(a0, a1));
+    *rb = _mm512_reduce_add_ps(_mm512_add_ps(b0, b1));
+}
+
+// One row of K (K % 64 == 0) against one vector.
+EO_AVX512BF16 float dot_bf16_avx512(const uint16_t* a, const uint16_t* x, int K) {
+    __m512 a0 = _mm512_setzero_ps(), a1 = _mm512_setzero_ps();
+    for (int i = 0; i < K; i += 64) {
+        a0 = _mm512_dpbf16_ps(a0, as_bh(_mm512_loadu_si512(a + i)), as_bh(_mm512_loadu_si512(x + i)));
+        a1 = _mm512_dpbf16_ps(a1, as_bh(_mm512_loadu_si512(a + i + 32)),
+                              as_bh(_mm512_loadu_si512(x + i + 32)));
+    }
+    return _mm512_reduce_add_ps(_mm512_add_ps(a0, a1));
+}
+
+uint16_t bf16_rne(float f) {
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+bool cpu_has_avx512bf16() {
+    static const bool ok = [] {
+        if (const char* v = std::getenv("EO_HOST_ISA"))
+            if (!std::strcmp(v, "avx2")) return false;
+        return __builtin_cpu_supports("avx512bf16") != 0;
+    }();
+    return ok;
+}
+
 }  // namespace
+
+bool host_ffn_uses_avx512bf16() { return cpu_has_avx512bf16(); }
 
 void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) {
     const int H = jb.H, I = jb.I, T = jb.T, k = jb.k;
@@ -261,6 +316,41 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
 
     constexpr int RB = 16;
     const int nb1 = (I + RB - 1) / RB;
+    if (fmt == EO_W_BF16 && jb.xb && H % 128 == 0 && I % 64 == 0 && cpu_has_avx512bf16()) {
+        // h as bf16 [ne][tokens][I], in the caller's scratch
+        if (scratch.size() < (hoff[ne] + 1) / 2) scratch.resize((hoff[ne] + 1) / 2);
+        uint16_t* hb = (uint16_t*)scratch.data();
+        pool->run(ne * nb1, [&](int task) {
+            const int ei = task / nb1, rb = task % nb1;
+            const uint16_t* W = (const uint16_t*)(jb.experts[exps[ei]] + lay.d13);
+            for (int r = rb * RB; r < std::min(I, rb * RB + RB); ++r)
+                for (size_t ti = 0; ti < toks[ei].size(); ++ti) {
+                    float g, u;
+                    dot2_bf16_avx512(W + (size_t)r * H, W + (size_t)(I + r) * H,
+                                     jb.xb + (size_t)toks[ei][ti] * H, H, &g, &u);
+                    hb[hoff[ei] + ti * I + r] = bf16_rne(g / (1.0f + std::exp(-g)) * u);
+                }
+        });
+        const int nb2 = (H + RB - 1) / RB;
+        pool->run(nb2, [&](int task) {
+            for (int o = task * RB; o < std::min(H, task * RB + RB); ++o)
+                for (int t = 0; t < T; ++t) {
+                    float acc = 0.0f;
+                    for (int j = 0; j < k; ++j) {
+                        int e = jb.ids[t * k + j];
+                        if (e < 0 || e >= EO_MAX_EXPERTS || !jb.experts[e]) continue;
+                        int ei = slot_of[e];
+                        const std::vector<int>& tl = toks[ei];
+                        int ti = (int)(std::lower_bound(tl.begin(), tl.end(), t) - tl.begin());
+                        const uint16_t* W2 = (const uint16_t*)(jb.experts[e] + lay.d2);
+                        acc += jb.w[t * k + j] *
+                               dot_bf16_avx512(W2 + (size_t)o * I, hb + hoff[ei] + ti * I, I);
+                    }
+                    jb.y[(size_t)t * H + o] += acc;
+                }
+        });
+        return;
+    }
     pool->run(ne * nb1, [&](int task) {
         const int ei = task / nb1, rb = task % nb1;
         const uint8_t* b = jb.experts[exps[ei]];

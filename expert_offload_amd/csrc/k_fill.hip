@@ -1,0 +1,58 @@
+// Cache fill: copy the planned experts from the pinned host pool into their
+// device slots with a kernel that reads the pool over PCIe (zero-copy).
+//
+// zhichai.net article, section 2, Decode paragraph: q* of a step's misses are
+// brought over PCIe into the device cache. The plan (fill list and slots) is
+// read from device memory, so the copy is queued behind the plan kernel on the
+// same stream with no round trip through the host; 64 workgroups already keep
+// enough 16-byte reads in flight to saturate the link, leaving the other CUs
+// free.
+#include "eo_internal.h"
+
+namespace eo {
+
+namespace {
+
+constexpr int kFillBlocks = 64;
+constexpr int kFillUnroll = 4;
+
+__global__ __launch_bounds__(256) void k_fill(const DevPlan* __restrict__ plan,
+                                              const uint8_t* __restrict__ pool,
+                                              uint8_t* __restrict__ slots, uint64_t S,
+                                              uint64_t S_pad) {
+    if (plan->pad != 0) return;  // rejected lookup: nothing to fill
+    const int q = plan->q_fill;
+    const uint64_t n16 = S / 16;
+    const uint64_t step = (uint64_t)gridDim.x * 256 * kFillUnroll;
+    for (int r = 0; r < q; ++r) {
+        const uint4* src = (const uint4*)(pool + (uint64_t)plan->fill_e[r] * S_pad);
+        uint4* dst = (uint4*)(slots + (uint64_t)plan->fill_slot[r] * S_pad);
+        for (uint64_t b = (uint64_t)blockIdx.x * 256 * kFillUnroll + threadIdx.x; b < n16;
+             b += step) {
+            uint4 v[kFillUnroll];
+#pragma unroll
+            for (int u = 0; u < kFillUnroll; ++u) {
+                const uint64_t i = b + (uint64_t)u * 256;
+                if (i < n16) v[u] = src[i];
+            }
+#pragma unroll
+            for (int u = 0; u < kFillUnroll; ++u) {
+                const uint64_t i = b + (uint64_t)u * 256;
+                if (i < n16) dst[i] = v[u];
+            }
+        }
+        const uint64_t tail = S - n16 * 16;
+        if (blockIdx.x == 0 && threadIdx.x < tail)
+            ((uint8_t*)dst)[n16 * 16 + threadIdx.x] = ((const uint8_t*)src)[n16 * 16 + threadIdx.x];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_fill(const DevPlan* plan, const uint8_t* pool_layer_dev, uint8_t* slots,
+                       uint64_t S, uint64_t S_pad, hipStream_t s) {
+    k_fill<<<kFillBlocks, 256, 0, s>>>(plan, pool_layer_dev, slots, S, S_pad);
+    return hipGetLastError();
+}
+
+}  // namespace eo

@@ -235,7 +235,8 @@ __global__ __launch_bounds__(256) void k_gemv_down(GemvArgs a) {
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ yp, int nparts,
                                                      const float* __restrict__ y_host, int H,
-                                                     float* __restrict__ y, void* __restrict__ x_res) {
+                                                     float* __restrict__ y, const void* x_in,
+                                                     void* x_res) {
     int o = blockIdx.x * blockDim.x + threadIdx.x;
     if (o >= H) return;
     float s = 0.0f;
@@ -244,11 +245,11 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ y
     if (y) y[o] = s;
     if (x_res) {
         if (BF16) {
-            uint16_t* xp = (uint16_t*)x_res;
-            xp[o] = (uint16_t)f32_bf16_rne(bf16_f32(xp[o]) + s);
+            const uint16_t* xi = (const uint16_t*)x_in;
+            ((uint16_t*)x_res)[o] = (uint16_t)f32_bf16_rne(bf16_f32(xi[o]) + s);
         } else {
-            float* xp = (float*)x_res;
-            xp[o] = xp[o] + s;
+            const float* xi = (const float*)x_in;
+            ((float*)x_res)[o] = xi[o] + s;
         }
     }
 }
@@ -557,11 +558,15 @@ hipError_t launch_ffn_gemv(int fmt, const Layout& lay, GroupW gw, const DevPlan*
 }
 
 hipError_t launch_gemv_reduce(const float* y_parts, int nparts, const float* y_host, int H,
-                              float* y, void* x_res, int act_bf16, hipStream_t s) {
+                              float* y, void* x_res, int act_bf16, hipStream_t s,
+                              const void* x_in) {
+    if (!x_in) x_in = x_res;
     if (act_bf16)
-        k_gemv_reduce<true><<<(H + 255) / 256, 256, 0, s>>>(y_parts, nparts, y_host, H, y, x_res);
+        k_gemv_reduce<true><<<(H + 255) / 256, 256, 0, s>>>(y_parts, nparts, y_host, H, y, x_in,
+                                                            x_res);
     else
-        k_gemv_reduce<false><<<(H + 255) / 256, 256, 0, s>>>(y_parts, nparts, y_host, H, y, x_res);
+        k_gemv_reduce<false><<<(H + 255) / 256, 256, 0, s>>>(y_parts, nparts, y_host, H, y, x_in,
+                                                             x_res);
     return hipGetLastError();
 }
 

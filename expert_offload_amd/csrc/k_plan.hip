@@ -17,6 +17,7 @@
 // touched by one thread only.
 #include "dev_common.h"
 #include "eo_internal.h"
+#include "route_dev.h"
 
 namespace eo {
 
@@ -85,12 +86,12 @@ __device__ uint64_t block_min_u64(uint64_t v, uint64_t* red) {
 }
 
 __global__ __launch_bounds__(kThreads) void k_plan(
-    int layer, const int32_t* __restrict__ ids, const float* __restrict__ w,
-    const uint8_t* __restrict__ x, int x_bytes, int T, int k, int E, int C,
-    int32_t* __restrict__ g_slot_key, int64_t* __restrict__ g_slot_stamp,
-    int32_t* __restrict__ key2slot, DevState* __restrict__ st, DevPlan* __restrict__ dp,
-    DevPlan* __restrict__ hp, int32_t* __restrict__ h_ids, float* __restrict__ h_w,
-    uint8_t* __restrict__ h_x) {
+    int layer, const int32_t* ids, const float* w, const uint8_t* __restrict__ x, int x_bytes,
+    int T, int k, int E, int C, int32_t* __restrict__ g_slot_key,
+    int64_t* __restrict__ g_slot_stamp, int32_t* __restrict__ key2slot,
+    DevState* __restrict__ st, DevPlan* __restrict__ dp, DevPlan* __restrict__ hp,
+    int32_t* __restrict__ h_ids, float* __restrict__ h_w, uint8_t* __restrict__ h_x,
+    PlanRoute rt) {
     extern __shared__ int64_t smem64[];
     int64_t* s_stamp = smem64;                    // [C]
     int32_t* s_key = (int32_t*)(smem64 + C);      // [C]
@@ -104,7 +105,22 @@ __global__ __launch_bounds__(kThreads) void k_plan(
     __shared__ int s_m, s_h, s_q, s_qfill;
     __shared__ int fill_e[kMaxE];
 
+    __shared__ int32_t s_ids[kMaxK];
+    __shared__ float s_w[kMaxK];
+
     const int tid = threadIdx.x;
+    if (rt.z) {
+        // one token: select its experts here from the logits (first wavefront)
+        if (tid < 64)
+            topk_token(rt.z, E, k, rt.forced, s_ids, s_w);
+        __syncthreads();
+        if (tid < k) {
+            rt.ids_out[tid] = s_ids[tid];
+            rt.w_out[tid] = s_w[tid];
+        }
+        ids = s_ids;
+        w = s_w;
+    }
     for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
     if (tid == 0) s_err = 0;
     for (int s = tid; s < C; s += kThreads) {
@@ -320,7 +336,9 @@ int plan_max_slots() { return kMaxSlotsLds; }
 hipError_t launch_plan(int layer, const int32_t* ids, const float* w, const void* x,
                        size_t x_bytes, int T, int k, int E, int64_t C, int32_t* slot_key,
                        int64_t* slot_stamp, int32_t* key2slot, DevState* st, DevPlan* d_plan,
-                       DevPlan* h_plan, int32_t* h_ids, float* h_w, void* h_x, hipStream_t s) {
+                       DevPlan* h_plan, int32_t* h_ids, float* h_w, void* h_x, hipStream_t s,
+                       PlanRoute rt) {
+    if (rt.z && T != 1) return hipErrorInvalidValue;
     static bool attr_set = false;
     size_t lds = 12 * (size_t)C;
     if (!attr_set) {
@@ -332,7 +350,7 @@ hipError_t launch_plan(int layer, const int32_t* ids, const float* w, const void
     }
     k_plan<<<1, kThreads, lds, s>>>(layer, ids, w, (const uint8_t*)x, (int)x_bytes, T, k, E,
                                     (int)C, slot_key, slot_stamp, key2slot, st, d_plan, h_plan,
-                                    h_ids, h_w, (uint8_t*)h_x);
+                                    h_ids, h_w, (uint8_t*)h_x, rt);
     return hipGetLastError();
 }
 

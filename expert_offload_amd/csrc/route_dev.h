@@ -1,0 +1,82 @@
+// Top-k selection and softmax weights of one token, by one wavefront.
+//
+// Shared by the router's top-k kernel and the plan kernel (which selects the
+// experts itself when it is handed logits). Selection is k rounds of
+// (max z, then smallest id); the weights are the softmax over the k selected
+// logits. With forced ids the given ids are taken in their order and the
+// softmax is taken over the logits at them.
+#pragma once
+
+#include "dev_common.h"
+#include "eo_host.h"
+
+namespace eo {
+
+__device__ __forceinline__ bool topk_better(float za, int ia, float zb, int ib) {
+    return za > zb || (za == zb && ia < ib);
+}
+
+// All 64 lanes of the wavefront call this; lane 0 writes ids[0..k) and w[0..k).
+__device__ __forceinline__ void topk_token(const float* __restrict__ zt, int E, int k,
+                                           const int32_t* __restrict__ forced_t,
+                                           int32_t* __restrict__ ids_t, float* __restrict__ w_t) {
+    const int lane = threadIdx.x & 63;
+    float zs[kMaxK];
+    int is[kMaxK];
+    if (forced_t) {
+        for (int j = 0; j < k; ++j) {
+            is[j] = forced_t[j];
+            // out-of-range ids are reported by the lookup; read in bounds here
+            zs[j] = zt[min(max(is[j], 0), E - 1)];
+        }
+    } else {
+        constexpr int kPer = kMaxE / 64;
+        float zl[kPer];
+        uint32_t taken = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            int e = lane + 64 * i;
+            zl[i] = e < E ? zt[e] : -INFINITY;
+        }
+        for (int j = 0; j < k; ++j) {
+            float bz = -INFINITY;
+            int bi = 0x7FFFFFFF;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                int e = lane + 64 * i;
+                if (e < E && !((taken >> i) & 1u) &&
+                    (bi == 0x7FFFFFFF || topk_better(zl[i], e, bz, bi))) {
+                    bz = zl[i];
+                    bi = e;
+                }
+            }
+#pragma unroll
+            for (int s = 32; s >= 1; s >>= 1) {
+                float oz = __shfl_xor(bz, s, 64);
+                int oi = __shfl_xor(bi, s, 64);
+                if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || topk_better(oz, oi, bz, bi))) {
+                    bz = oz;
+                    bi = oi;
+                }
+            }
+            zs[j] = bz;
+            is[j] = bi;
+            if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        }
+    }
+    if (lane == 0) {
+        float zmax = zs[0];
+        for (int j = 1; j < k; ++j) zmax = fmaxf(zmax, zs[j]);
+        float ex[kMaxK], sum = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            ex[j] = expf(zs[j] - zmax);
+            sum += ex[j];
+        }
+        for (int j = 0; j < k; ++j) {
+            ids_t[j] = is[j];
+            w_t[j] = ex[j] / sum;
+        }
+    }
+}
+
+}  // namespace eo

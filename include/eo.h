@@ -159,9 +159,14 @@ eo_status eo_route(eo_engine* e, int32_t layer, const void* x, int32_t T,
 eo_status eo_lookup_plan(eo_engine* e, int32_t layer, const int32_t* ids, int32_t T,
                          void* stream);
 
-/* Issue the last plan's fills (pinned pool -> cache slot) on the engine's copy
- * stream and make `stream` wait for them. Waits on the host for the plan.
- * EO_ERR_STATE without a pending plan. */
+/* Queue the last plan's fills (pinned pool -> cache slot, zhichai.net article,
+ * section 2, Decode paragraph) on `stream`: a kernel reads the fill list from
+ * device memory and copies each expert block over PCIe from the pool's
+ * device-visible mapping, so the call does not wait for the plan on the host.
+ * (Environment EO_FILL_SDMA=1 at engine creation: hipMemcpyAsync per expert on
+ * the engine's copy stream instead, after a host wait for the plan.)
+ * EO_ERR_STATE without a pending plan. Fills are counted in eo_stats when the
+ * host reads the plan. */
 eo_status eo_fill(eo_engine* e, void* stream);
 
 /* Run the last plan's host-list experts on the host cores for the tokens

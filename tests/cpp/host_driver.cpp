@@ -70,6 +70,16 @@ int main(int argc, char** argv) {
         eo::HostJob jb;
         jb.fmt = fmt; jb.lay = lay; jb.H = H; jb.I = I; jb.T = T; jb.k = k;
         jb.x = (const float*)x.data();
+        // bf16 bits of x when every value is a bf16 value (the bf16 route needs them)
+        std::vector<uint16_t> xb((size_t)T * H);
+        bool exact = true;
+        for (size_t i = 0; i < xb.size(); ++i) {
+            uint32_t u;
+            std::memcpy(&u, (const float*)x.data() + i, 4);
+            exact = exact && (u & 0xFFFFu) == 0;
+            xb[i] = (uint16_t)(u >> 16);
+        }
+        jb.xb = exact ? xb.data() : nullptr;
         jb.ids = (const int32_t*)ids.data();
         jb.w = (const float*)w.data();
         jb.experts = table.data();

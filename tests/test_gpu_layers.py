@@ -221,6 +221,75 @@ def test_decode_stack_against_oracle_chain(fmt):
         eo.eo_destroy(e)
 
 
+def _decode_capture(shape, seed, steps, forced, env):
+    """Decode `steps` tokens (fresh engine, EO_FUSED_ENTRY=env); returns the
+    final streams and every capture as bytes."""
+    import os
+    L, k, H = shape.layers, shape.top_k, shape.hidden
+    old = os.environ.get("EO_FUSED_ENTRY")
+    os.environ["EO_FUSED_ENTRY"] = env
+    try:
+        e = make_engine(shape, seed, cache_slots=7, max_tokens=1)
+    finally:
+        if old is None:
+            del os.environ["EO_FUSED_ENTRY"]
+        else:
+            os.environ["EO_FUSED_ENTRY"] = old
+    out = []
+    try:
+        eo.eo_set_bandwidth(e, 3, 5)
+        tr = synth.sticky_zipf_trace(seed, steps, L, shape.experts, k)
+        cx = torch.zeros((L, 1, H), dtype=torch.int16, device="cuda")
+        cy = torch.zeros((L, 1, H), dtype=torch.float32, device="cuda")
+        ci = torch.zeros((L, 1, k), dtype=torch.int32, device="cuda")
+        cw = torch.zeros((L, 1, k), dtype=torch.float32, device="cuda")
+        eo.eo_set_capture(e, cx, cy, ci, cw, 1)
+        for s in range(steps):
+            x = synth.activations(seed, 900 + s, 1, H, 1.0, True)
+            xd = dev(x.view(np.int16))
+            eo.eo_decode_step(e, xd, 1, dev(tr[s].reshape(L, 1, k)) if forced else None,
+                              _stream())
+            torch.cuda.synchronize()
+            out.append((x, xd.cpu().numpy().view(np.uint16).copy(),
+                        cx.cpu().numpy().view(np.uint16).copy(), cy.cpu().numpy().copy(),
+                        ci.cpu().numpy().copy(), cw.cpu().numpy().copy()))
+        out.append(eo.eo_stats_get(e))
+    finally:
+        eo.eo_destroy(e)
+    return out
+
+
+@pytest.mark.parametrize("forced", [True, False])
+def test_decode_fused_entry_matches_separate_kernels(forced):
+    # the fused one-token layer entry (residual + norm + logits, top-k in the
+    # plan kernel) does the same arithmetic in the same order as the separate
+    # residual, normalisation, router and top-k kernels: results are identical
+    shape = small_shape("bf16", layers=3)
+    a = _decode_capture(shape, 13, 4, forced, "1")
+    b = _decode_capture(shape, 13, 4, forced, "0")
+    for s in range(4):
+        for i in range(1, 6):
+            assert np.array_equal(a[s][i], b[s][i]), (s, i)
+    assert a[-1] == b[-1]
+
+
+def test_decode_routed_ids_bit_exact():
+    # no forced ids: the top-k taken inside the plan kernel against the oracle
+    shape = small_shape("bf16", layers=3)
+    seed = 14
+    res = _decode_capture(shape, seed, 5, False, "1")
+    for s in range(5):
+        x, xout, xin, ys, ids, ws = res[s]
+        rL = check_residual_stream(x, xin, ys)
+        assert np.array_equal(xout, rL)
+        for l in range(shape.layers):
+            R = synth.router_weights(seed, l, shape.experts, shape.hidden)
+            rid, rw, _ = OR.route(synth.bf16_bits_to_f32(xin[l]), R, shape.top_k)
+            assert np.array_equal(ids[l], rid), (s, l)
+            assert np.max(np.abs(ws[l] - rw)) <= 1e-6
+            check_layer(shape, seed, l, xin[l], ys[l], ids[l])
+
+
 def test_decode_determinism():
     shape = small_shape("bf16", layers=2)
     outs = []

@@ -71,7 +71,7 @@ struct eo_engine {
     uint8_t* d_slots = nullptr;
     uint8_t* d_shared = nullptr;
     float* d_router = nullptr;
-    float* d_router_t = nullptr;  // per-chain layout [L][E][64][H/64]
+    float* d_router_t = nullptr;  // chain-interleaved layout [L][E][H/256][64][4]
     uint16_t* d_xt = nullptr;     // [max_tokens][64][H/64] bf16 scratch
     int32_t* d_slot_key = nullptr;
     int64_t* d_slot_stamp = nullptr;
@@ -726,13 +726,14 @@ eo_status eo_set_router(eo_engine* e, int32_t layer, const float* host_w) {
     HIPCHK(hipSetDevice(e->cfg.device));
     HIPCHK(hipMemcpy(e->d_router + (size_t)layer * e->E * e->H, host_w,
                      sizeof(float) * e->E * e->H, hipMemcpyHostToDevice));
-    // per-chain copy: Rt[e][i][j] = R[e][i + 64 j]
+    // chain-interleaved copy: Rq[e][j/4][i][j%4] = R[e][i + 64 j]
     const int J = e->H / 64;
     std::vector<float> rt((size_t)e->E * e->H);
     for (int x = 0; x < e->E; ++x)
-        for (int i = 0; i < 64; ++i)
-            for (int j = 0; j < J; ++j)
-                rt[((size_t)x * 64 + i) * J + j] = host_w[(size_t)x * e->H + i + 64 * j];
+        for (int j = 0; j < J; ++j)
+            for (int i = 0; i < 64; ++i)
+                rt[(size_t)x * e->H + ((size_t)(j / 4) * 64 + i) * 4 + (j % 4)] =
+                    host_w[(size_t)x * e->H + i + 64 * j];
     HIPCHK(hipMemcpy(e->d_router_t + (size_t)layer * e->E * e->H, rt.data(),
                      sizeof(float) * e->E * e->H, hipMemcpyHostToDevice));
     return EO_OK;

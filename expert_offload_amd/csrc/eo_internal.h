@@ -37,8 +37,9 @@ struct DevState {
 
 // ---------------------------------------------------------------- launches
 // Router (fixed-order fp32 logits, top-k, softmax).
-// Rt: R laid out per chain ([E][64][H/64]) and xT: scratch for x laid out the
-// same way ([T][64][H/64] bf16); both optional (then the direct kernel runs).
+// Rt: R interleaved per chain ([E][H/256][64][4] fp32) and xT: scratch for x
+// interleaved the same way ([T][H/512][64][8] bf16); both optional (then the
+// direct kernel runs).
 hipError_t launch_route(const void* x, int act_bf16, const float* R, const float* Rt, int T,
                         int E, int H, int k, const int32_t* forced, int32_t* ids, float* w,
                         float* z_scratch, uint16_t* xT, hipStream_t s);
@@ -46,7 +47,7 @@ hipError_t launch_route(const void* x, int act_bf16, const float* R, const float
 // Layer entry of one token in the stacked decode step (bf16 activations):
 // r_out = bf16(r_in + sum_j parts[j] + y_host) (r_in copied when there are no
 // parts), u = bf16(r_out / sqrt(mean(r_out^2) + 1e-6)), z[e] = router logit of
-// u in the fixed chain order from the per-chain router Rt [E][64][H/64].
+// u in the fixed chain order from the chain-interleaved router Rt.
 // y_out (optional) receives the summed parts. r_out must not alias r_in when
 // parts are given. Needs entry_ok(E, H, act_bf16).
 struct EntryArgs {

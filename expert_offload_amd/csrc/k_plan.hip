@@ -24,6 +24,8 @@ namespace eo {
 namespace {
 
 constexpr int kThreads = 1024;
+constexpr int kMaxSlotsLds = 8192;
+constexpr int kMaxSlotsPerThread = kMaxSlotsLds / kThreads;
 
 __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
 #pragma unroll
@@ -74,6 +76,29 @@ __device__ int2 block_scan(int v, int* red) {
     return make_int2(base + incl - v, tot);
 }
 
+// Block-wide exclusive prefix of a 64-bit v in thread order (fields packed in
+// v must not carry into each other); returns the prefix, *total gets the sum.
+__device__ uint64_t block_scan64(uint64_t v, uint64_t* red, uint64_t* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t incl = v;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+        uint32_t lo = __shfl_up((uint32_t)incl, s, 64);
+        uint32_t hi = __shfl_up((uint32_t)(incl >> 32), s, 64);
+        if (lane >= s) incl += ((uint64_t)hi << 32) | lo;
+    }
+    __syncthreads();
+    if (lane == 63) red[wave] = incl;
+    __syncthreads();
+    uint64_t base = 0, tot = 0;
+    for (int i = 0; i < kThreads / 64; ++i) {
+        if (i < wave) base += red[i];
+        tot += red[i];
+    }
+    *total = tot;
+    return base + incl - v;
+}
+
 __device__ uint64_t block_min_u64(uint64_t v, uint64_t* red) {
     v = wave_min_u64(v);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -108,12 +133,51 @@ __global__ __launch_bounds__(kThreads) void k_plan(
     __shared__ int32_t s_ids[kMaxK];
     __shared__ float s_w[kMaxK];
 
+    __shared__ int s_vslot;
+
+    __shared__ int s_miss[kMaxE];
+    __shared__ long long s_credit0;
+    __shared__ int s_bp, s_bh, s_seq0;
+
     const int tid = threadIdx.x;
+    // slot table into LDS (every load of a thread issued before its first
+    // store), the empty slots of this thread counted on the way; the residency
+    // counters
+    int my_empty = 0;
+    {
+        int32_t kr[kMaxSlotsPerThread];
+        int64_t sr[kMaxSlotsPerThread];
+#pragma unroll
+        for (int i = 0; i < kMaxSlotsPerThread; ++i) {
+            const int sl = tid + i * kThreads;
+            if (sl < C) {
+                kr[i] = g_slot_key[sl];
+                sr[i] = g_slot_stamp[sl];
+            }
+        }
+        if (tid == 0) {
+            s_clock = st->clock;
+            s_credit0 = st->credit;
+            s_bp = st->bp;
+            s_bh = st->bh;
+            s_seq0 = st->seq;
+        }
+#pragma unroll
+        for (int i = 0; i < kMaxSlotsPerThread; ++i) {
+            const int sl = tid + i * kThreads;
+            if (sl < C) {
+                s_key[sl] = kr[i];
+                s_stamp[sl] = sr[i];
+                my_empty += kr[i] < 0;
+            }
+        }
+    }
+    for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
+    if (tid == 0) s_err = 0;
+    if (rt.z && tid < 64)  // one token: select its experts from the logits
+        topk_token(rt.z, E, k, rt.forced, s_ids, s_w);
+    __syncthreads();
     if (rt.z) {
-        // one token: select its experts here from the logits (first wavefront)
-        if (tid < 64)
-            topk_token(rt.z, E, k, rt.forced, s_ids, s_w);
-        __syncthreads();
         if (tid < k) {
             rt.ids_out[tid] = s_ids[tid];
             rt.w_out[tid] = s_w[tid];
@@ -121,13 +185,6 @@ __global__ __launch_bounds__(kThreads) void k_plan(
         ids = s_ids;
         w = s_w;
     }
-    for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
-    if (tid == 0) s_err = 0;
-    for (int s = tid; s < C; s += kThreads) {
-        s_key[s] = g_slot_key[s];
-        s_stamp[s] = g_slot_stamp[s];
-    }
-    __syncthreads();
 
     // token counts per expert; ids must be in range and distinct per token
     for (int p = tid; p < T * k; p += kThreads) {
@@ -144,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void k_plan(
     __syncthreads();
     if (s_err) {
         if (tid == 0) {
-            int seq = st->seq + 1;
+            int seq = s_seq0 + 1;
             st->seq = seq;
             dp->pad = s_err;
             hp->pad = s_err;
@@ -154,60 +211,63 @@ __global__ __launch_bounds__(kThreads) void k_plan(
         }
         return;
     }
-    if (tid == 0) s_clock = st->clock + 1;
-    __syncthreads();
-    const int64_t clock = s_clock;
+    const int64_t clock = s_clock + 1;
 
-    // hits and misses
-    for (int e = tid; e < E; e += kThreads) {
-        int kd = 0, sl = -1;
-        if (cnt[e] > 0) {
-            int key = layer * E + e;
-            int s = key2slot[key];
-            if (s >= 0) {
-                kd = 1;
-                sl = s;
-                s_stamp[s] = clock;
-            } else {
-                kd = 2;
-            }
+    // hits and misses (E <= kThreads: one expert per thread)
+    const int my_e = tid < E ? tid : -1;
+    int kd = 0, sl = -1;
+    if (my_e >= 0 && cnt[my_e] > 0) {
+        int s = key2slot[layer * E + my_e];
+        if (s >= 0) {
+            kd = 1;
+            sl = s;
+            s_stamp[s] = clock;
+        } else {
+            kd = 2;
         }
-        kind[e] = kd;
-        slot_of[e] = sl;
     }
-    __syncthreads();
-
-    // counts (E <= kThreads: one expert per thread)
-    int my_e = tid < E ? tid : -1;
-    int is_hit = (my_e >= 0 && kind[my_e] == 1) ? 1 : 0;
-    int is_miss = (my_e >= 0 && kind[my_e] == 2) ? 1 : 0;
-    int2 hs = block_scan(is_hit, red);
-    if (is_hit) {
-        dp->hit_e[hs.x] = hp->hit_e[hs.x] = my_e;
-        dp->hit_slot[hs.x] = hp->hit_slot[hs.x] = slot_of[my_e];
+    if (my_e >= 0) {
+        kind[my_e] = kd;
+        slot_of[my_e] = sl;
     }
-    int m = block_sum(is_miss, red);
+    // one scan: hit index (bits 0-15), miss index (16-31), empty slots (32-)
+    uint64_t tot;
+    const uint64_t pre = block_scan64((uint64_t)(kd == 1) | ((uint64_t)(kd == 2) << 16) |
+                                          ((uint64_t)my_empty << 32),
+                                      red64, &tot);
+    const int n_hit0 = (int)(tot & 0xFFFF), m = (int)((tot >> 16) & 0xFFFF);
+    const int empty = (int)(tot >> 32);
+    if (kd == 1) {
+        const int hi = (int)(pre & 0xFFFF);
+        dp->hit_e[hi] = hp->hit_e[hi] = my_e;
+        dp->hit_slot[hi] = hp->hit_slot[hi] = sl;
+    } else if (kd == 2) {
+        s_miss[(pre >> 16) & 0xFFFF] = my_e;
+    }
     if (tid == 0) {
-        s_h = hs.y;
+        s_h = n_hit0;
         s_m = m;
-        long long c = st->credit, bp = st->bp, bh = st->bh;
+        long long c = s_credit0, bp = s_bp, bh = s_bh;
         long long q = (c + (long long)m * bp) / bh;
         if (q > m) q = m;
         long long c2 = c + (long long)m * bp - q * bh;
         if (c2 > bh - 1) c2 = bh - 1;
         s_credit = c2;
         s_q = (int)q;
-        int room = C - hs.y;
+        int room = C - n_hit0;
         s_qfill = (int)(q < room ? q : room);
     }
     __syncthreads();
     const int q_fill = s_qfill;
 
-    // rank misses by (count desc, id asc)
-    if (is_miss) {
-        int c0 = cnt[my_e], r = 0;
-        for (int e = 0; e < E; ++e)
-            if (kind[e] == 2 && (cnt[e] > c0 || (cnt[e] == c0 && e < my_e))) ++r;
+    // rank misses by (count desc, id asc) within the list of misses
+    if (kd == 2) {
+        const int c0 = cnt[my_e];
+        int r = 0;
+        for (int j = 0; j < m; ++j) {
+            const int e2 = s_miss[j], c2 = cnt[e2];
+            r += (c2 > c0 || (c2 == c0 && e2 < my_e));
+        }
         if (r < q_fill) {
             fill_e[r] = my_e;
             dp->fill_e[r] = hp->fill_e[r] = my_e;
@@ -217,28 +277,31 @@ __global__ __launch_bounds__(kThreads) void k_plan(
     }
 
     // victims among occupied slots not touched this call (stamp < clock)
-    int empty = 0;
-    for (int s = tid; s < C; s += kThreads) empty += (s_key[s] < 0);
-    empty = block_sum(empty, red);
     int need = q_fill - empty;
     int n_ev = 0;
     for (int r = 0; r < need; ++r, ++n_ev) {
         uint64_t best = ~0ull;
+        int best_slot = -1;
         for (int s = tid; s < C; s += kThreads) {
             if (s_key[s] >= 0 && s_stamp[s] < clock) {
                 uint64_t v = ((uint64_t)s_stamp[s] << 24) | (uint64_t)s_key[s];
-                best = v < best ? v : best;
+                if (v < best) {
+                    best = v;
+                    best_slot = s;
+                }
             }
         }
+        const uint64_t mine = best;
         best = block_min_u64(best, red64);
         if (best == ~0ull) break;  // unreachable: q_fill <= C - hits
-        int vkey = (int)(best & 0xFFFFFFull);
-        int vslot = key2slot[vkey];
+        // keys are unique among occupied slots: one thread holds the victim
+        if (mine == best) s_vslot = best_slot;
         __syncthreads();
         if (tid == 0) {
+            const int vkey = (int)(best & 0xFFFFFFull);
             dp->evict_key[r] = hp->evict_key[r] = vkey;
             key2slot[vkey] = -1;
-            s_key[vslot] = -1;
+            s_key[s_vslot] = -1;  // refilled below: every freed slot takes a fill
         }
         __syncthreads();
     }
@@ -246,28 +309,30 @@ __global__ __launch_bounds__(kThreads) void k_plan(
     // empty slots in ascending order go to the fills in rank order
     const int per = (C + kThreads - 1) / kThreads;
     const int s_lo = min(C, tid * per), s_hi = min(C, s_lo + per);
-    int my_empty = 0;
-    for (int s = s_lo; s < s_hi; ++s) my_empty += (s_key[s] < 0);
-    int2 es = block_scan(my_empty, red);
-    int r = es.x;
+    int range_empty = 0;
+    if (q_fill > 0)  // block-uniform
+        for (int s = s_lo; s < s_hi; ++s) range_empty += (s_key[s] < 0);
+    int r = q_fill > 0 ? block_scan(range_empty, red).x : 0;
     for (int s = s_lo; s < s_hi && r < q_fill; ++s) {
         if (s_key[s] < 0) {
             int e = fill_e[r];
             int key = layer * E + e;
             s_key[s] = key;
             s_stamp[s] = clock;
+            g_slot_key[s] = key;
+            g_slot_stamp[s] = clock;
             key2slot[key] = s;
             slot_of[e] = s;
             dp->fill_slot[r] = hp->fill_slot[r] = s;
             ++r;
         }
     }
+    // write-back of the rest of the table: only hit stamps changed (evicted
+    // slots are all refilled above)
+    for (int e = tid; e < E; e += kThreads)
+        if (kind[e] == 1) g_slot_stamp[slot_of[e]] = clock;
     __syncthreads();
 
-    for (int s = tid; s < C; s += kThreads) {
-        g_slot_key[s] = s_key[s];
-        g_slot_stamp[s] = s_stamp[s];
-    }
     for (int e = tid; e < E; e += kThreads) {
         dp->e2slot[e] = slot_of[e];
         dp->count[e] = cnt[e];
@@ -319,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void k_plan(
     }
     __syncthreads();
     if (tid == 0) {
-        int seq = st->seq + 1;
+        int seq = s_seq0 + 1;
         st->seq = seq;
         dp->seq = seq;
         __threadfence_system();
@@ -328,8 +393,6 @@ __global__ __launch_bounds__(kThreads) void k_plan(
 }
 
 }  // namespace
-
-constexpr int kMaxSlotsLds = 8192;
 
 int plan_max_slots() { return kMaxSlotsLds; }
 

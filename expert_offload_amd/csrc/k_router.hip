@@ -84,50 +84,53 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ z, int T
 }
 
 // ---------------------------------------------------------------- many tokens
-// Same accumulation order, with the operands laid out per chain: chain i of
-// row r is stored contiguously (xT[t][i][j] = x[t][i + 64 j], Rt[e][i][j] =
-// R[e][i + 64 j]), so lane i reads 8 (x) or 4 (R) consecutive steps j with one
-// 16-byte load instead of one element per load. The FMAs still run j = 0, 1, ...
-// in order from +0, and the butterfly is unchanged, so z is bit-identical.
+// Same accumulation order, with the operands interleaved per chain so that a
+// 16-byte load gives a lane several consecutive steps of its own chain and a
+// wavefront's load is one contiguous 1 KiB: router Rq[e][j/4][i][j%4] =
+// R[e][i + 64 j] (fp32, 4 steps per load) and activations
+// xq[t][j/8][i][j%8] = x[t][i + 64 j] (bf16, 8 steps per load). The FMAs still
+// run j = 0, 1, ... in order from +0 and the butterfly is unchanged, so z is
+// bit-identical to the direct kernel.
 constexpr int kTT2 = 8, kEE2 = 8;
 
 __global__ __launch_bounds__(64) void k_chain_transpose(const uint16_t* __restrict__ x, int H,
-                                                        uint16_t* __restrict__ xT) {
-    const int t = blockIdx.x, i = threadIdx.x, J = H / 64;
+                                                        uint16_t* __restrict__ xq) {
+    const int t = blockIdx.x, i = threadIdx.x, J8 = H / 512;
     const uint16_t* xr = x + (size_t)t * H;
-    uint16_t* dst = xT + ((size_t)t * 64 + i) * J;
-    for (int j0 = 0; j0 < J; j0 += 8) {
+    uint4* dst = (uint4*)xq + (size_t)t * J8 * 64;
+    for (int j8 = 0; j8 < J8; ++j8) {
         uint32_t w[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            w[q] = (uint32_t)xr[i + 64 * (j0 + 2 * q)] | ((uint32_t)xr[i + 64 * (j0 + 2 * q + 1)] << 16);
-        *(uint4*)(dst + j0) = make_uint4(w[0], w[1], w[2], w[3]);
+            w[q] = (uint32_t)xr[i + 64 * (8 * j8 + 2 * q)] |
+                   ((uint32_t)xr[i + 64 * (8 * j8 + 2 * q + 1)] << 16);
+        dst[(size_t)j8 * 64 + i] = make_uint4(w[0], w[1], w[2], w[3]);
     }
 }
 
-__global__ __launch_bounds__(256) void k_logits_chains(const uint16_t* __restrict__ xT,
-                                                       const float* __restrict__ Rt, int T, int E,
+__global__ __launch_bounds__(256) void k_logits_chains(const uint16_t* __restrict__ xq,
+                                                       const float* __restrict__ Rq, int T, int E,
                                                        int H, float* __restrict__ z) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t0 = blockIdx.x * kTT2;
     const int e0 = (blockIdx.y * 4 + wave) * kEE2;
-    const int J = H / 64;
+    const int J8 = H / 512;
     float acc[kTT2][kEE2];
 #pragma unroll
     for (int a = 0; a < kTT2; ++a)
 #pragma unroll
         for (int b = 0; b < kEE2; ++b) acc[a][b] = 0.0f;
-    const uint16_t* xp[kTT2];
+    const uint4* xp[kTT2];
 #pragma unroll
-    for (int a = 0; a < kTT2; ++a) xp[a] = xT + ((size_t)min(t0 + a, T - 1) * 64 + lane) * J;
-    const float* rp[kEE2];
+    for (int a = 0; a < kTT2; ++a) xp[a] = (const uint4*)xq + (size_t)min(t0 + a, T - 1) * J8 * 64 + lane;
+    const float4* rp[kEE2];
 #pragma unroll
-    for (int b = 0; b < kEE2; ++b) rp[b] = Rt + ((size_t)(e0 + b) * 64 + lane) * J;
-    for (int j0 = 0; j0 < J; j0 += 8) {
+    for (int b = 0; b < kEE2; ++b) rp[b] = (const float4*)Rq + (size_t)(e0 + b) * (2 * J8) * 64 + lane;
+    for (int j8 = 0; j8 < J8; ++j8) {
         float xv[kTT2][8];
 #pragma unroll
         for (int a = 0; a < kTT2; ++a) {
-            uint4 q = *(const uint4*)(xp[a] + j0);
+            uint4 q = xp[a][(size_t)j8 * 64];
             uint32_t wds[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(256) void k_logits_chains(const uint16_t* __restric
         }
 #pragma unroll
         for (int b = 0; b < kEE2; ++b) {
-            float4 r0 = *(const float4*)(rp[b] + j0), r1 = *(const float4*)(rp[b] + j0 + 4);
+            float4 r0 = rp[b][(size_t)(2 * j8) * 64], r1 = rp[b][(size_t)(2 * j8 + 1) * 64];
             float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj)
@@ -167,18 +170,20 @@ __global__ __launch_bounds__(256) void k_logits_chains(const uint16_t* __restric
 // the token's row (r_new = r + sum of parts + host part, stored in bf16) and
 // u = r_new / sqrt(mean(r_new^2) + 1e-6) in the same fixed order as the
 // separate residual and normalisation kernels; block 0 writes r_new, y and u.
-// Each wavefront then owns one expert's logit: lane i runs chain i over
-// Rt[e][i][:] (contiguous) against u[i + 64 j] from LDS, then the butterfly.
-// acc = fma chain over j = 0..J-1 of u[lane + 64 j] * rp[j], loading CH steps
-// of the chain (CH/4 16-byte loads) before their FMAs.
+// Each wavefront then owns one expert's logit: lane i runs chain i over the
+// interleaved router Rq[e][:][i][:] against u[i + 64 j] from LDS, then the
+// butterfly.
+// acc = fma chain over j = 0..J-1 of u[lane + 64 j] * R[e][lane + 64 j] with
+// rq = &Rq[e][0][lane] (float4 steps 64 apart), loading CH steps of the chain
+// (CH/4 coalesced 16-byte loads) before their FMAs.
 template <int CH>
-__device__ __forceinline__ float chain_dot(const float* __restrict__ rp, const float* s_u,
+__device__ __forceinline__ float chain_dot(const float4* __restrict__ rq, const float* s_u,
                                            int lane, int J, float acc) {
     for (int j0 = 0; j0 < J; j0 += CH) {
         float rr[CH];
 #pragma unroll
         for (int q = 0; q < CH / 4; ++q) {
-            float4 v = ((const float4*)(rp + j0))[q];
+            float4 v = rq[(size_t)(j0 / 4 + q) * 64];
             rr[4 * q] = v.x; rr[4 * q + 1] = v.y; rr[4 * q + 2] = v.z; rr[4 * q + 3] = v.w;
         }
 #pragma unroll
@@ -259,12 +264,12 @@ __global__ __launch_bounds__(256) void k_entry(EntryArgs a) {
     const int e = blockIdx.x * 4 + wave;
     if (e >= a.E) return;
     const int J = H / 64;
-    const float* rp = a.Rt + ((size_t)e * 64 + lane) * J;
+    const float4* rq = (const float4*)a.Rt + (size_t)e * (J / 4) * 64 + lane;
     float acc = 0.0f;
     if (J % 32 == 0)
-        acc = chain_dot<32>(rp, s_u, lane, J, acc);
+        acc = chain_dot<32>(rq, s_u, lane, J, acc);
     else
-        acc = chain_dot<8>(rp, s_u, lane, J, acc);
+        acc = chain_dot<8>(rq, s_u, lane, J, acc);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) acc = acc + __shfl_xor(acc, m, 64);
     if (lane == 0) a.z[e] = acc;

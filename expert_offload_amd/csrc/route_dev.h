@@ -16,21 +16,12 @@ __device__ __forceinline__ bool topk_better(float za, int ia, float zb, int ib) 
     return za > zb || (za == zb && ia < ib);
 }
 
-// All 64 lanes of the wavefront call this; lane 0 writes ids[0..k) and w[0..k).
-__device__ __forceinline__ void topk_token(const float* __restrict__ zt, int E, int k,
-                                           const int32_t* __restrict__ forced_t,
-                                           int32_t* __restrict__ ids_t, float* __restrict__ w_t) {
+// k rounds of (max z, then smallest id) over E <= 64 * kPer logits.
+template <int kPer>
+__device__ __forceinline__ void topk_select(const float* __restrict__ zt, int E, int k, float* zs,
+                                            int* is) {
     const int lane = threadIdx.x & 63;
-    float zs[kMaxK];
-    int is[kMaxK];
-    if (forced_t) {
-        for (int j = 0; j < k; ++j) {
-            is[j] = forced_t[j];
-            // out-of-range ids are reported by the lookup; read in bounds here
-            zs[j] = zt[min(max(is[j], 0), E - 1)];
-        }
-    } else {
-        constexpr int kPer = kMaxE / 64;
+    {
         float zl[kPer];
         uint32_t taken = 0;
 #pragma unroll
@@ -63,6 +54,28 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ zt, int E, 
             is[j] = bi;
             if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
         }
+    }
+}
+
+// All 64 lanes of the wavefront call this; lane 0 writes ids[0..k) and w[0..k).
+__device__ __forceinline__ void topk_token(const float* __restrict__ zt, int E, int k,
+                                           const int32_t* __restrict__ forced_t,
+                                           int32_t* __restrict__ ids_t, float* __restrict__ w_t) {
+    const int lane = threadIdx.x & 63;
+    float zs[kMaxK];
+    int is[kMaxK];
+    if (forced_t) {
+        for (int j = 0; j < k; ++j) {
+            is[j] = forced_t[j];
+            // out-of-range ids are reported by the lookup; read in bounds here
+            zs[j] = zt[min(max(is[j], 0), E - 1)];
+        }
+    } else if (E <= 128) {
+        topk_select<2>(zt, E, k, zs, is);
+    } else if (E <= 256) {
+        topk_select<4>(zt, E, k, zs, is);
+    } else {
+        topk_select<kMaxE / 64>(zt, E, k, zs, is);
     }
     if (lane == 0) {
         float zmax = zs[0];

@@ -17,6 +17,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <functional>
+#include <memory>
 #include <mutex>
 #include <thread>
 
@@ -248,15 +249,22 @@ EO_AVX512BF16 void dot2_bf16_avx512(const uint16_t* a, const uint16_t* b, const 
     *rb = _mm512_reduce_add_ps(_mm512_add_ps(b0, b1));
 }
 
-// One row of K (K % 64 == 0) against one vector.
-EO_AVX512BF16 float dot_bf16_avx512(const uint16_t* a, const uint16_t* x, int K) {
-    __m512 a0 = _mm512_setzero_ps(), a1 = _mm512_setzero_ps();
-    for (int i = 0; i < K; i += 64) {
-        a0 = _mm512_dpbf16_ps(a0, as_bh(_mm512_loadu_si512(a + i)), as_bh(_mm512_loadu_si512(x + i)));
-        a1 = _mm512_dpbf16_ps(a1, as_bh(_mm512_loadu_si512(a + i + 32)),
-                              as_bh(_mm512_loadu_si512(x + i + 32)));
+// Four rows (stride ld, K % 64 == 0) against one vector.
+EO_AVX512BF16 void dot4_bf16_avx512(const uint16_t* a, size_t ld, const uint16_t* x, int K,
+                                    float* out) {
+    __m512 s0 = _mm512_setzero_ps(), s1 = _mm512_setzero_ps();
+    __m512 s2 = _mm512_setzero_ps(), s3 = _mm512_setzero_ps();
+    for (int i = 0; i < K; i += 32) {
+        __m512bh xv = as_bh(_mm512_loadu_si512(x + i));
+        s0 = _mm512_dpbf16_ps(s0, as_bh(_mm512_loadu_si512(a + i)), xv);
+        s1 = _mm512_dpbf16_ps(s1, as_bh(_mm512_loadu_si512(a + ld + i)), xv);
+        s2 = _mm512_dpbf16_ps(s2, as_bh(_mm512_loadu_si512(a + 2 * ld + i)), xv);
+        s3 = _mm512_dpbf16_ps(s3, as_bh(_mm512_loadu_si512(a + 3 * ld + i)), xv);
     }
-    return _mm512_reduce_add_ps(_mm512_add_ps(a0, a1));
+    out[0] = _mm512_reduce_add_ps(s0);
+    out[1] = _mm512_reduce_add_ps(s1);
+    out[2] = _mm512_reduce_add_ps(s2);
+    out[3] = _mm512_reduce_add_ps(s3);
 }
 
 uint16_t bf16_rne(float f) {
@@ -317,38 +325,84 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
     constexpr int RB = 16;
     const int nb1 = (I + RB - 1) / RB;
     if (fmt == EO_W_BF16 && jb.xb && H % 128 == 0 && I % 64 == 0 && cpu_has_avx512bf16()) {
-        // h as bf16 [ne][tokens][I], in the caller's scratch
-        if (scratch.size() < (hoff[ne] + 1) / 2) scratch.resize((hoff[ne] + 1) / 2);
+        // One pool run, pipelined over experts: gate/up rows of expert i (h_i,
+        // bf16) and the down rows of expert i-1 (v_i = W_down h_i per token,
+        // unweighted fp32) are queued alternately; a down task waits for its
+        // expert's gate/up tasks, which were all handed out before it. The
+        // weighted sum over each token's slots follows in slot order.
+        std::vector<size_t> voff(ne + 1, 0);
+        for (int i = 0; i < ne; ++i) voff[i + 1] = voff[i] + toks[i].size() * (size_t)H;
+        const size_t vtot = voff[ne];
+        const size_t hwords = (hoff[ne] + 1) / 2;
+        if (scratch.size() < hwords + vtot) scratch.resize(hwords + vtot);
         uint16_t* hb = (uint16_t*)scratch.data();
-        pool->run(ne * nb1, [&](int task) {
-            const int ei = task / nb1, rb = task % nb1;
-            const uint16_t* W = (const uint16_t*)(jb.experts[exps[ei]] + lay.d13);
-            for (int r = rb * RB; r < std::min(I, rb * RB + RB); ++r)
-                for (size_t ti = 0; ti < toks[ei].size(); ++ti) {
-                    float g, u;
-                    dot2_bf16_avx512(W + (size_t)r * H, W + (size_t)(I + r) * H,
-                                     jb.xb + (size_t)toks[ei][ti] * H, H, &g, &u);
-                    hb[hoff[ei] + ti * I + r] = bf16_rne(g / (1.0f + std::exp(-g)) * u);
-                }
-        });
-        const int nb2 = (H + RB - 1) / RB;
-        pool->run(nb2, [&](int task) {
-            for (int o = task * RB; o < std::min(H, task * RB + RB); ++o)
-                for (int t = 0; t < T; ++t) {
-                    float acc = 0.0f;
-                    for (int j = 0; j < k; ++j) {
-                        int e = jb.ids[t * k + j];
-                        if (e < 0 || e >= EO_MAX_EXPERTS || !jb.experts[e]) continue;
-                        int ei = slot_of[e];
-                        const std::vector<int>& tl = toks[ei];
-                        int ti = (int)(std::lower_bound(tl.begin(), tl.end(), t) - tl.begin());
-                        const uint16_t* W2 = (const uint16_t*)(jb.experts[e] + lay.d2);
-                        acc += jb.w[t * k + j] *
-                               dot_bf16_avx512(W2 + (size_t)o * I, hb + hoff[ei] + ti * I, I);
+        float* v = scratch.data() + hwords;
+        const int nb2 = H / RB;  // H % 128 == 0
+        // segments: (phase, expert) in queue order
+        std::vector<std::pair<int, int>> seg;
+        seg.push_back({1, 0});
+        for (int i = 1; i < ne; ++i) {
+            seg.push_back({1, i});
+            seg.push_back({2, i - 1});
+        }
+        seg.push_back({2, ne - 1});
+        std::vector<int> seg_start(seg.size() + 1, 0);
+        for (size_t q = 0; q < seg.size(); ++q)
+            seg_start[q + 1] = seg_start[q] + (seg[q].first == 1 ? nb1 : nb2);
+        std::unique_ptr<std::atomic<int>[]> done1(new std::atomic<int>[ne]);
+        for (int i = 0; i < ne; ++i) done1[i].store(0, std::memory_order_relaxed);
+        pool->run(seg_start.back(), [&](int task) {
+            size_t q = 0;
+            while (task >= seg_start[q + 1]) ++q;
+            const int ph = seg[q].first, ei = seg[q].second, blk = task - seg_start[q];
+            const uint8_t* b = jb.experts[exps[ei]];
+            const size_t nt = toks[ei].size();
+            if (ph == 1) {
+                const uint16_t* W = (const uint16_t*)(b + lay.d13);
+                for (int r = blk * RB; r < std::min(I, blk * RB + RB); ++r)
+                    for (size_t ti = 0; ti < nt; ++ti) {
+                        float g, u;
+                        dot2_bf16_avx512(W + (size_t)r * H, W + (size_t)(I + r) * H,
+                                         jb.xb + (size_t)toks[ei][ti] * H, H, &g, &u);
+                        hb[hoff[ei] + ti * I + r] = bf16_rne(g / (1.0f + std::exp(-g)) * u);
                     }
-                    jb.y[(size_t)t * H + o] += acc;
-                }
+                done1[ei].fetch_add(1, std::memory_order_release);
+            } else {
+                while (done1[ei].load(std::memory_order_acquire) < nb1) _mm_pause();
+                const uint16_t* W2 = (const uint16_t*)(b + lay.d2);
+                for (int o = blk * RB; o < blk * RB + RB; o += 4)
+                    for (size_t ti = 0; ti < nt; ++ti) {
+                        float out[4];
+                        dot4_bf16_avx512(W2 + (size_t)o * I, I, hb + hoff[ei] + ti * I, I, out);
+                        float* vo = v + voff[ei] + ti * H + o;
+                        vo[0] = out[0];
+                        vo[1] = out[1];
+                        vo[2] = out[2];
+                        vo[3] = out[3];
+                    }
+            }
         });
+        // y[t] += sum over the token's host slots, in slot order, of w * v
+        auto combine_rows = [&](int t) {
+            float* yt = jb.y + (size_t)t * H;
+            thread_local std::vector<float> a;
+            a.assign(H, 0.0f);
+            for (int j = 0; j < k; ++j) {
+                int e = jb.ids[t * k + j];
+                if (e < 0 || e >= EO_MAX_EXPERTS || !jb.experts[e]) continue;
+                const int ei = slot_of[e];
+                const std::vector<int>& tl = toks[ei];
+                const size_t ti = std::lower_bound(tl.begin(), tl.end(), t) - tl.begin();
+                const float* vt = v + voff[ei] + ti * H;
+                const float wt = jb.w[t * k + j];
+                for (int o = 0; o < H; ++o) a[o] += wt * vt[o];
+            }
+            for (int o = 0; o < H; ++o) yt[o] += a[o];
+        };
+        if (T == 1)
+            combine_rows(0);
+        else
+            pool->run(T, combine_rows);
         return;
     }
     pool->run(ne * nb1, [&](int task) {

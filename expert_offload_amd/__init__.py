@@ -250,11 +250,12 @@ def eo_set_timing(e, enable: bool) -> None:
 
 
 def eo_kernel_times(e, reset: bool = False) -> dict:
-    ms = (ctypes.c_double * 4)()
-    n = (_I64 * 2)()
+    ms = (ctypes.c_double * 5)()
+    n = (_I64 * 3)()
     _check(lib().eo_kernel_times(e, ms, n, 1 if reset else 0))
     return {"gemv_gate_up_ms": ms[0], "gemv_down_ms": ms[1], "gemm_gate_up_ms": ms[2],
-            "gemm_down_ms": ms[3], "gemv_launches": n[0], "gemm_launches": n[1]}
+            "gemm_down_ms": ms[3], "fill_ms": ms[4], "gemv_launches": n[0],
+            "gemm_launches": n[1], "fill_launches": n[2]}
 
 
 def eo_sync(e) -> None:

@@ -125,9 +125,9 @@ struct eo_engine {
 
     bool timing = false;
     int gemv_fast = 1;  // EO_GEMV_FAST=0 selects the generic decode GEMV kernels
-    std::vector<TimedSet> gemv_ev, gemm_ev, free_ev;
-    double kms[4] = {0, 0, 0, 0};  // gemv gate/up, gemv down, gemm1, gemm2
-    int64_t gemv_n = 0, gemm_n = 0;
+    std::vector<TimedSet> gemv_ev, gemm_ev, fill_ev, free_ev;
+    double kms[5] = {0, 0, 0, 0, 0};  // gemv gate/up, gemv down, gemm1, gemm2, fill
+    int64_t gemv_n = 0, gemm_n = 0, fill_n = 0;
 
     void* cap_x = nullptr;
     float* cap_y = nullptr;
@@ -144,7 +144,10 @@ eo_status get_set(eo_engine* e, TimedSet* p) {
         e->free_ev.pop_back();
         return EO_OK;
     }
-    for (int i = 0; i < 4; ++i) HIPCHK(hipEventCreate(&p->ev[i]));
+    // timing only: no system-scope fence at record time, so the cache writeback
+    // and invalidation it implies do not slow the kernels being timed
+    for (int i = 0; i < 4; ++i)
+        HIPCHK(hipEventCreateWithFlags(&p->ev[i], hipEventDisableSystemFence));
     return EO_OK;
 }
 
@@ -163,6 +166,15 @@ eo_status harvest_times(eo_engine* e) {
         }
         v->clear();
     }
+    for (auto& p : e->fill_ev) {
+        HIPCHK(hipEventSynchronize(p.ev[1]));
+        float m0 = 0;
+        HIPCHK(hipEventElapsedTime(&m0, p.ev[0], p.ev[1]));
+        e->kms[4] += m0;
+        e->fill_n += 1;
+        e->free_ev.push_back(p);
+    }
+    e->fill_ev.clear();
     return EO_OK;
 }
 
@@ -280,9 +292,12 @@ eo_status do_fill(eo_engine* e, hipStream_t s) {
     if (!e->plan_pending) return fail(EO_ERR_STATE, "no pending plan (call eo_lookup_plan first)");
     if (e->C == 0) return EO_OK;
     if (!e->fill_sdma) {
+        TimedSet ts{};
+        if (e->timing) EOCHK(get_set(e, &ts));
         hipError_t he = launch_fill(e->d_plan, e->pool_dev[e->plan_layer], e->d_slots, e->S,
-                                    e->S_pad, s);
+                                    e->S_pad, s, ts.ev[0], ts.ev[1]);
         if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("fill: ") + hipGetErrorString(he));
+        if (e->timing) e->fill_ev.push_back(ts);
         return EO_OK;
     }
     EOCHK(wait_plan(e));
@@ -536,7 +551,7 @@ void destroy_all(eo_engine* e) {
     for (hipEvent_t ev : {e->ev_fill, e->ev_copy[0], e->ev_copy[1], e->ev_comp[0], e->ev_comp[1],
                           e->ev_start})
         if (ev) (void)hipEventDestroy(ev);
-    for (auto* v : {&e->gemv_ev, &e->gemm_ev, &e->free_ev})
+    for (auto* v : {&e->gemv_ev, &e->gemm_ev, &e->fill_ev, &e->free_ev})
         for (auto& p : *v)
             for (hipEvent_t ev : p.ev) (void)hipEventDestroy(ev);
     if (e->tp) threadpool_destroy(e->tp);
@@ -1076,14 +1091,15 @@ eo_status eo_kernel_times(eo_engine* e, double* ms, int64_t* launches, int32_t r
     if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
     EOCHK(harvest_times(e));
     if (ms)
-        for (int i = 0; i < 4; ++i) ms[i] = e->kms[i];
+        for (int i = 0; i < 5; ++i) ms[i] = e->kms[i];
     if (launches) {
         launches[0] = e->gemv_n;
         launches[1] = e->gemm_n;
+        launches[2] = e->fill_n;
     }
     if (reset) {
         for (double& v : e->kms) v = 0;
-        e->gemv_n = e->gemm_n = 0;
+        e->gemv_n = e->gemm_n = e->fill_n = 0;
     }
     return EO_OK;
 }

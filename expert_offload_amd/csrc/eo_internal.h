@@ -86,7 +86,8 @@ hipError_t launch_plan(int layer, const int32_t* ids, const float* w, const void
 // pointer to pinned host memory, E * S_pad bytes) into their slots. Reads the
 // fill list from d_plan; no host synchronisation.
 hipError_t launch_fill(const DevPlan* plan, const uint8_t* pool_layer_dev, uint8_t* slots,
-                       uint64_t S, uint64_t S_pad, hipStream_t s);
+                       uint64_t S, uint64_t S_pad, hipStream_t s, hipEvent_t ev_start = nullptr,
+                       hipEvent_t ev_stop = nullptr);
 
 // Permute: group the (token, k) pairs whose expert is resident by expert,
 // stable in pair order; the shared expert (when present) is group E holding

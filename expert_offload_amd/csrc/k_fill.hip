@@ -7,6 +7,8 @@
 // same stream with no round trip through the host; 64 workgroups already keep
 // enough 16-byte reads in flight to saturate the link, leaving the other CUs
 // free.
+#include <hip/hip_ext.h>
+
 #include "eo_internal.h"
 
 namespace eo {
@@ -50,8 +52,10 @@ __global__ __launch_bounds__(256) void k_fill(const DevPlan* __restrict__ plan,
 }  // namespace
 
 hipError_t launch_fill(const DevPlan* plan, const uint8_t* pool_layer_dev, uint8_t* slots,
-                       uint64_t S, uint64_t S_pad, hipStream_t s) {
-    k_fill<<<kFillBlocks, 256, 0, s>>>(plan, pool_layer_dev, slots, S, S_pad);
+                       uint64_t S, uint64_t S_pad, hipStream_t s, hipEvent_t ev_start,
+                       hipEvent_t ev_stop) {
+    hipExtLaunchKernelGGL(k_fill, dim3(kFillBlocks), dim3(256), 0, s, ev_start, ev_stop, 0, plan,
+                          pool_layer_dev, slots, S, S_pad);
     return hipGetLastError();
 }
 

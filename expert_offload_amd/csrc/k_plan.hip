@@ -162,6 +162,9 @@ __global__ __launch_bounds__(kThreads) void k_plan(
             s_bh = st->bh;
             s_seq0 = st->seq;
         }
+        // one token: the first wavefront selects its experts from the logits
+        // while the table loads are in flight
+        if (rt.z && tid < 64) topk_token(rt.z, E, k, rt.forced, s_ids, s_w);
 #pragma unroll
         for (int i = 0; i < kMaxSlotsPerThread; ++i) {
             const int sl = tid + i * kThreads;
@@ -174,8 +177,6 @@ __global__ __launch_bounds__(kThreads) void k_plan(
     }
     for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
     if (tid == 0) s_err = 0;
-    if (rt.z && tid < 64)  // one token: select its experts from the logits
-        topk_token(rt.z, E, k, rt.forced, s_ids, s_w);
     __syncthreads();
     if (rt.z) {
         if (tid < k) {

@@ -199,6 +199,16 @@ __global__ __launch_bounds__(256) void k_entry(EntryArgs a) {
     const int H = a.H, nv = H / 8;
     const uint4* rv = (const uint4*)a.r_in;
     const bool writer = blockIdx.x == 0;
+    // this wavefront's expert: the first kPre steps of its router chain are
+    // loaded now, so their latency hides behind the residual and the norm
+    constexpr int kPre = 32;
+    const int e = blockIdx.x * 4 + wave;
+    const int J = H / 64, npre = min(J, kPre);  // J % 8 == 0
+    const float4* rq = (const float4*)a.Rt + (size_t)min(e, a.E - 1) * (J / 4) * 64 + lane;
+    float4 pre[kPre / 4];
+#pragma unroll
+    for (int q = 0; q < kPre / 4; ++q)
+        if (4 * q < npre) pre[q] = rq[(size_t)q * 64];
     float ss = 0.0f;
     for (int c = tid; c < nv; c += 256) {
         uint4 v = rv[c];
@@ -261,15 +271,23 @@ __global__ __launch_bounds__(256) void k_entry(EntryArgs a) {
         if (writer) ((uint4*)a.u)[c] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
     }
     __syncthreads();
-    const int e = blockIdx.x * 4 + wave;
     if (e >= a.E) return;
-    const int J = H / 64;
-    const float4* rq = (const float4*)a.Rt + (size_t)e * (J / 4) * 64 + lane;
     float acc = 0.0f;
-    if (J % 32 == 0)
-        acc = chain_dot<32>(rq, s_u, lane, J, acc);
-    else
-        acc = chain_dot<8>(rq, s_u, lane, J, acc);
+#pragma unroll
+    for (int q = 0; q < kPre / 4; ++q) {
+        if (4 * q < npre) {
+            acc = __builtin_fmaf(s_u[lane + 64 * (4 * q)], pre[q].x, acc);
+            acc = __builtin_fmaf(s_u[lane + 64 * (4 * q + 1)], pre[q].y, acc);
+            acc = __builtin_fmaf(s_u[lane + 64 * (4 * q + 2)], pre[q].z, acc);
+            acc = __builtin_fmaf(s_u[lane + 64 * (4 * q + 3)], pre[q].w, acc);
+        }
+    }
+    if (J > kPre) {
+        if ((J - kPre) % 32 == 0)
+            acc = chain_dot<32>(rq + (size_t)(kPre / 4) * 64, s_u + 64 * kPre, lane, J - kPre, acc);
+        else
+            acc = chain_dot<8>(rq + (size_t)(kPre / 4) * 64, s_u + 64 * kPre, lane, J - kPre, acc);
+    }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) acc = acc + __shfl_xor(acc, m, 64);
     if (lane == 0) a.z[e] = acc;

@@ -221,14 +221,16 @@ eo_status eo_last_plan(eo_engine* e, eo_plan_host* out);
  * [W_gate (I*H) | W_up (I*H) | W_down (H*I)]. Synchronous. */
 eo_status eo_dequant(eo_engine* e, int32_t layer, int32_t expert, float* out_host);
 eo_status eo_stats_get(eo_engine* e, eo_stats* out);
-/* Device time of the expert FFN kernels since the last reset, from HIP start/stop
- * events attached to each kernel launch on the compute stream while timing is
- * enabled (hipExtLaunchKernel: the events take the kernel's own start and end):
- * ms[0] decode GEMV gate/up kernel, ms[1] decode GEMV down kernel, ms[2] grouped
- * GEMM gate/up (+SwiGLU) kernel, ms[3] grouped GEMM down kernel (totals);
- * launches[0] decode GEMV pairs, launches[1] grouped GEMM pairs. Either pointer
- * may be NULL; reset != 0 clears after reading. Synchronises on the events. */
-eo_status eo_kernel_times(eo_engine* e, double* ms /*[4]*/, int64_t* launches /*[2]*/,
+/* Device time of the expert FFN and fill kernels since the last reset, from HIP
+ * start/stop events attached to each kernel launch on the compute stream while
+ * timing is enabled (hipExtLaunchKernel: the events take the kernel's own start
+ * and end; they are created without a system-scope fence so that they do not
+ * slow the kernels they time): ms[0] decode GEMV gate/up kernel, ms[1] decode
+ * GEMV down kernel, ms[2] grouped GEMM gate/up (+SwiGLU) kernel, ms[3] grouped
+ * GEMM down kernel, ms[4] fill kernel (totals); launches[0] decode GEMV pairs,
+ * launches[1] grouped GEMM pairs, launches[2] fill kernels. Either pointer may
+ * be NULL; reset != 0 clears after reading. Synchronises on the events. */
+eo_status eo_kernel_times(eo_engine* e, double* ms /*[5]*/, int64_t* launches /*[3]*/,
                           int32_t reset);
 /* Enable (1) or disable (0) the per-launch timing events behind eo_kernel_times. */
 eo_status eo_set_timing(eo_engine* e, int32_t enable);

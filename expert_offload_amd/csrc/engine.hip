@@ -789,9 +789,13 @@ eo_status eo_measure_bandwidth(eo_engine* e, uint32_t* bp_out, uint32_t* bh_out)
     std::vector<double> tp, th;
     for (int r = 0; r < reps + warm; ++r) {
         int id = (r * 7919) % n_exp;
-        const uint8_t* src = e->pool[id / e->E] + (uint64_t)(id % e->E) * e->S_pad;
+        const uint64_t off = (uint64_t)(id % e->E) * e->S_pad;
         HIPCHK(hipEventRecord(a, e->copy_stream));
-        HIPCHK(hipMemcpyAsync(dst, src, e->S, hipMemcpyHostToDevice, e->copy_stream));
+        if (e->fill_sdma)
+            HIPCHK(hipMemcpyAsync(dst, e->pool[id / e->E] + off, e->S, hipMemcpyHostToDevice,
+                                  e->copy_stream));
+        else  // the way fills are made: the fill kernel's copy over the pool's mapping
+            HIPCHK(launch_copy_expert(e->pool_dev[id / e->E] + off, dst, e->S, e->copy_stream));
         HIPCHK(hipEventRecord(b, e->copy_stream));
         HIPCHK(hipEventSynchronize(b));
         float ms = 0;

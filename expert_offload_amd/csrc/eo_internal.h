@@ -89,6 +89,10 @@ hipError_t launch_fill(const DevPlan* plan, const uint8_t* pool_layer_dev, uint8
                        uint64_t S, uint64_t S_pad, hipStream_t s, hipEvent_t ev_start = nullptr,
                        hipEvent_t ev_stop = nullptr);
 
+// One expert block from host (device-visible address) to device with the fill
+// kernel's copy (the B_P probe).
+hipError_t launch_copy_expert(const uint8_t* src_dev, uint8_t* dst, uint64_t S, hipStream_t s);
+
 // Permute: group the (token, k) pairs whose expert is resident by expert,
 // stable in pair order; the shared expert (when present) is group E holding
 // every token. Produces offsets [E+2], tile offsets, perm_pair, x_perm.

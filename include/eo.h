@@ -126,7 +126,9 @@ eo_status eo_set_shared_expert(eo_engine* e, int32_t layer, const void* host_blo
 /* Copy router weights R_l, fp32 [E, H] host, to the device. Synchronous. */
 eo_status eo_set_router(eo_engine* e, int32_t layer, const float* host_w);
 
-/* Measure B_P (one expert host->device copy into a cache slot) and B_H (the
+/* Measure B_P (one expert host->device copy into a cache slot, made the way
+ * fills are made: by the fill kernel, or by hipMemcpyAsync under EO_FILL_SDMA=1)
+ * and B_H (the
  * host-core expert routine over one expert at T = 1, with the engine's thread
  * count), each the median of several timed runs over different experts,
  * floored to integer MB/s, and use them for the miss split (zhichai.net

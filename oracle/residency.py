@@ -26,6 +26,18 @@ device implementation can match it bit for bit):
    empty and freed slots, in ascending slot index, go to the fills in rank
    order; each takes the new key and stamp = clock.
 6. The cache starts empty; prefill streaming does not touch it.
+
+Elastic resize (zhichai.net article, section 2, the elastic VRAM paragraph:
+the expert cache is a run-time quantity, rebuilt at scheduler safe points
+without restarting the engine or reloading weights). Reading, between two
+lookup calls, to a new capacity C':
+7. If more than C' experts are resident, the least recently used are evicted
+   in (stamp ascending, key ascending) order until C' remain.
+8. A survivor in a slot below C' stays there; the survivors in slots >= C',
+   in ascending order of their old slot, move to the empty slots below C' in
+   ascending order (a device-to-device copy, not a reload from the pool).
+9. Stamps, clock and credit are unchanged; slots C..C'-1 of a grown cache are
+   empty.
 """
 from __future__ import annotations
 
@@ -110,3 +122,30 @@ class Residency:
 
     def snapshot(self):
         return list(self.slot_key), list(self.slot_stamp), self.clock, self.credit
+
+    def resize(self, capacity: int):
+        """Resize to `capacity` slots; returns (evicted keys in eviction order,
+        moves [(old slot, new slot)] in order)."""
+        if capacity < 0:
+            raise ValueError("capacity >= 0")
+        occupied = [s for s in range(self.C) if self.slot_key[s] >= 0]
+        excess = max(0, len(occupied) - capacity)
+        victims = sorted(occupied, key=lambda s: (self.slot_stamp[s], self.slot_key[s]))[:excess]
+        evicted = [self.slot_key[s] for s in victims]
+        for s in victims:
+            self.slot_key[s] = -1
+        keep = {s: (self.slot_key[s], self.slot_stamp[s]) for s in range(self.C)
+                if self.slot_key[s] >= 0}
+        key = [-1] * capacity
+        stamp = [0] * capacity
+        for s, (k, t) in keep.items():
+            if s < capacity:
+                key[s], stamp[s] = k, t
+        movers = sorted(s for s in keep if s >= capacity)
+        holes = [s for s in range(capacity) if key[s] < 0]
+        moves = []
+        for s, d in zip(movers, holes):
+            key[d], stamp[d] = keep[s]
+            moves.append((s, d))
+        self.C, self.slot_key, self.slot_stamp = capacity, key, stamp
+        return evicted, moves

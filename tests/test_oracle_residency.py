@@ -161,3 +161,62 @@ def test_capacity_below_k_overflows_to_host():
     r = Residency(2, 1, 8, 1, 1)
     p = r.lookup_plan(0, [[0, 1, 2, 3]])
     assert p.q == 4 and p.q_fill == 2 and p.fills == [(0, 0), (1, 1)] and p.host == [2, 3]
+
+
+def test_resize_hand_worked():
+    # 1 layer, 8 experts, 4 slots, every miss filled
+    r = Residency(4, 1, 8, 1, 1)
+    for ids in ([[0]], [[1]], [[2]], [[3]], [[1]]):  # slots 0..3 <- 0,1,2,3; 1 touched again
+        r.lookup_plan(0, ids)
+    assert r.snapshot()[:2] == ([0, 1, 2, 3], [1, 5, 3, 4])
+    # shrink to 2: LRU order is key 0 (stamp 1), key 2 (3), key 3 (4), key 1 (5) -> evict 0, 2;
+    # survivors: key 1 in slot 1 stays, key 3 in slot 3 moves to the hole at slot 0
+    evicted, moves = r.resize(2)
+    assert evicted == [0, 2] and moves == [(3, 0)]
+    assert r.snapshot() == ([3, 1], [4, 5], 5, 0)
+    # grow to 5: everything stays, slots 2..4 empty; the next misses fill them in order
+    assert r.resize(5) == ([], [])
+    assert r.snapshot()[:2] == ([3, 1, -1, -1, -1], [4, 5, 0, 0, 0])
+    p = r.lookup_plan(0, [[6, 7]])
+    assert p.fills == [(6, 2), (7, 3)] and p.evicted == []
+
+
+def test_resize_keeps_the_most_recent_keys():
+    # brute force: after shrinking, the resident keys are the C' largest (stamp, key)
+    rng = np.random.default_rng(11)
+    r = Residency(24, 3, 16, 1, 1)
+    for _ in range(80):
+        l = int(rng.integers(0, 3))
+        r.lookup_plan(l, [list(rng.choice(16, size=3, replace=False))])
+    keys, stamps, clock, credit = r.snapshot()
+    before = {k: t for k, t in zip(keys, stamps) if k >= 0}
+    for cap in (20, 9, 1, 0):
+        evicted, moves = r.resize(cap)
+        keys, stamps, c2, cr2 = r.snapshot()
+        assert (c2, cr2) == (clock, credit) and len(keys) == cap
+        want = sorted(before, key=lambda k: (before[k], k))[-cap:] if cap else []
+        assert sorted(k for k in keys if k >= 0) == sorted(want)
+        assert all(before[k] == t for k, t in zip(keys, stamps) if k >= 0)
+        assert sorted(evicted) == sorted(set(before) - set(want))
+        before = {k: before[k] for k in want}
+        # moved blocks only go down into holes, and each source is a distinct old slot
+        assert all(d < cap <= s for s, d in moves)
+
+
+def test_resize_then_lookups_match_a_cache_built_at_that_size():
+    # shrinking to C' keeps the same recency order the smaller cache would have,
+    # so with every miss filled the resident sets agree from then on (LRU is a
+    # stack algorithm); slot positions may differ
+    rng = np.random.default_rng(5)
+    calls = [(int(rng.integers(0, 2)), [list(rng.choice(12, size=2, replace=False))])
+             for _ in range(120)]
+    a, b = Residency(16, 2, 12, 1, 1), Residency(6, 2, 12, 1, 1)
+    for l, ids in calls[:60]:
+        a.lookup_plan(l, ids)
+        b.lookup_plan(l, ids)
+    a.resize(6)
+    assert set(a.resident()) == set(b.resident())
+    for l, ids in calls[60:]:
+        pa, pb = a.lookup_plan(l, ids), b.lookup_plan(l, ids)
+        assert [e for e, _ in pa.hits] == [e for e, _ in pb.hits]
+        assert set(a.resident()) == set(b.resident())

@@ -82,6 +82,7 @@ _SIGS = {
     "eo_last_plan": [_P, ctypes.POINTER(eo_plan_host)],
     "eo_dequant": [_P, _I32, _I32, _P],
     "eo_stats_get": [_P, ctypes.POINTER(eo_stats)],
+    "eo_resize_cache": [_P, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
     "eo_kernel_times": [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64), _I32],
     "eo_set_timing": [_P, _I32],
     "eo_expert_bytes": [_I32, _I32, _I32],
@@ -237,6 +238,13 @@ def eo_last_plan(e) -> dict:
 
 def eo_dequant(e, layer, expert, out_host) -> None:
     _check(lib().eo_dequant(e, layer, expert, _ptr(out_host)))
+
+
+def eo_resize_cache(e, slots: int):
+    """Elastic resize between steps; returns (evicted, moved)."""
+    ne, nm = _I64(0), _I64(0)
+    _check(lib().eo_resize_cache(e, slots, ctypes.byref(ne), ctypes.byref(nm)))
+    return ne.value, nm.value
 
 
 def eo_stats_get(e) -> dict:

@@ -1035,6 +1035,94 @@ eo_status eo_set_capture(eo_engine* e, void* x_in, float* y, int32_t* ids, float
     return EO_OK;
 }
 
+eo_status eo_resize_cache(eo_engine* e, int64_t slots, int64_t* n_evicted, int64_t* n_moved) {
+    if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
+    if (slots < 0 || slots > plan_max_slots())
+        return fail(EO_ERR_INVALID_ARG, "slots out of range [0, 8192]");
+    if (e->plan_pending) return fail(EO_ERR_STATE, "a lookup plan is pending: resize between steps");
+    HIPCHK(hipSetDevice(e->cfg.device));
+    HIPCHK(hipDeviceSynchronize());
+    const int64_t C = e->C, Cn = slots;
+    std::vector<int32_t> key(C);
+    std::vector<int64_t> stamp(C);
+    if (C) {
+        HIPCHK(hipMemcpy(key.data(), e->d_slot_key, sizeof(int32_t) * C, hipMemcpyDeviceToHost));
+        HIPCHK(hipMemcpy(stamp.data(), e->d_slot_stamp, sizeof(int64_t) * C, hipMemcpyDeviceToHost));
+    }
+    // least recently used first: (stamp asc, key asc)
+    std::vector<int64_t> occ;
+    for (int64_t i = 0; i < C; ++i)
+        if (key[i] >= 0) occ.push_back(i);
+    std::sort(occ.begin(), occ.end(), [&](int64_t a, int64_t b) {
+        return stamp[a] != stamp[b] ? stamp[a] < stamp[b] : key[a] < key[b];
+    });
+    const int64_t excess = std::max<int64_t>(0, (int64_t)occ.size() - Cn);
+    std::vector<int32_t> nkey(Cn, -1);
+    std::vector<int64_t> nstamp(Cn, 0);
+    std::vector<char> evict(C, 0);
+    for (int64_t i = 0; i < excess; ++i) evict[occ[i]] = 1;
+    std::vector<std::pair<int64_t, int64_t>> moves;  // (old slot, new slot)
+    std::vector<int64_t> movers;
+    for (int64_t i = 0; i < C; ++i) {
+        if (key[i] < 0 || evict[i]) continue;
+        if (i < Cn) {
+            nkey[i] = key[i];
+            nstamp[i] = stamp[i];
+        } else {
+            movers.push_back(i);
+        }
+    }
+    int64_t hole = 0;
+    for (int64_t src : movers) {  // ascending old slot -> ascending holes below Cn
+        while (nkey[hole] >= 0) ++hole;
+        nkey[hole] = key[src];
+        nstamp[hole] = stamp[src];
+        moves.push_back({src, hole});
+    }
+    // new device storage first, so that a failed allocation leaves the engine as it was
+    uint8_t* nslots = nullptr;
+    int32_t* nd_key = nullptr;
+    int64_t* nd_stamp = nullptr;
+    eo_status st = dmalloc(&nslots, (uint64_t)Cn * e->S_pad);
+    if (st == EO_OK) st = dmalloc(&nd_key, sizeof(int32_t) * std::max<int64_t>(Cn, 1));
+    if (st == EO_OK) st = dmalloc(&nd_stamp, sizeof(int64_t) * std::max<int64_t>(Cn, 1));
+    if (st != EO_OK) {
+        if (nslots) (void)hipFree(nslots);
+        if (nd_key) (void)hipFree(nd_key);
+        return st;
+    }
+    std::vector<int32_t> k2s((size_t)e->L * e->E);
+    HIPCHK(hipMemcpy(k2s.data(), e->d_key2slot, sizeof(int32_t) * k2s.size(), hipMemcpyDeviceToHost));
+    for (int64_t i = 0; i < Cn; ++i) {
+        if (nkey[i] < 0) continue;
+        int64_t src = i;  // where this block lives now
+        for (auto& m : moves)
+            if (m.second == i) src = m.first;
+        HIPCHK(hipMemcpy(nslots + (uint64_t)i * e->S_pad, e->d_slots + (uint64_t)src * e->S_pad, e->S,
+                         hipMemcpyDeviceToDevice));
+        k2s[nkey[i]] = (int32_t)i;
+    }
+    for (int64_t i = 0; i < C; ++i)
+        if (evict[i]) k2s[key[i]] = -1;
+    if (Cn) {
+        HIPCHK(hipMemcpy(nd_key, nkey.data(), sizeof(int32_t) * Cn, hipMemcpyHostToDevice));
+        HIPCHK(hipMemcpy(nd_stamp, nstamp.data(), sizeof(int64_t) * Cn, hipMemcpyHostToDevice));
+    }
+    HIPCHK(hipMemcpy(e->d_key2slot, k2s.data(), sizeof(int32_t) * k2s.size(), hipMemcpyHostToDevice));
+    HIPCHK(hipDeviceSynchronize());
+    (void)hipFree(e->d_slots);
+    (void)hipFree(e->d_slot_key);
+    (void)hipFree(e->d_slot_stamp);
+    e->d_slots = nslots;
+    e->d_slot_key = nd_key;
+    e->d_slot_stamp = nd_stamp;
+    e->C = Cn;
+    e->cfg.cache_slots = Cn;
+    if (n_evicted) *n_evicted = excess;
+    if (n_moved) *n_moved = (int64_t)moves.size();
+    return EO_OK;
+}
+
 eo_status eo_cache_snapshot(eo_engine* e, int32_t* slot_key, int64_t* slot_stamp, int64_t* clock,
                             int64_t* credit) {
     if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");

@@ -213,6 +213,19 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t double_buff
 eo_status eo_set_capture(eo_engine* e, void* x_in, float* y, int32_t* ids, float* w,
                          int32_t tokens_per_layer);
 
+/* Elastic cache resize (zhichai.net article, section 2, the elastic VRAM
+ * paragraph: the expert cache is a run-time quantity, rebuilt at scheduler safe
+ * points without restarting the engine or reloading weights from the pool).
+ * Call between steps (no pending lookup plan: EO_ERR_STATE otherwise); waits for
+ * the device. New capacity `slots` in [0, 8192]. If more experts are resident
+ * than `slots`, the least recently used are evicted in (stamp asc, key asc)
+ * order; survivors in slots below the new capacity stay, the others move, in
+ * ascending old slot order, to the lowest empty slots (device-to-device
+ * copies). Stamps, clock and credit are kept. The slot memory is reallocated at
+ * the new size (the old block is freed after the copies; both exist during the
+ * call); on EO_ERR_OOM the engine is unchanged. n_evicted / n_moved may be NULL. */
+eo_status eo_resize_cache(eo_engine* e, int64_t slots, int64_t* n_evicted, int64_t* n_moved);
+
 /* ---- introspection ---- */
 /* Slot table and counters (host buffers of C entries each). Synchronous. */
 eo_status eo_cache_snapshot(eo_engine* e, int32_t* slot_key, int64_t* slot_stamp, int64_t* clock,

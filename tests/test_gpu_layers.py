@@ -290,6 +290,59 @@ def test_decode_routed_ids_bit_exact():
             check_layer(shape, seed, l, xin[l], ys[l], ids[l])
 
 
+def test_elastic_resize_between_steps():
+    # shrink and grow the cache between decode steps: the slot table must follow
+    # the oracle's resize bit for bit and the moved experts must still compute
+    shape = small_shape("mxfp4", layers=3)
+    seed = 15
+    L, k, H = shape.layers, shape.top_k, shape.hidden
+    C0 = 20
+    e = make_engine(shape, seed, cache_slots=C0, max_tokens=1)
+    try:
+        eo.eo_set_bandwidth(e, 7, 7)  # every miss filled: the cache churns
+        res = Residency(C0, L, shape.experts, 7, 7)
+        trace = synth.sticky_zipf_trace(seed, 12, L, shape.experts, k)
+        cx = torch.zeros((L, 1, H), dtype=torch.int16, device="cuda")
+        cy = torch.zeros((L, 1, H), dtype=torch.float32, device="cuda")
+        ci = torch.zeros((L, 1, k), dtype=torch.int32, device="cuda")
+        cw = torch.zeros((L, 1, k), dtype=torch.float32, device="cuda")
+        eo.eo_set_capture(e, cx, cy, ci, cw, 1)
+
+        def check_state(C):
+            keys = np.zeros(max(C, 1), dtype=np.int32)
+            stamps = np.zeros(max(C, 1), dtype=np.int64)
+            clock, credit = eo.eo_cache_snapshot(e, keys, stamps)
+            rk, rs, rc, rcr = res.snapshot()
+            assert list(keys[:C]) == rk and list(stamps[:C]) == rs and (clock, credit) == (rc, rcr)
+
+        for s, C in enumerate([None, None, None, 8, None, None, 3, None, 30, None, None, 0]):
+            if C is not None:
+                ne, nm = eo.eo_resize_cache(e, C)
+                ev, mv = res.resize(C)
+                assert (ne, nm) == (len(ev), len(mv)), s
+                check_state(C)
+            x = synth.activations(seed, 800 + s, 1, H, 1.0, True)
+            eo.eo_decode_step(e, dev(x.view(np.int16)), 1, dev(trace[s].reshape(L, 1, k)), _stream())
+            torch.cuda.synchronize()
+            for l in range(L):
+                res.lookup_plan(l, trace[s, l][None, :])
+            check_state(res.C)
+            xin = cx.cpu().numpy().view(np.uint16)
+            ys, ws = cy.cpu().numpy(), cw.cpu().numpy()
+            for l in range(L):
+                xf = synth.bf16_bits_to_f32(xin[l])
+                R = synth.router_weights(seed, l, shape.experts, H)
+                ids, w, _ = OR.route(xf, R, k, trace[s, l][None, :])
+                assert rel_err(ys[l], oracle_layer(shape, seed, l, xf, ids, w)) <= TOL, (s, l)
+        # not between steps: a pending plan blocks the resize
+        eo.eo_lookup_plan(e, 0, dev(trace[0, 0][None, :].astype(np.int32)), 1, _stream())
+        with pytest.raises(eo.EOError) as ei:
+            eo.eo_resize_cache(e, 4)
+        assert ei.value.status == eo.EO_ERR_STATE
+    finally:
+        eo.eo_destroy(e)
+
+
 def test_decode_determinism():
     shape = small_shape("bf16", layers=2)
     outs = []

@@ -210,8 +210,11 @@ def eo_decode_step(e, x_inout, T, forced_ids=None, stream=None) -> None:
     _check(lib().eo_decode_step(e, _ptr(x_inout), T, _ptr(forced_ids), _stream(stream)))
 
 
-def eo_prefill(e, x_inout, T, double_buffer=1, stream=None) -> None:
-    _check(lib().eo_prefill(e, _ptr(x_inout), T, double_buffer, _stream(stream)))
+EO_PREFILL_DOUBLE_BUFFER, EO_PREFILL_SKIP_RESIDENT = 1, 2
+
+
+def eo_prefill(e, x_inout, T, flags=EO_PREFILL_DOUBLE_BUFFER, stream=None) -> None:
+    _check(lib().eo_prefill(e, _ptr(x_inout), T, flags, _stream(stream)))
 
 
 def eo_set_capture(e, x_in, y, ids, w, tokens_per_layer) -> None:

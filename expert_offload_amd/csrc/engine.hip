@@ -109,6 +109,8 @@ struct eo_engine {
     float* d_opairs = nullptr;
 
     uint8_t* d_staging[2] = {nullptr, nullptr};
+    const uint8_t** d_gbase = nullptr;  // [L][E] weight bases of a resident-aware prefill
+    size_t gbase_n = 0;
     hipStream_t copy_stream = nullptr;
     hipEvent_t ev_fill = nullptr, ev_copy[2] = {nullptr, nullptr}, ev_comp[2] = {nullptr, nullptr};
     hipEvent_t ev_start = nullptr;
@@ -545,7 +547,7 @@ void destroy_all(eo_engine* e) {
     fr(e->d_y); fr(e->d_u); fr(e->d_r); fr(e->d_hgemv); fr(e->d_yparts); fr(e->d_yhost);
     fr(e->pb.counts); fr(e->pb.offsets); fr(e->pb.tile_off); fr(e->pb.perm_pair);
     fr(e->pb.chunk_cnt); fr(e->pb.x_perm); fr(e->d_hbuf); fr(e->d_opairs);
-    fr(e->d_staging[0]); fr(e->d_staging[1]);
+    fr(e->d_staging[0]); fr(e->d_staging[1]); fr((void*)e->d_gbase);
     fh(e->h_plan); fh(e->h_ids); fh(e->h_w); fh(e->h_x); fh(e->h_yhost);
     if (e->copy_stream) (void)hipStreamDestroy(e->copy_stream);
     for (hipEvent_t ev : {e->ev_fill, e->ev_copy[0], e->ev_copy[1], e->ev_comp[0], e->ev_comp[1],
@@ -944,10 +946,14 @@ eo_status eo_decode_step(eo_engine* e, void* x_inout, int32_t T, const int32_t* 
     return EO_OK;
 }
 
-eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t double_buffer, void* stream) {
+eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t flags, void* stream) {
     if (!e || !x_inout) return fail(EO_ERR_INVALID_ARG, "null argument");
     EOCHK(check_T(e, T));
     if (!aligned16(x_inout)) return fail(EO_ERR_INVALID_ARG, "x must be 16-byte aligned");
+    if (flags & ~(EO_PREFILL_DOUBLE_BUFFER | EO_PREFILL_SKIP_RESIDENT))
+        return fail(EO_ERR_INVALID_ARG, "unknown prefill flags");
+    const bool double_buffer = flags & EO_PREFILL_DOUBLE_BUFFER;
+    const bool skip = (flags & EO_PREFILL_SKIP_RESIDENT) && e->C > 0;
     hipStream_t s = (hipStream_t)stream;
     HIPCHK(hipSetDevice(e->cfg.device));
     const uint64_t layer_bytes = (uint64_t)e->E * e->S_pad;
@@ -956,10 +962,59 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t double_buff
     EOCHK(ensure_gemm(e, T, s));
     const size_t xb = (size_t)T * e->H * e->act_size;
     const bool cap = e->cap_y && T <= e->cap_T;
+    // Resident-aware streaming: experts resident in the cache are read from
+    // their slots, only the others are streamed; prefill does not change the
+    // cache, so the residency read once here holds for the whole call.
+    std::vector<int32_t> k2s;
+    if (skip) {
+        HIPCHK(hipStreamSynchronize(s));
+        k2s.resize((size_t)e->L * e->E);
+        HIPCHK(hipMemcpy(k2s.data(), e->d_key2slot, sizeof(int32_t) * k2s.size(), hipMemcpyDeviceToHost));
+        std::vector<const uint8_t*> gb(k2s.size());
+        for (int l = 0; l < e->L; ++l)
+            for (int g = 0; g < e->E; ++g) {
+                const int32_t sl = k2s[(size_t)l * e->E + g];
+                gb[(size_t)l * e->E + g] = sl >= 0 ? e->d_slots + (uint64_t)sl * e->S_pad
+                                                   : e->d_staging[l & 1] + (uint64_t)g * e->S_pad;
+            }
+        if (e->gbase_n < gb.size()) {
+            if (e->d_gbase) (void)hipFree(e->d_gbase);
+            e->d_gbase = nullptr;
+            e->gbase_n = 0;
+            EOCHK(dmalloc(&e->d_gbase, sizeof(const uint8_t*) * gb.size()));
+            e->gbase_n = gb.size();
+        }
+        HIPCHK(hipMemcpy(e->d_gbase, gb.data(), sizeof(const uint8_t*) * gb.size(), hipMemcpyHostToDevice));
+    }
+    int64_t streamed = 0;
+    // layer l's experts into staging buffer `buf` on the copy stream (runs of
+    // consecutive non-resident experts when skipping)
+    auto copy_layer = [&](int l, int buf) -> eo_status {
+        if (!skip) {
+            HIPCHK(hipMemcpyAsync(e->d_staging[buf], e->pool[l], layer_bytes, hipMemcpyHostToDevice,
+                                  e->copy_stream));
+            streamed += (int64_t)layer_bytes;
+            return EO_OK;
+        }
+        for (int g = 0; g < e->E;) {
+            if (k2s[(size_t)l * e->E + g] >= 0) {
+                ++g;
+                continue;
+            }
+            int g1 = g;
+            while (g1 < e->E && k2s[(size_t)l * e->E + g1] < 0) ++g1;
+            const uint64_t off = (uint64_t)g * e->S_pad, n = (uint64_t)(g1 - g) * e->S_pad;
+            HIPCHK(hipMemcpyAsync(e->d_staging[buf] + off, e->pool[l] + off, n, hipMemcpyHostToDevice,
+                                  e->copy_stream));
+            streamed += (int64_t)n;
+            g = g1;
+        }
+        return EO_OK;
+    };
     // the first copy must not overwrite staging still read by earlier work on s
     HIPCHK(hipEventRecord(e->ev_start, s));
     HIPCHK(hipStreamWaitEvent(e->copy_stream, e->ev_start, 0));
-    HIPCHK(hipMemcpyAsync(e->d_staging[0], e->pool[0], layer_bytes, hipMemcpyHostToDevice, e->copy_stream));
+    EOCHK(copy_layer(0, 0));
     HIPCHK(hipEventRecord(e->ev_copy[0], e->copy_stream));
     for (int l = 0; l < e->L; ++l) {
         const int b = l & 1, nb = b ^ 1;
@@ -967,8 +1022,7 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t double_buff
         if (double_buffer && l + 1 < e->L) {
             // buffer nb was last read by layer l-1's compute
             if (l >= 1) HIPCHK(hipStreamWaitEvent(e->copy_stream, e->ev_comp[nb], 0));
-            HIPCHK(hipMemcpyAsync(e->d_staging[nb], e->pool[l + 1], layer_bytes,
-                                  hipMemcpyHostToDevice, e->copy_stream));
+            EOCHK(copy_layer(l + 1, nb));
             HIPCHK(hipEventRecord(e->ev_copy[nb], e->copy_stream));
         }
         int32_t* ids = e->d_ids;
@@ -998,6 +1052,7 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t double_buff
             gw.e2slot = nullptr;
             gw.stride = e->S_pad;
             gw.shared_w = e->shared ? e->d_shared + (uint64_t)l * e->S_pad : nullptr;
+            gw.gbase = skip ? e->d_gbase + (size_t)l * e->E : nullptr;
             he = launch_ffn_gemm(e->fmt, e->lay, gw, e->E, e->shared, e->H, e->I, T * e->k + T,
                                  e->pb.offsets, e->pb.tile_off, e->pb.x_perm, e->d_hbuf,
                                  e->pb.perm_pair, ids, w, e->k, T, e->d_opairs, s,
@@ -1011,13 +1066,12 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t double_buff
         HIPCHK(hipEventRecord(e->ev_comp[b], s));
         if (!double_buffer && l + 1 < e->L) {
             HIPCHK(hipStreamWaitEvent(e->copy_stream, e->ev_comp[b], 0));
-            HIPCHK(hipMemcpyAsync(e->d_staging[nb], e->pool[l + 1], layer_bytes,
-                                  hipMemcpyHostToDevice, e->copy_stream));
+            EOCHK(copy_layer(l + 1, nb));
             HIPCHK(hipEventRecord(e->ev_copy[nb], e->copy_stream));
         }
     }
     e->stats.prefill_layers += e->L;
-    e->stats.pcie_bytes += (int64_t)layer_bytes * e->L;
+    e->stats.pcie_bytes += streamed;
     if (e->timing) EOCHK(harvest_times(e));
     return EO_OK;
 }

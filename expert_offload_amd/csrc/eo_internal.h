@@ -115,6 +115,7 @@ struct GroupW {
     const int32_t* e2slot;  // null: group g lives at slots + g*stride
     uint64_t stride;
     const uint8_t* shared_w;
+    const uint8_t* const* gbase = nullptr;  // when set: group g (< E) lives at gbase[g]
 };
 hipError_t launch_ffn_gemm(int fmt, const Layout& lay, GroupW gw, int E, int has_shared, int H,
                            int I, int P_max, const int32_t* offsets, const int32_t* tile_off,

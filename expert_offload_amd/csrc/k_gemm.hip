@@ -66,6 +66,7 @@ __device__ __forceinline__ int find_group(const int32_t* tile_off, int G, int ti
 
 __device__ __forceinline__ const uint8_t* group_base(const GroupW& gw, int g, int E) {
     if (g == E) return gw.shared_w;
+    if (gw.gbase) return gw.gbase[g];
     int s = gw.e2slot ? gw.e2slot[g] : g;
     return gw.slots + (uint64_t)s * gw.stride;
 }

@@ -199,12 +199,17 @@ eo_status eo_decode_step(eo_engine* e, void* x_inout, int32_t T, const int32_t* 
                          void* stream);
 
 /* Prefill of T tokens (T <= max_tokens) through all layers, in place (the
- * same residual stream and normalisation as eo_decode_step), with
- * full-layer double-buffered streaming of each layer's E experts from the
- * pool (the cache is neither read nor updated). double_buffer = 0 serialises
- * copy and compute (ablation). */
-eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t double_buffer,
-                     void* stream);
+ * same residual stream and normalisation as eo_decode_step), with full-layer
+ * double-buffered streaming of each layer's E experts from the pool (zhichai.net
+ * article, section 2, Prefill paragraph); the cache is not updated. flags:
+ * EO_PREFILL_DOUBLE_BUFFER overlaps layer l+1's copy with layer l's compute
+ * (0: serialised, the ablation); EO_PREFILL_SKIP_RESIDENT streams only the
+ * experts that are not resident in the cache and reads the resident ones from
+ * their slots (waits for `stream` once to read the residency). Other bits:
+ * EO_ERR_INVALID_ARG. */
+#define EO_PREFILL_DOUBLE_BUFFER 1
+#define EO_PREFILL_SKIP_RESIDENT 2
+eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t flags, void* stream);
 
 /* Optional per-layer capture for tests, device buffers written by
  * eo_decode_step / eo_prefill (NULL disables): x_in [L, T, H] layer inputs u_l

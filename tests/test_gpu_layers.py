@@ -343,6 +343,50 @@ def test_elastic_resize_between_steps():
         eo.eo_destroy(e)
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "nvfp4"])
+def test_prefill_skipping_resident_experts(fmt):
+    # resident-aware streaming reads cached experts from their slots and streams
+    # only the rest: the same result bit for bit, fewer bytes over PCIe, and the
+    # cache untouched
+    shape = small_shape(fmt, layers=3)
+    seed = 16
+    L, k, H, T = shape.layers, shape.top_k, shape.hidden, 300
+    e = make_engine(shape, seed, cache_slots=22, max_tokens=T)
+    try:
+        eo.eo_set_bandwidth(e, 5, 5)
+        tr = synth.sticky_zipf_trace(seed, 6, L, shape.experts, k)
+        for s in range(6):
+            xd = dev(synth.activations(seed, 900 + s, 1, H, 1.0, True).view(np.int16))
+            eo.eo_decode_step(e, xd, 1, dev(tr[s].reshape(L, 1, k)), _stream())
+        torch.cuda.synchronize()
+        keys = np.zeros(22, dtype=np.int32)
+        stamps = np.zeros(22, dtype=np.int64)
+        before = eo.eo_cache_snapshot(e, keys, stamps), keys.copy(), stamps.copy()
+        n_res = int((keys >= 0).sum())
+        assert n_res > 0
+        S_pad = (synth.expert_bytes(H, shape.inter, shape.fmt) + 4095) // 4096 * 4096
+        x = synth.activations(seed, 950, T, H, 1.0, True)
+        outs = []
+        for flags in (1, 3, 2):
+            xd = dev(x.view(np.int16))
+            b0 = eo.eo_stats_get(e)["pcie_bytes"]
+            eo.eo_prefill(e, xd, T, flags, _stream())
+            torch.cuda.synchronize()
+            outs.append((xd.cpu().numpy().tobytes(), eo.eo_stats_get(e)["pcie_bytes"] - b0))
+        assert outs[0][0] == outs[1][0] == outs[2][0]
+        assert outs[0][1] == L * shape.experts * S_pad
+        assert outs[1][1] == outs[2][1] == (L * shape.experts - n_res) * S_pad
+        keys2 = np.zeros(22, dtype=np.int32)
+        stamps2 = np.zeros(22, dtype=np.int64)
+        after = eo.eo_cache_snapshot(e, keys2, stamps2)
+        assert after == before[0] and np.array_equal(keys2, before[1]) and \
+            np.array_equal(stamps2, before[2])
+        with pytest.raises(eo.EOError):
+            eo.eo_prefill(e, dev(x.view(np.int16)), T, 4, _stream())
+    finally:
+        eo.eo_destroy(e)
+
+
 def test_decode_determinism():
     shape = small_shape("bf16", layers=2)
     outs = []

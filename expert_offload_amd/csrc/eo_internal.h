@@ -26,6 +26,7 @@ struct DevPlan {
     int32_t fill_e[kMaxE], fill_slot[kMaxE];
     int32_t host_e[kMaxE];
     int32_t evict_key[kMaxE];
+    int32_t tok_slot[kMaxK];  // one-token plans: slot of the token's j-th expert, -1 if not resident
 };
 
 // Residency state in device memory.
@@ -138,6 +139,8 @@ struct GemvExperts {
     const uint8_t* base[kMaxK + 1];
     float w[kMaxK + 1];
 };
+// Without ex, a one-token plan's weight bases come from plan->tok_slot (one
+// load) rather than from ids and e2slot.
 hipError_t launch_ffn_gemv(int fmt, const Layout& lay, GroupW gw, const DevPlan* plan,
                            const int32_t* ids, const float* w, int k, int E, int has_shared,
                            int H, int I, const void* x, int act_bf16, float* h_buf,

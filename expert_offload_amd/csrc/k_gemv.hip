@@ -140,9 +140,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ const uint8_t* expert_base(const GemvArgs& a, int j) {
     if (a.ex.valid) return a.ex.base[j];
     if (j == a.k) return a.gw.shared_w;
-    int e = a.ids[j];
-    if (e < 0 || e >= a.E) return nullptr;
-    int s = a.plan->e2slot[e];
+    const int s = a.plan->tok_slot[j];
     if (s < 0) return nullptr;
     return a.gw.slots + (uint64_t)s * a.gw.stride;
 }

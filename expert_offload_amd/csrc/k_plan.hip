@@ -201,6 +201,7 @@ __global__ __launch_bounds__(kThreads) void k_plan(
     }
     __syncthreads();
     if (s_err) {
+        if (tid < kMaxK) dp->tok_slot[tid] = -1;  // nothing resident for this token
         if (tid == 0) {
             int seq = s_seq0 + 1;
             st->seq = seq;
@@ -338,6 +339,7 @@ __global__ __launch_bounds__(kThreads) void k_plan(
         dp->e2slot[e] = slot_of[e];
         dp->count[e] = cnt[e];
     }
+    if (T == 1 && tid < k) dp->tok_slot[tid] = slot_of[ids[tid]];
     const int n_hit = s_h, n_host = s_m - q_fill, n_evict = n_ev;
     if (tid == 0) {
         dp->pad = 0;

@@ -68,6 +68,7 @@ _SIGS = {
     "eo_set_shared_expert": [_P, _I32, _P, _U64],
     "eo_set_router": [_P, _I32, _P],
     "eo_measure_bandwidth": [_P, ctypes.POINTER(_U32), ctypes.POINTER(_U32)],
+    "eo_remeasure_bandwidth": [_P, ctypes.POINTER(_U32), ctypes.POINTER(_U32)],
     "eo_set_bandwidth": [_P, _U32, _U32],
     "eo_route": [_P, _I32, _P, _I32, _P, _P, _P, _P],
     "eo_lookup_plan": [_P, _I32, _P, _I32, _P],
@@ -173,6 +174,12 @@ def eo_set_router(e: int, layer: int, host_w) -> None:
 def eo_measure_bandwidth(e: int):
     bp, bh = _U32(), _U32()
     _check(lib().eo_measure_bandwidth(e, ctypes.byref(bp), ctypes.byref(bh)))
+    return bp.value, bh.value
+
+
+def eo_remeasure_bandwidth(e: int):
+    bp, bh = _U32(), _U32()
+    _check(lib().eo_remeasure_bandwidth(e, ctypes.byref(bp), ctypes.byref(bh)))
     return bp.value, bh.value
 
 

@@ -773,13 +773,17 @@ eo_status eo_set_bandwidth(eo_engine* e, uint32_t bp_mbps, uint32_t bh_mbps) {
     return EO_OK;
 }
 
-eo_status eo_measure_bandwidth(eo_engine* e, uint32_t* bp_out, uint32_t* bh_out) {
+// B_P and B_H probes. keep_cache: copy into a scratch buffer and keep the
+// cache, clock and (clamped) credit; else copy into slot 0 and reset the cache.
+static eo_status measure_impl(eo_engine* e, bool keep_cache, uint32_t* bp_out, uint32_t* bh_out) {
     if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
+    if (keep_cache && e->plan_pending)
+        return fail(EO_ERR_STATE, "a lookup plan is pending: re-measure between steps");
     HIPCHK(hipSetDevice(e->cfg.device));
     HIPCHK(hipDeviceSynchronize());
     uint8_t* dst = e->d_slots;
     uint8_t* tmp = nullptr;
-    if (e->C == 0) {
+    if (e->C == 0 || keep_cache) {
         EOCHK(dmalloc(&tmp, e->S));
         dst = tmp;
     }
@@ -850,12 +854,24 @@ eo_status eo_measure_bandwidth(eo_engine* e, uint32_t* bp_out, uint32_t* bh_out)
     double bp = (double)e->S / tp[tp.size() / 2] / 1e6, bh = (double)e->S / th[th.size() / 2] / 1e6;
     uint32_t bpi = (uint32_t)std::max(1.0, std::min(2e9, bp));
     uint32_t bhi = (uint32_t)std::max(1.0, std::min(2e9, bh));
-    e->bp = bpi;
-    e->bh = bhi;
-    EOCHK(reset_cache(e));
+    if (keep_cache) {
+        EOCHK(eo_set_bandwidth(e, bpi, bhi));
+    } else {
+        e->bp = bpi;
+        e->bh = bhi;
+        EOCHK(reset_cache(e));
+    }
     if (bp_out) *bp_out = bpi;
     if (bh_out) *bh_out = bhi;
     return EO_OK;
+}
+
+eo_status eo_measure_bandwidth(eo_engine* e, uint32_t* bp_out, uint32_t* bh_out) {
+    return measure_impl(e, false, bp_out, bh_out);
+}
+
+eo_status eo_remeasure_bandwidth(eo_engine* e, uint32_t* bp_out, uint32_t* bh_out) {
+    return measure_impl(e, true, bp_out, bh_out);
 }
 
 eo_status eo_route(eo_engine* e, int32_t layer, const void* x, int32_t T, const int32_t* forced_ids,

@@ -137,6 +137,13 @@ eo_status eo_set_router(eo_engine* e, int32_t layer, const float* host_w);
  * and the split credit to 0. Either output pointer may be NULL. */
 eo_status eo_measure_bandwidth(eo_engine* e, uint32_t* bp_mbps, uint32_t* bh_mbps);
 
+/* The same probes while serving (B_P and B_H change at run time on a shared
+ * machine; the split is re-derived from the next lookup on): the copy goes to a
+ * scratch buffer, the cache, clock and stamps are kept and the credit is
+ * clamped below the new B_H, as eo_set_bandwidth does. Call between steps
+ * (EO_ERR_STATE with a pending lookup plan). Either output pointer may be NULL. */
+eo_status eo_remeasure_bandwidth(eo_engine* e, uint32_t* bp_mbps, uint32_t* bh_mbps);
+
 /* Set B_P and B_H (MB/s, both > 0) directly; clips the credit below B_H. */
 eo_status eo_set_bandwidth(eo_engine* e, uint32_t bp_mbps, uint32_t bh_mbps);
 

@@ -387,6 +387,43 @@ def test_prefill_skipping_resident_experts(fmt):
         eo.eo_destroy(e)
 
 
+def test_remeasure_bandwidth_keeps_the_cache():
+    # online re-measurement between steps: residency, stamps and clock kept,
+    # credit clamped, and the following plans use the new split
+    shape = small_shape("bf16", layers=2)
+    seed = 17
+    L, k, H = shape.layers, shape.top_k, shape.hidden
+    e = make_engine(shape, seed, cache_slots=9, max_tokens=1)
+    try:
+        eo.eo_set_bandwidth(e, 3, 11)
+        res = Residency(9, L, shape.experts, 3, 11)
+        tr = synth.sticky_zipf_trace(seed, 8, L, shape.experts, k)
+        for s in range(8):
+            if s == 4:
+                keys0 = np.zeros(9, dtype=np.int32)
+                stamps0 = np.zeros(9, dtype=np.int64)
+                clock0, _ = eo.eo_cache_snapshot(e, keys0, stamps0)
+                bp, bh = eo.eo_remeasure_bandwidth(e)
+                assert bp > 0 and bh > 0
+                res.set_bandwidth(bp, bh)
+                keys = np.zeros(9, dtype=np.int32)
+                stamps = np.zeros(9, dtype=np.int64)
+                clock, credit = eo.eo_cache_snapshot(e, keys, stamps)
+                assert np.array_equal(keys, keys0) and np.array_equal(stamps, stamps0)
+                assert clock == clock0 and credit == res.credit < bh
+            xd = dev(synth.activations(seed, 990 + s, 1, H, 1.0, True).view(np.int16))
+            eo.eo_decode_step(e, xd, 1, dev(tr[s].reshape(L, 1, k)), _stream())
+            torch.cuda.synchronize()
+            for l in range(L):
+                res.lookup_plan(l, tr[s, l][None, :])
+            keys = np.zeros(9, dtype=np.int32)
+            stamps = np.zeros(9, dtype=np.int64)
+            assert eo.eo_cache_snapshot(e, keys, stamps) == (res.clock, res.credit)
+            assert list(keys) == res.snapshot()[0] and list(stamps) == res.snapshot()[1]
+    finally:
+        eo.eo_destroy(e)
+
+
 def test_decode_determinism():
     shape = small_shape("bf16", layers=2)
     outs = []

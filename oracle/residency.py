@@ -38,6 +38,14 @@ lookup calls, to a new capacity C':
    ascending order (a device-to-device copy, not a reload from the pool).
 9. Stamps, clock and credit are unchanged; slots C..C'-1 of a grown cache are
    empty.
+
+Static placements, for the placement-policy comparison (zhichai.net article,
+section 2, LRU paragraph: the same routing trace replayed under the global LRU,
+under a placement fixed from prefill routing, and under a routing-blind static
+split). Reading: a static placement puts the given keys in slots 0..n-1 (stamp
+0, the rest empty) and freezes the cache: lookups still count hits, stamp them
+and run the credit split, but nothing is filled or evicted (q_fill = 0), so
+every miss runs on the host. Clearing it returns to the LRU from that state.
 """
 from __future__ import annotations
 
@@ -69,6 +77,7 @@ class Residency:
         self.slot_stamp = [0] * capacity
         self.clock = 0
         self.credit = 0
+        self.frozen = False
 
     def set_bandwidth(self, bp_mbps: int, bh_mbps: int) -> None:
         self.bp, self.bh = int(bp_mbps), int(bh_mbps)
@@ -97,7 +106,7 @@ class Residency:
 
         q = min(m, (self.credit + m * self.bp) // self.bh)
         self.credit = min(self.credit + m * self.bp - q * self.bh, self.bh - 1)
-        q_fill = min(q, self.C - h)
+        q_fill = 0 if self.frozen else min(q, self.C - h)
 
         ranked = sorted(misses, key=lambda e: (-counts[e], e))
         fill_experts, host = ranked[:q_fill], ranked[q_fill:]
@@ -149,3 +158,16 @@ class Residency:
             moves.append((s, d))
         self.C, self.slot_key, self.slot_stamp = capacity, key, stamp
         return evicted, moves
+
+    def set_static(self, keys) -> None:
+        """Static placement: keys in slots 0..n-1 (stamp 0), cache frozen."""
+        keys = [int(k) for k in keys]
+        if len(keys) > self.C or len(set(keys)) != len(keys) or \
+                any(k < 0 or k >= self.L * self.E for k in keys):
+            raise ValueError("at most C distinct keys in range")
+        self.slot_key = keys + [-1] * (self.C - len(keys))
+        self.slot_stamp = [0] * self.C
+        self.frozen = True
+
+    def clear_static(self) -> None:
+        self.frozen = False

@@ -220,3 +220,33 @@ def test_resize_then_lookups_match_a_cache_built_at_that_size():
         pa, pb = a.lookup_plan(l, ids), b.lookup_plan(l, ids)
         assert [e for e, _ in pa.hits] == [e for e, _ in pb.hits]
         assert set(a.resident()) == set(b.resident())
+
+
+def test_static_placement_frozen_then_lru():
+    r = Residency(3, 2, 4, 5, 5)  # B_P = B_H: the LRU would fill every miss
+    r.set_static([5, 0, 7])       # layer 1 expert 1, layer 0 expert 0, layer 1 expert 3
+    p = r.lookup_plan(0, [[0, 2]])
+    assert p.hits == [(0, 1)] and p.q == 1 and p.q_fill == 0 and p.fills == [] and p.host == [2]
+    p = r.lookup_plan(1, [[1, 2], [3, 2]])
+    assert p.hits == [(1, 0), (3, 2)] and p.host == [2] and p.evicted == []
+    assert r.snapshot() == ([5, 0, 7], [2, 1, 2], 2, 0)
+    r.clear_static()              # LRU again from this state: key 0 (stamp 1) goes first
+    p = r.lookup_plan(0, [[3]])
+    assert p.fills == [(3, 1)] and p.evicted == [0]
+    with pytest.raises(ValueError):
+        r.set_static([1, 1])
+
+
+def test_static_placement_miss_rate_is_membership():
+    # frozen: a key hits iff it is in the placement, whatever the order of calls
+    rng = np.random.default_rng(2)
+    keys = list(rng.choice(48, size=10, replace=False))
+    r = Residency(12, 3, 16, 1, 3)
+    r.set_static(keys)
+    for _ in range(50):
+        l = int(rng.integers(0, 3))
+        ids = [list(rng.choice(16, size=4, replace=False))]
+        p = r.lookup_plan(l, ids)
+        assert sorted(e for e, _ in p.hits) == sorted(e for e in ids[0] if l * 16 + e in keys)
+        assert p.q_fill == 0 and not p.fills and not p.evicted
+    assert sorted(k for k in r.snapshot()[0] if k >= 0) == sorted(int(k) for k in keys)

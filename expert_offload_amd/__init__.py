@@ -84,6 +84,8 @@ _SIGS = {
     "eo_dequant": [_P, _I32, _I32, _P],
     "eo_stats_get": [_P, ctypes.POINTER(eo_stats)],
     "eo_resize_cache": [_P, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
+    "eo_set_static_placement": [_P, _P, _I32],
+    "eo_clear_static_placement": [_P],
     "eo_kernel_times": [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64), _I32],
     "eo_set_timing": [_P, _I32],
     "eo_expert_bytes": [_I32, _I32, _I32],
@@ -255,6 +257,17 @@ def eo_resize_cache(e, slots: int):
     ne, nm = _I64(0), _I64(0)
     _check(lib().eo_resize_cache(e, slots, ctypes.byref(ne), ctypes.byref(nm)))
     return ne.value, nm.value
+
+
+def eo_set_static_placement(e, keys) -> None:
+    """keys: int32 host array of layer*E + expert (numpy)."""
+    import numpy as np
+    k = np.ascontiguousarray(keys, dtype=np.int32)
+    _check(lib().eo_set_static_placement(e, k.ctypes.data if k.size else None, int(k.size)))
+
+
+def eo_clear_static_placement(e) -> None:
+    _check(lib().eo_clear_static_placement(e))
 
 
 def eo_stats_get(e) -> dict:

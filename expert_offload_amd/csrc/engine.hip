@@ -529,6 +529,7 @@ eo_status reset_cache(eo_engine* e) {
     st.credit = 0;
     st.bp = (int32_t)e->bp;
     st.bh = (int32_t)e->bh;
+    st.frozen = 0;
     HIPCHK(hipMemcpy(e->d_state, &st, sizeof(DevState), hipMemcpyHostToDevice));
     return EO_OK;
 }
@@ -1190,6 +1191,52 @@ eo_status eo_resize_cache(eo_engine* e, int64_t slots, int64_t* n_evicted, int64
     e->cfg.cache_slots = Cn;
     if (n_evicted) *n_evicted = excess;
     if (n_moved) *n_moved = (int64_t)moves.size();
+    return EO_OK;
+}
+
+eo_status eo_set_static_placement(eo_engine* e, const int32_t* keys, int32_t n) {
+    if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
+    if (n < 0 || n > e->C || (n > 0 && !keys))
+        return fail(EO_ERR_INVALID_ARG, "0 <= n <= cache slots keys required");
+    if (e->plan_pending) return fail(EO_ERR_STATE, "a lookup plan is pending: place between steps");
+    const int64_t nk = (int64_t)e->L * e->E;
+    std::vector<int32_t> k2s(nk, -1);
+    for (int32_t i = 0; i < n; ++i) {
+        if (keys[i] < 0 || keys[i] >= nk) return fail(EO_ERR_INVALID_ARG, "key out of range");
+        if (k2s[keys[i]] >= 0) return fail(EO_ERR_INVALID_ARG, "repeated key");
+        k2s[keys[i]] = i;
+    }
+    HIPCHK(hipSetDevice(e->cfg.device));
+    HIPCHK(hipDeviceSynchronize());
+    for (int32_t i = 0; i < n; ++i)
+        HIPCHK(hipMemcpyAsync(e->d_slots + (uint64_t)i * e->S_pad,
+                              e->pool[keys[i] / e->E] + (uint64_t)(keys[i] % e->E) * e->S_pad, e->S,
+                              hipMemcpyHostToDevice, e->copy_stream));
+    std::vector<int32_t> skey(e->C, -1);
+    for (int32_t i = 0; i < n; ++i) skey[i] = keys[i];
+    if (e->C) {
+        HIPCHK(hipMemcpy(e->d_slot_key, skey.data(), sizeof(int32_t) * e->C, hipMemcpyHostToDevice));
+        HIPCHK(hipMemset(e->d_slot_stamp, 0, sizeof(int64_t) * e->C));
+    }
+    HIPCHK(hipMemcpy(e->d_key2slot, k2s.data(), sizeof(int32_t) * nk, hipMemcpyHostToDevice));
+    DevState st{};
+    HIPCHK(hipMemcpy(&st, e->d_state, sizeof(DevState), hipMemcpyDeviceToHost));
+    st.frozen = 1;
+    HIPCHK(hipMemcpy(e->d_state, &st, sizeof(DevState), hipMemcpyHostToDevice));
+    HIPCHK(hipStreamSynchronize(e->copy_stream));
+    e->stats.pcie_bytes += (int64_t)n * (int64_t)e->S;
+    return EO_OK;
+}
+
+eo_status eo_clear_static_placement(eo_engine* e) {
+    if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
+    if (e->plan_pending) return fail(EO_ERR_STATE, "a lookup plan is pending");
+    HIPCHK(hipSetDevice(e->cfg.device));
+    HIPCHK(hipDeviceSynchronize());
+    DevState st{};
+    HIPCHK(hipMemcpy(&st, e->d_state, sizeof(DevState), hipMemcpyDeviceToHost));
+    st.frozen = 0;
+    HIPCHK(hipMemcpy(e->d_state, &st, sizeof(DevState), hipMemcpyHostToDevice));
     return EO_OK;
 }
 

@@ -33,7 +33,8 @@ struct DevPlan {
 struct DevState {
     int64_t clock, credit;
     int32_t bp, bh;  // MB/s
-    int32_t seq, pad;
+    int32_t seq;
+    int32_t frozen;  // static placement: lookups fill and evict nothing
 };
 
 // ---------------------------------------------------------------- launches

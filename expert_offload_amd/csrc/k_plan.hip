@@ -7,7 +7,8 @@
 // all layers. Integer rules (exactly reproducible):
 //   clock += 1 per call; hits get stamp = clock;
 //   q = min(m, floor((c + m*B_P)/B_H)), c <- min(c + m*B_P - q*B_H, B_H - 1);
-//   q_fill = min(q, C - hits); misses ranked by (tokens desc, id asc), the
+//   q_fill = min(q, C - hits) (0 under a static placement); misses ranked by
+//   (tokens desc, id asc), the
 //   first q_fill filled, the rest host-executed and not inserted;
 //   evict max(0, q_fill - empty) slots not touched this call in
 //   (stamp asc, key asc) order; empty + freed slots, ascending, go to the
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void k_plan(
 
     __shared__ int s_miss[kMaxE];
     __shared__ long long s_credit0;
-    __shared__ int s_bp, s_bh, s_seq0;
+    __shared__ int s_bp, s_bh, s_seq0, s_frozen;
 
     const int tid = threadIdx.x;
     // slot table into LDS (every load of a thread issued before its first
@@ -161,6 +162,7 @@ __global__ __launch_bounds__(kThreads) void k_plan(
             s_bp = st->bp;
             s_bh = st->bh;
             s_seq0 = st->seq;
+            s_frozen = st->frozen;
         }
         // one token: the first wavefront selects its experts from the logits
         // while the table loads are in flight
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void k_plan(
         if (c2 > bh - 1) c2 = bh - 1;
         s_credit = c2;
         s_q = (int)q;
-        int room = C - n_hit0;
+        int room = s_frozen ? 0 : C - n_hit0;  // a static placement takes no fills
         s_qfill = (int)(q < room ? q : room);
     }
     __syncthreads();

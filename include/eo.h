@@ -238,6 +238,18 @@ eo_status eo_set_capture(eo_engine* e, void* x_in, float* y, int32_t* ids, float
  * call); on EO_ERR_OOM the engine is unchanged. n_evicted / n_moved may be NULL. */
 eo_status eo_resize_cache(eo_engine* e, int64_t slots, int64_t* n_evicted, int64_t* n_moved);
 
+/* Static placement, for the placement-policy comparison (zhichai.net article,
+ * section 2, LRU paragraph: one routing trace replayed under the global LRU,
+ * under a placement fixed from prefill routing and under a routing-blind static
+ * split). Between steps: the n keys (host array, key = layer*E + expert,
+ * distinct, n <= cache slots) are copied from the pool into slots 0..n-1 (stamp
+ * 0; other slots empty) and the cache is frozen: lookups still count and stamp
+ * hits and run the credit split, but fill and evict nothing, so every miss runs
+ * on the host. Synchronous. eo_clear_static_placement returns to the LRU from
+ * the current residency. EO_ERR_STATE with a pending lookup plan. */
+eo_status eo_set_static_placement(eo_engine* e, const int32_t* keys, int32_t n);
+eo_status eo_clear_static_placement(eo_engine* e);
+
 /* ---- introspection ---- */
 /* Slot table and counters (host buffers of C entries each). Synchronous. */
 eo_status eo_cache_snapshot(eo_engine* e, int32_t* slot_key, int64_t* slot_stamp, int64_t* clock,

@@ -424,6 +424,57 @@ def test_remeasure_bandwidth_keeps_the_cache():
         eo.eo_destroy(e)
 
 
+def test_static_placement_then_lru():
+    # a frozen placement: hits only on the placed keys, nothing filled or
+    # evicted, every miss on the host; then back to the LRU from that state
+    shape = small_shape("fp8", layers=3)
+    seed = 18
+    L, k, H, E = shape.layers, shape.top_k, shape.hidden, shape.experts
+    C = 14
+    e = make_engine(shape, seed, cache_slots=C, max_tokens=1)
+    try:
+        eo.eo_set_bandwidth(e, 9, 9)
+        res = Residency(C, L, E, 9, 9)
+        keys = np.random.default_rng(seed).choice(L * E, size=11, replace=False).astype(np.int32)
+        eo.eo_set_static_placement(e, keys)
+        res.set_static(keys)
+        tr = synth.sticky_zipf_trace(seed, 8, L, E, k)
+        cx = torch.zeros((L, 1, H), dtype=torch.int16, device="cuda")
+        cy = torch.zeros((L, 1, H), dtype=torch.float32, device="cuda")
+        ci = torch.zeros((L, 1, k), dtype=torch.int32, device="cuda")
+        cw = torch.zeros((L, 1, k), dtype=torch.float32, device="cuda")
+        eo.eo_set_capture(e, cx, cy, ci, cw, 1)
+        st0 = eo.eo_stats_get(e)
+        for s in range(8):
+            if s == 5:
+                eo.eo_clear_static_placement(e)
+                res.clear_static()
+            xd = dev(synth.activations(seed, 970 + s, 1, H, 1.0, True).view(np.int16))
+            eo.eo_decode_step(e, xd, 1, dev(tr[s].reshape(L, 1, k)), _stream())
+            torch.cuda.synchronize()
+            for l in range(L):
+                res.lookup_plan(l, tr[s, l][None, :])
+            kk = np.zeros(C, dtype=np.int32)
+            ss = np.zeros(C, dtype=np.int64)
+            assert eo.eo_cache_snapshot(e, kk, ss) == (res.clock, res.credit)
+            assert list(kk) == res.snapshot()[0] and list(ss) == res.snapshot()[1], s
+            if s == 4:
+                st = eo.eo_stats_get(e)
+                assert st["fills"] == st0["fills"]  # frozen: no fills at all
+            xin = cx.cpu().numpy().view(np.uint16)
+            ys = cy.cpu().numpy()
+            for l in range(L):
+                xf = synth.bf16_bits_to_f32(xin[l])
+                R = synth.router_weights(seed, l, E, H)
+                ids, w, _ = OR.route(xf, R, k, tr[s, l][None, :])
+                assert rel_err(ys[l], oracle_layer(shape, seed, l, xf, ids, w)) <= TOL, (s, l)
+        assert eo.eo_stats_get(e)["fills"] > st0["fills"]  # the LRU filled again
+        with pytest.raises(eo.EOError):
+            eo.eo_set_static_placement(e, np.array([1, 1], dtype=np.int32))
+    finally:
+        eo.eo_destroy(e)
+
+
 def test_decode_determinism():
     shape = small_shape("bf16", layers=2)
     outs = []

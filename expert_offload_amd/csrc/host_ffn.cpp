@@ -323,8 +323,14 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
     };
 
     constexpr int RB = 16;
-    const int nb1 = (I + RB - 1) / RB;
+    const int nb1_fp32 = (I + RB - 1) / RB;
     if (fmt == EO_W_BF16 && jb.xb && H % 128 == 0 && I % 64 == 0 && cpu_has_avx512bf16()) {
+        // task sizes: about two gate/up tasks per thread and expert (measured
+        // best on the 16-core host: smaller tasks cost dispatch, larger ones
+        // leave threads idle at the end), 64 output rows per down task
+        const int RB1 = std::max(4, std::min(64, (I / (2 * threadpool_size(pool))) & ~3));
+        const int nb1 = (I + RB1 - 1) / RB1;
+        constexpr int RB2 = 64;
         // One pool run, pipelined over experts: gate/up rows of expert i (h_i,
         // bf16) and the down rows of expert i-1 (v_i = W_down h_i per token,
         // unweighted fp32) are queued alternately; a down task waits for its
@@ -337,7 +343,7 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
         if (scratch.size() < hwords + vtot) scratch.resize(hwords + vtot);
         uint16_t* hb = (uint16_t*)scratch.data();
         float* v = scratch.data() + hwords;
-        const int nb2 = H / RB;  // H % 128 == 0
+        const int nb2 = H / RB2;  // H % 128 == 0
         // segments: (phase, expert) in queue order
         std::vector<std::pair<int, int>> seg;
         seg.push_back({1, 0});
@@ -359,7 +365,7 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
             const size_t nt = toks[ei].size();
             if (ph == 1) {
                 const uint16_t* W = (const uint16_t*)(b + lay.d13);
-                for (int r = blk * RB; r < std::min(I, blk * RB + RB); ++r)
+                for (int r = blk * RB1; r < std::min(I, blk * RB1 + RB1); ++r)
                     for (size_t ti = 0; ti < nt; ++ti) {
                         float g, u;
                         dot2_bf16_avx512(W + (size_t)r * H, W + (size_t)(I + r) * H,
@@ -370,7 +376,7 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
             } else {
                 while (done1[ei].load(std::memory_order_acquire) < nb1) _mm_pause();
                 const uint16_t* W2 = (const uint16_t*)(b + lay.d2);
-                for (int o = blk * RB; o < blk * RB + RB; o += 4)
+                for (int o = blk * RB2; o < blk * RB2 + RB2; o += 4)
                     for (size_t ti = 0; ti < nt; ++ti) {
                         float out[4];
                         dot4_bf16_avx512(W2 + (size_t)o * I, I, hb + hoff[ei] + ti * I, I, out);
@@ -405,8 +411,8 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
             pool->run(T, combine_rows);
         return;
     }
-    pool->run(ne * nb1, [&](int task) {
-        const int ei = task / nb1, rb = task % nb1;
+    pool->run(ne * nb1_fp32, [&](int task) {
+        const int ei = task / nb1_fp32, rb = task % nb1_fp32;
         const uint8_t* b = jb.experts[exps[ei]];
         thread_local std::vector<float> rg, ru;
         rg.resize(H);

@@ -325,12 +325,14 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
     constexpr int RB = 16;
     const int nb1_fp32 = (I + RB - 1) / RB;
     if (fmt == EO_W_BF16 && jb.xb && H % 128 == 0 && I % 64 == 0 && cpu_has_avx512bf16()) {
-        // task sizes: about two gate/up tasks per thread and expert (measured
-        // best on the 16-core host: smaller tasks cost dispatch, larger ones
-        // leave threads idle at the end), 64 output rows per down task
-        const int RB1 = std::max(4, std::min(64, (I / (2 * threadpool_size(pool))) & ~3));
+        // task sizes: two tasks per thread and expert in each phase, so that
+        // every thread streams the same share (measured on the 16-core host:
+        // smaller tasks cost dispatch, uneven counts leave threads idle)
+        const int nth = threadpool_size(pool);
+        const int RB1 = std::max(4, (I + 2 * nth - 1) / (2 * nth));
         const int nb1 = (I + RB1 - 1) / RB1;
-        constexpr int RB2 = 64;
+        const int RB2 = 4 * std::max(1, (H + 8 * nth - 1) / (8 * nth));  // multiple of 4
+        const int nb2 = (H + RB2 - 1) / RB2;
         // One pool run, pipelined over experts: gate/up rows of expert i (h_i,
         // bf16) and the down rows of expert i-1 (v_i = W_down h_i per token,
         // unweighted fp32) are queued alternately; a down task waits for its
@@ -343,7 +345,6 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
         if (scratch.size() < hwords + vtot) scratch.resize(hwords + vtot);
         uint16_t* hb = (uint16_t*)scratch.data();
         float* v = scratch.data() + hwords;
-        const int nb2 = H / RB2;  // H % 128 == 0
         // segments: (phase, expert) in queue order
         std::vector<std::pair<int, int>> seg;
         seg.push_back({1, 0});
@@ -376,7 +377,7 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
             } else {
                 while (done1[ei].load(std::memory_order_acquire) < nb1) _mm_pause();
                 const uint16_t* W2 = (const uint16_t*)(b + lay.d2);
-                for (int o = blk * RB2; o < blk * RB2 + RB2; o += 4)
+                for (int o = blk * RB2; o < std::min(H, blk * RB2 + RB2); o += 4)  // H % 4 == 0
                     for (size_t ti = 0; ti < nt; ++ti) {
                         float out[4];
                         dot4_bf16_avx512(W2 + (size_t)o * I, I, hb + hoff[ei] + ti * I, I, out);

@@ -154,8 +154,6 @@ hipError_t launch_gemv_reduce(const float* y_parts, int nparts, const float* y_h
                               float* y, void* x_res, int act_bf16, hipStream_t s,
                               const void* x_in = nullptr);
 
-// Residual add: x = act(x + y), T*H elements.
-hipError_t launch_residual(void* x, const float* y, int64_t n, int act_bf16, hipStream_t s);
 // u [T,H] = RMS-normalised rows of r (activation dtype, 16-byte aligned rows).
 hipError_t launch_rmsnorm(const void* r, void* u, int T, int H, int act_bf16, hipStream_t s);
 

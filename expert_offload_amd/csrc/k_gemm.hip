@@ -801,11 +801,9 @@ hipError_t launch_ffn_gemm(int fmt, const Layout& lay, GroupW gw, int E, int has
                            const int32_t* ids, const float* w, int k, int T, void* o_pairs,
                            hipStream_t s, hipEvent_t* ev) {
     (void)ids;
-    static bool env_read = false;
-    if (!env_read) {
-        if (const char* v = getenv("EO_GEMM_PATH")) g_gemm_tiles = atoi(v);
-        env_read = true;
-    }
+    // EO_GEMM_PATH (read per call, so that tests can compare the kernels)
+    const char* path = getenv("EO_GEMM_PATH");
+    g_gemm_tiles = path ? atoi(path) : 2;
     const int G = E + (has_shared ? 1 : 0);
     const int tiles = (P_max + kTileM - 1) / kTileM + G;  // upper bound on row tiles
     GemmArgs a1{};

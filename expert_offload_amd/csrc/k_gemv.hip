@@ -437,8 +437,6 @@ __global__ __launch_bounds__(256) void k_gemv_dn(GemvArgs a, const uint16_t* __r
     }
 }
 
-int g_gemv_variant = -1;  // EO_GEMV_VARIANT selects a tuning variant (0 = default)
-
 // Lanes per row G and chunks per lane NC for a row of `nch` chunks.
 bool split_rows(int nch, int* G, int* NC) {
     for (int g = 64; g >= 4; g >>= 1)
@@ -472,15 +470,6 @@ hipError_t fast_dispatch(const GemvArgs& a, uint16_t* hb, hipStream_t s, hipEven
 #define EO_FAST(ga, nca, ra, gb, ncb, rb)                         \
     if (GA == ga && NCA == nca && GB == gb && NCB == ncb)         \
         return run_fast<FMT, ga, nca, ra, gb, ncb, rb>(a, hb, s, ev);
-    if (FMT == EO_W_BF16 && GA == 64 && NCA == 4 && GB == 32 && NCB == 3) {
-        switch (g_gemv_variant) {  // rows per lane group (gate/up, down); tuning sweep
-        case 2: return run_fast<FMT, 64, 4, 4, 32, 3, 4>(a, hb, s, ev);
-        case 3: return run_fast<FMT, 64, 4, 1, 32, 3, 2>(a, hb, s, ev);
-        case 4: return run_fast<FMT, 64, 4, 2, 32, 3, 4>(a, hb, s, ev);
-        case 5: return run_fast<FMT, 64, 4, 2, 32, 3, 2>(a, hb, s, ev);
-        default: break;
-        }
-    }
     EO_FAST(64, 4, 1, 32, 3, 1)  // bf16 H 2048, I 768
     EO_FAST(64, 1, 4, 32, 1, 4)  // bf16 H 512, I 256
     EO_FAST(32, 1, 4, 16, 1, 4)  // fp8 H 512, I 256
@@ -523,10 +512,6 @@ hipError_t launch_ffn_gemv(int fmt, const Layout& lay, GroupW gw, const DevPlan*
     a.h = h_buf;
     a.yp = y_parts;
     if (ex) a.ex = *ex;
-    if (g_gemv_variant < 0) {
-        const char* v = getenv("EO_GEMV_VARIANT");
-        g_gemv_variant = v ? atoi(v) : 0;
-    }
     if (allow_fast && act_bf16 && fmt != EO_W_FP32) {
         hipError_t he = hipErrorNotSupported;
         uint16_t* hb = (uint16_t*)h_buf;

@@ -186,20 +186,6 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ o_pair
     }
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(256) void k_residual(void* __restrict__ x, const float* __restrict__ y,
-                                                  int64_t n) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    if (BF16) {
-        uint16_t* xp = (uint16_t*)x;
-        xp[i] = (uint16_t)f32_bf16_rne(bf16_f32(xp[i]) + y[i]);
-    } else {
-        float* xp = (float*)x;
-        xp[i] = xp[i] + y[i];
-    }
-}
-
 // Layer input from the residual stream: u = r / sqrt(mean(r^2) + 1e-6), one
 // block per token. The sum of squares is taken in fp32 in a fixed order (per
 // lane, then a butterfly within each wavefront, then the wavefronts in order),
@@ -299,13 +285,5 @@ hipError_t launch_combine(const void* o_pairs, const int32_t* ids, const int32_t
     return hipGetLastError();
 }
 
-hipError_t launch_residual(void* x, const float* y, int64_t n, int act_bf16, hipStream_t s) {
-    int64_t blocks = (n + 255) / 256;
-    if (act_bf16)
-        k_residual<true><<<(unsigned)blocks, 256, 0, s>>>(x, y, n);
-    else
-        k_residual<false><<<(unsigned)blocks, 256, 0, s>>>(x, y, n);
-    return hipGetLastError();
-}
 
 }  // namespace eo

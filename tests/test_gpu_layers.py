@@ -475,6 +475,56 @@ def test_static_placement_then_lru():
         eo.eo_destroy(e)
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
+def test_every_gemm_and_gemv_kernel_against_the_oracle(fmt, monkeypatch):
+    # the grouped GEMM's three kernels (plain 128x128, register-prefetch
+    # 128x256, async-ring 128x256 for bf16) and both decode GEMV families on one
+    # shape, each against the oracle
+    shape = small_shape(fmt)
+    seed = 19
+    x = synth.activations(seed, 77, 300, shape.hidden, 1.0, True)
+    for path in ("0", "1", "2"):
+        monkeypatch.setenv("EO_GEMM_PATH", path)
+        e = make_engine(shape, seed, max_tokens=300)
+        try:
+            eo.eo_set_bandwidth(e, 50, 50)
+            y = torch.zeros((300, shape.hidden), dtype=torch.float32, device="cuda")
+            eo.eo_moe_layer(e, 1, dev(x.view(np.int16)), y, 300, None, _stream())
+            torch.cuda.synchronize()
+            check_layer(shape, seed, 1, x, y.cpu().numpy())
+        finally:
+            eo.eo_destroy(e)
+    monkeypatch.delenv("EO_GEMM_PATH")
+    x1 = x[:1]
+    for fast in ("1", "0"):
+        monkeypatch.setenv("EO_GEMV_FAST", fast)
+        e = make_engine(shape, seed, max_tokens=1)
+        try:
+            eo.eo_set_bandwidth(e, 50, 50)
+            y = torch.zeros((1, shape.hidden), dtype=torch.float32, device="cuda")
+            eo.eo_moe_layer(e, 1, dev(x1.view(np.int16)), y, 1, None, _stream())
+            torch.cuda.synchronize()
+            check_layer(shape, seed, 1, x1, y.cpu().numpy())
+        finally:
+            eo.eo_destroy(e)
+
+
+def test_fills_by_kernel_and_by_copy_engine_agree():
+    # EO_FILL_SDMA=1 fills with hipMemcpyAsync after a host wait; same results
+    shape = small_shape("mxfp4", layers=3)
+    a = _decode_capture(shape, 20, 4, True, "1")
+    import os
+    os.environ["EO_FILL_SDMA"] = "1"
+    try:
+        b = _decode_capture(shape, 20, 4, True, "1")
+    finally:
+        del os.environ["EO_FILL_SDMA"]
+    for s in range(4):
+        for i in range(1, 6):
+            assert np.array_equal(a[s][i], b[s][i]), (s, i)
+    assert a[-1] == b[-1]
+
+
 def test_decode_determinism():
     shape = small_shape("bf16", layers=2)
     outs = []

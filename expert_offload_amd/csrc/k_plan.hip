@@ -397,6 +397,263 @@ __global__ __launch_bounds__(kThreads) void k_plan(
     }
 }
 
+// ---------------------------------------------------------------- one token
+// The same rules for a single token (T = 1, every decode step). The token's k
+// experts are lanes of the first wavefront, which takes every decision with
+// ballots and shuffles and no workgroup barrier; the other wavefronts only
+// stage the slot table in LDS (needed when something is filled) and help with
+// the host mirror. With one token every routed expert has count 1, so misses
+// rank by expert id, and hits are listed in expert-id order.
+constexpr int kThreads1 = 256;
+
+__device__ __forceinline__ uint64_t wave_min_u64_1(uint64_t v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+        uint32_t lo = __shfl_xor((uint32_t)v, s, 64);
+        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), s, 64);
+        uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o < v ? o : v;
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(kThreads1) void k_plan1(
+    int layer, const int32_t* ids_in, const float* w_in, const uint8_t* __restrict__ x,
+    int x_bytes, int k, int E, int C, int32_t* __restrict__ g_slot_key,
+    int64_t* __restrict__ g_slot_stamp, int32_t* __restrict__ key2slot,
+    DevState* __restrict__ st, DevPlan* __restrict__ dp, DevPlan* __restrict__ hp,
+    int32_t* __restrict__ h_ids, float* __restrict__ h_w, uint8_t* __restrict__ h_x,
+    PlanRoute rt) {
+    extern __shared__ int64_t smem64[];
+    int64_t* s_stamp = smem64;                // [C]
+    int32_t* s_key = (int32_t*)(smem64 + C);  // [C]
+    __shared__ int32_t s_ids[kMaxK];
+    __shared__ float s_w[kMaxK];
+    __shared__ int32_t s_fill_slot[kMaxK];
+    __shared__ int s_err, s_nhost, s_qfill, s_empty, s_vslot;
+    __shared__ long long s_clock0, s_credit0;
+    __shared__ int s_bp, s_bh, s_seq0, s_frozen;
+    __shared__ int red[kThreads1 / 64];
+    __shared__ uint64_t red64[kThreads1 / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // each thread owns a contiguous range of slots (empty-slot order is by index)
+    const int per = (C + kThreads1 - 1) / kThreads1;
+    const int s_lo = min(C, tid * per), s_hi = min(C, s_lo + per);
+
+    // slot table into LDS in batches whose loads are all issued before their
+    // stores, empty slots counted on the way; the first wavefront takes the
+    // token's experts meanwhile
+    if (tid == 0) s_empty = 0;
+    if (tid < kMaxK) s_fill_slot[tid] = -1;
+    int my_empty = 0;
+    constexpr int kB = 16;
+    for (int b0 = 0; b0 == 0 || b0 < per; b0 += kB) {
+        int32_t kr[kB];
+        int64_t sr[kB];
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            const int sl = s_lo + b0 + i;
+            if (sl < s_hi) {
+                kr[i] = g_slot_key[sl];
+                sr[i] = g_slot_stamp[sl];
+            }
+        }
+        if (b0 == 0) {
+            if (tid == 0) {
+                s_clock0 = st->clock;
+                s_credit0 = st->credit;
+                s_bp = st->bp;
+                s_bh = st->bh;
+                s_seq0 = st->seq;
+                s_frozen = st->frozen;
+                s_err = 0;
+            }
+            if (wave == 0) {
+                if (rt.z) {
+                    topk_token(rt.z, E, k, rt.forced, s_ids, s_w);
+                } else if (lane < k) {
+                    s_ids[lane] = ids_in[lane];
+                    s_w[lane] = w_in ? w_in[lane] : 0.0f;
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            const int sl = s_lo + b0 + i;
+            if (sl < s_hi) {
+                s_key[sl] = kr[i];
+                s_stamp[sl] = sr[i];
+                my_empty += kr[i] < 0;
+            }
+        }
+    }
+    __syncthreads();
+    if (my_empty) atomicAdd(&s_empty, my_empty);
+
+    // the decisions, in the first wavefront (lane j holds the token's j-th expert)
+    const bool act = wave == 0 && lane < k;
+    const int e = act ? s_ids[lane] : -1;
+    const int key = layer * E + e;
+    int slot = -1, rank = 0;
+    bool hit = false, miss = false;
+    long long q = 0, c2 = 0;
+    int m = 0, n_hit = 0;
+    const int64_t clock = s_clock0 + 1;
+    if (wave == 0) {
+        const bool bad = act && (e < 0 || e >= E);
+        bool dup = false;
+        if (act && !bad)
+            for (int jj = 0; jj < lane; ++jj) dup |= s_ids[jj] == e;
+        const uint64_t mbad = __ballot(bad), mdup = __ballot(dup);
+        if (mbad | mdup) {
+            if (lane == 0) s_err = mbad ? 1 : 2;
+        } else {
+            slot = act ? key2slot[key] : -1;
+            hit = act && slot >= 0;
+            miss = act && slot < 0;
+            const uint64_t mh = __ballot(hit), mm = __ballot(miss);
+            n_hit = __popcll(mh);
+            m = __popcll(mm);
+            for (int jj = 0; jj < k; ++jj)  // rank among the hits (or misses) by expert id
+                rank += ((hit ? (mh >> jj) : (mm >> jj)) & 1) && s_ids[jj] < e;
+            if (lane == 0) {  // the split (integer credit)
+                const long long c = s_credit0, bp = s_bp, bh = s_bh;
+                q = (c + (long long)m * bp) / bh;
+                if (q > m) q = m;
+                c2 = c + (long long)m * bp - q * bh;
+                if (c2 > bh - 1) c2 = bh - 1;
+                s_qfill = s_frozen ? 0 : (int)min(q, (long long)(C - n_hit));
+            }
+            q = __shfl(q, 0, 64);
+            c2 = __shfl(c2, 0, 64);
+            if (hit) {
+                s_stamp[slot] = clock;  // touched: not evictable in this call
+                g_slot_stamp[slot] = clock;
+                dp->hit_e[rank] = hp->hit_e[rank] = e;
+                dp->hit_slot[rank] = hp->hit_slot[rank] = slot;
+            }
+        }
+    }
+    __syncthreads();
+    if (s_err) {
+        if (tid < kMaxK) dp->tok_slot[tid] = -1;
+        if (tid == 0) {
+            const int seq = s_seq0 + 1;
+            st->seq = seq;
+            dp->pad = s_err;
+            hp->pad = s_err;
+            dp->seq = seq;
+            __threadfence_system();
+            __hip_atomic_store(&hp->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+        return;
+    }
+    const int q_fill = s_qfill;
+    int n_ev = 0;
+    if (q_fill > 0) {  // block-uniform
+        // victims (stamp asc, key asc) among occupied slots not touched in
+        // this call, one per missing empty slot
+        for (int r = 0; r < q_fill - s_empty; ++r, ++n_ev) {
+            uint64_t best = ~0ull;
+            int best_slot = -1;
+            for (int sl = s_lo; sl < s_hi; ++sl)
+                if (s_key[sl] >= 0 && s_stamp[sl] < clock) {
+                    const uint64_t v = ((uint64_t)s_stamp[sl] << 24) | (uint64_t)s_key[sl];
+                    if (v < best) {
+                        best = v;
+                        best_slot = sl;
+                    }
+                }
+            const uint64_t mine = best;
+            best = wave_min_u64_1(best);
+            if (lane == 0) red64[wave] = best;
+            __syncthreads();
+            best = red64[0];
+#pragma unroll
+            for (int i = 1; i < kThreads1 / 64; ++i) best = red64[i] < best ? red64[i] : best;
+            if (best == ~0ull) break;  // no candidate (cannot happen on a consistent table)
+            if (mine == best) s_vslot = best_slot;  // keys are unique
+            __syncthreads();
+            if (tid == 0) {
+                const int vkey = (int)(best & 0xFFFFFFull);
+                dp->evict_key[r] = hp->evict_key[r] = vkey;
+                key2slot[vkey] = -1;
+                s_key[s_vslot] = -1;  // refilled below
+            }
+            __syncthreads();
+        }
+        // empty and freed slots in ascending order go to the fills in rank order
+        int mine_empty = 0;
+        for (int sl = s_lo; sl < s_hi; ++sl) mine_empty += s_key[sl] < 0;
+        int incl = mine_empty;
+#pragma unroll
+        for (int s = 1; s < 64; s <<= 1) {
+            const int o = __shfl_up(incl, s, 64);
+            if (lane >= s) incl += o;
+        }
+        if (lane == 63) red[wave] = incl;
+        __syncthreads();
+        int r0 = incl - mine_empty;
+        for (int i = 0; i < wave; ++i) r0 += red[i];
+        for (int sl = s_lo; sl < s_hi && r0 < q_fill; ++sl)
+            if (s_key[sl] < 0) s_fill_slot[r0++] = sl;
+        __syncthreads();
+        if (miss && rank < q_fill && s_fill_slot[rank] >= 0) {
+            const int sl = s_fill_slot[rank];
+            g_slot_key[sl] = key;
+            g_slot_stamp[sl] = clock;
+            key2slot[key] = sl;
+            dp->fill_e[rank] = hp->fill_e[rank] = e;
+            dp->fill_slot[rank] = hp->fill_slot[rank] = sl;
+        }
+    }
+    if (miss && rank >= q_fill) dp->host_e[rank - q_fill] = hp->host_e[rank - q_fill] = e;
+    if (act) {
+        dp->tok_slot[lane] = hit ? slot : (rank < q_fill ? s_fill_slot[rank] : -1);
+        if (rt.z) {
+            rt.ids_out[lane] = e;
+            rt.w_out[lane] = s_w[lane];
+        }
+        if (h_ids && h_w) {
+            h_ids[lane] = e;
+            h_w[lane] = s_w[lane];
+        }
+    }
+    if (tid == 0) {
+        const int n_host = m - q_fill;
+        s_nhost = n_host;
+        dp->pad = 0;
+        dp->layer = hp->layer = layer;
+        dp->T = hp->T = 1;
+        dp->k = hp->k = k;
+        dp->m = hp->m = m;
+        dp->q = hp->q = (int)q;
+        dp->q_fill = hp->q_fill = q_fill;
+        dp->n_hit = hp->n_hit = n_hit;
+        dp->n_host = hp->n_host = n_host;
+        dp->n_evict = hp->n_evict = n_ev;
+        dp->clock = hp->clock = clock;
+        dp->credit = hp->credit = c2;
+        st->clock = clock;
+        st->credit = c2;
+        hp->pad = 0;
+    }
+    __syncthreads();
+    if (h_x && s_nhost > 0) {
+        const uint4* xs = (const uint4*)x;
+        uint4* xd = (uint4*)h_x;
+        for (int i = tid; i < x_bytes / 16; i += kThreads1) xd[i] = xs[i];
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const int seq = s_seq0 + 1;
+        st->seq = seq;
+        dp->seq = seq;
+        __threadfence_system();
+        __hip_atomic_store(&hp->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+}
+
 }  // namespace
 
 int plan_max_slots() { return kMaxSlotsLds; }
@@ -413,8 +670,19 @@ hipError_t launch_plan(int layer, const int32_t* ids, const float* w, const void
         hipError_t e = hipFuncSetAttribute((const void*)k_plan,
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            12 * kMaxSlotsLds);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute((const void*)k_plan1, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    12 * kMaxSlotsLds);
         if (e != hipSuccess) return e;
         attr_set = true;
+    }
+    // EO_PLAN1=0 sends one-token lookups to the general kernel (tests compare them)
+    const char* p1 = getenv("EO_PLAN1");
+    if (T == 1 && k <= 64 && !(p1 && p1[0] == '0')) {
+        k_plan1<<<1, kThreads1, lds, s>>>(layer, ids, w, (const uint8_t*)x, (int)x_bytes, k, E,
+                                          (int)C, slot_key, slot_stamp, key2slot, st, d_plan,
+                                          h_plan, h_ids, h_w, (uint8_t*)h_x, rt);
+        return hipGetLastError();
     }
     k_plan<<<1, kThreads, lds, s>>>(layer, ids, w, (const uint8_t*)x, (int)x_bytes, T, k, E,
                                     (int)C, slot_key, slot_stamp, key2slot, st, d_plan, h_plan,

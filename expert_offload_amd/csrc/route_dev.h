@@ -70,10 +70,35 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ zt, int E, 
             // out-of-range ids are reported by the lookup; read in bounds here
             zs[j] = zt[min(max(is[j], 0), E - 1)];
         }
-    } else if (E <= 128) {
-        topk_select<2>(zt, E, k, zs, is);
     } else if (E <= 256) {
-        topk_select<4>(zt, E, k, zs, is);
+        // each logit's rank = how many logits beat it (larger, or equal with a
+        // smaller id); the k of rank < k are the selection, in (z desc, id asc)
+        // order: the same result as k rounds of selection
+        __shared__ float s_zw[4][256];  // per wavefront of the workgroup (up to 4)
+        __shared__ int32_t s_selw[4][kMaxK];
+        float* s_z = s_zw[(threadIdx.x >> 6) & 3];
+        int32_t* s_sel = s_selw[(threadIdx.x >> 6) & 3];
+        for (int e = lane; e < E; e += 64) s_z[e] = zt[e];
+        if (lane < k) s_sel[lane] = -1;  // stays -1 only for unordered (NaN) logits
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        for (int e = lane; e < E; e += 64) {
+            const float z = s_z[e];
+            int r = 0;
+            for (int o = 0; o < E; ++o) {
+                const float zo = s_z[o];
+                r += zo > z || (zo == z && o < e);
+            }
+            if (r < k) s_sel[r] = e;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        for (int j = 0; j < k; ++j) {
+            is[j] = s_sel[j];
+            zs[j] = is[j] >= 0 ? s_z[is[j]] : -INFINITY;
+        }
     } else {
         topk_select<kMaxE / 64>(zt, E, k, zs, is);
     }

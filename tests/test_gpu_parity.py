@@ -102,6 +102,43 @@ def test_plan_and_cache_state_bit_exact(case):
         eo.eo_destroy(e)
 
 
+@pytest.mark.parametrize("case", range(5))
+def test_one_token_plan_bit_exact(case, monkeypatch):
+    # one-token lookups go to their own kernel; both kernels against the oracle
+    rng = np.random.default_rng(100 + case)
+    L, E, k = 3, 24, int(rng.integers(1, 9))
+    C = [9, 2, 30, 0, 72][case]
+    bp, bh = [(5, 5), (1, 3), (11800, 47500), (7, 2), (3, 4)][case]
+    shape = dataclasses.replace(TINY, layers=L, experts=E, top_k=k, cache_slots=C)
+    for plan1 in ("1", "0"):
+        monkeypatch.setenv("EO_PLAN1", plan1)
+        e = make_engine(shape, 0, max_tokens=1, fill_pool=False)
+        try:
+            eo.eo_set_bandwidth(e, bp, bh)
+            ref = Residency(C, L, E, bp, bh)
+            for call in range(80):
+                l = int(rng.integers(0, L))
+                ids = rng.choice(E, size=(1, k), replace=False).astype(np.int32)
+                eo.eo_lookup_plan(e, l, dev(ids), 1, _stream())
+                got = eo.eo_last_plan(e)
+                p = ref.lookup_plan(l, ids)
+                assert got["hits"] == p.hits and got["fills"] == p.fills, (plan1, call)
+                assert got["host"] == p.host and got["evicted"] == p.evicted, (plan1, call)
+                assert (got["m"], got["q"], got["q_fill"], got["clock"], got["credit"]) == \
+                    (p.m, p.q, p.q_fill, p.clock, p.credit)
+            keys = np.zeros(max(C, 1), dtype=np.int32)
+            stamps = np.zeros(max(C, 1), dtype=np.int64)
+            assert eo.eo_cache_snapshot(e, keys, stamps) == (ref.clock, ref.credit)
+            assert list(keys[:C]) == ref.snapshot()[0] and list(stamps[:C]) == ref.snapshot()[1]
+            bad = dev(np.array([[0] * k], dtype=np.int32)) if k > 1 else \
+                dev(np.array([[E]], dtype=np.int32))
+            with pytest.raises(eo.EOError):
+                eo.eo_lookup_plan(e, 0, bad, 1, _stream())
+                eo.eo_last_plan(e)
+        finally:
+            eo.eo_destroy(e)
+
+
 @pytest.mark.parametrize("fmt", ["fp32", "bf16", "mxfp4", "nvfp4", "fp8"])
 def test_device_dequant_bit_exact(fmt):
     f = synth.FMT_NAMES[fmt]

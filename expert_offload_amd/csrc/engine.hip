@@ -270,13 +270,20 @@ eo_status wait_plan(eo_engine* e) {
     return EO_OK;
 }
 
+// ea != null: the layer entry runs in the same launch (one token; x is ea->u)
 eo_status do_plan(eo_engine* e, int layer, const int32_t* ids, const float* w, const void* x,
-                  int T, hipStream_t s, PlanRoute rt = PlanRoute{nullptr, nullptr, nullptr, nullptr}) {
+                  int T, hipStream_t s, PlanRoute rt = PlanRoute{nullptr, nullptr, nullptr, nullptr},
+                  const EntryArgs* ea = nullptr) {
     const size_t xb = (size_t)T * e->H * e->act_size;
-    hipError_t he = launch_plan(layer, ids, w ? w : nullptr, x, xb, T, e->k, e->E, e->C,
-                                e->d_slot_key, e->d_slot_stamp, e->d_key2slot, e->d_state,
-                                e->d_plan, e->h_plan_dev, w ? e->h_ids_dev : nullptr,
-                                w ? e->h_w_dev : nullptr, x ? e->h_x_dev : nullptr, s, rt);
+    hipError_t he =
+        ea ? launch_entry_plan(*ea, layer, e->k, e->C, e->d_slot_key, e->d_slot_stamp,
+                               e->d_key2slot, e->d_state, e->d_plan, e->h_plan_dev,
+                               w ? e->h_ids_dev : nullptr, w ? e->h_w_dev : nullptr,
+                               x ? e->h_x_dev : nullptr, s, rt)
+           : launch_plan(layer, ids, w ? w : nullptr, x, xb, T, e->k, e->E, e->C,
+                         e->d_slot_key, e->d_slot_stamp, e->d_key2slot, e->d_state, e->d_plan,
+                         e->h_plan_dev, w ? e->h_ids_dev : nullptr, w ? e->h_w_dev : nullptr,
+                         x ? e->h_x_dev : nullptr, s, rt);
     if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("plan launch: ") + hipGetErrorString(he));
     e->plan_seq += 1;
     e->plan_pending = true;
@@ -473,6 +480,10 @@ eo_status decode_one_token(eo_engine* e, uint16_t* x_inout, const int32_t* force
                            hipStream_t s) {
     const int H = e->H, k = e->k, nparts = e->k + e->shared;
     const bool cap = e->cap_y && 1 <= e->cap_T;
+    // EO_ENTRY_PLAN=0 keeps the entry and the plan in separate launches (tests compare them)
+    const char* ep = std::getenv("EO_ENTRY_PLAN");
+    const bool fuse_plan = !(ep && ep[0] == '0') &&
+                           entry_plan_ok(1, k, e->E, H, e->C, e->act_bf16);
     const float* prev_host = nullptr;
     for (int l = 0; l < e->L; ++l) {
         int32_t* ids = e->d_ids;
@@ -489,16 +500,22 @@ eo_status decode_one_token(eo_engine* e, uint16_t* x_inout, const int32_t* force
         a.z = e->d_z;
         a.E = e->E;
         a.H = H;
-        hipError_t he = launch_entry(a, s);
-        if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("layer entry: ") + hipGetErrorString(he));
         if (cap) {
-            HIPCHK(hipMemcpyAsync((uint8_t*)e->cap_x + (size_t)l * e->cap_T * H * 2, e->d_u,
-                                  (size_t)H * 2, hipMemcpyDeviceToDevice, s));
             ids = e->cap_ids + (size_t)l * e->cap_T * k;
             w = e->cap_w + (size_t)l * e->cap_T * k;
         }
         PlanRoute rt{e->d_z, forced_ids ? forced_ids + (size_t)l * k : nullptr, ids, w};
-        EOCHK(do_plan(e, l, ids, w, e->d_u, 1, s, rt));
+        if (fuse_plan) {
+            EOCHK(do_plan(e, l, ids, w, e->d_u, 1, s, rt, &a));
+        } else {
+            hipError_t he = launch_entry(a, s);
+            if (he != hipSuccess)
+                return fail(EO_ERR_HIP, std::string("layer entry: ") + hipGetErrorString(he));
+            EOCHK(do_plan(e, l, ids, w, e->d_u, 1, s, rt));
+        }
+        if (cap)  // u is not changed by the plan
+            HIPCHK(hipMemcpyAsync((uint8_t*)e->cap_x + (size_t)l * e->cap_T * H * 2, e->d_u,
+                                  (size_t)H * 2, hipMemcpyDeviceToDevice, s));
         EOCHK(do_fill(e, s));
         EOCHK(do_ffn_device(e, l, e->d_u, ids, w, s));
         EOCHK(do_host(e, e->d_u, ids, w, s));

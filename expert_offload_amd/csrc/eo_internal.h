@@ -35,6 +35,7 @@ struct DevState {
     int32_t bp, bh;  // MB/s
     int32_t seq;
     int32_t frozen;  // static placement: lookups fill and evict nothing
+    int32_t ticket;  // workgroups done in the fused entry + plan launch (0 between launches)
 };
 
 // ---------------------------------------------------------------- launches
@@ -83,6 +84,13 @@ hipError_t launch_plan(int layer, const int32_t* ids, const float* w, const void
                        int64_t* slot_stamp, int32_t* key2slot, DevState* st, DevPlan* d_plan,
                        DevPlan* h_plan, int32_t* h_ids, float* h_w, void* h_x, hipStream_t s,
                        PlanRoute rt = PlanRoute{nullptr, nullptr, nullptr, nullptr});
+// Layer entry and the one-token plan in one launch (E/4 workgroups; the last
+// to finish plans). rt.z must be a.z; x of the plan is a.u.
+bool entry_plan_ok(int T, int k, int E, int H, int64_t C, int act_bf16);
+hipError_t launch_entry_plan(const EntryArgs& a, int layer, int k, int64_t C, int32_t* slot_key,
+                             int64_t* slot_stamp, int32_t* key2slot, DevState* st,
+                             DevPlan* d_plan, DevPlan* h_plan, int32_t* h_ids, float* h_w,
+                             void* h_x, hipStream_t s, PlanRoute rt);
 
 // Fill: copy the plan's q_fill experts from the layer's pool (device-visible
 // pointer to pinned host memory, E * S_pad bytes) into their slots. Reads the

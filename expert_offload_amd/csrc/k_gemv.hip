@@ -297,6 +297,14 @@ template <> struct FastC<EO_W_FP8> { static constexpr int n = 16, xq = 2; };
 template <> struct FastC<EO_W_MXFP4> { static constexpr int n = 32, xq = 4; };
 template <> struct FastC<EO_W_NVFP4> { static constexpr int n = 32, xq = 4; };
 
+// A weight chunk: streamed once per call, so the load carries the nontemporal
+// hint and does not allocate in the caches (x and the scales stay cached).
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
+    const u32x4_nt v = __builtin_nontemporal_load((const u32x4_nt*)p);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <int FMT>
 __device__ __forceinline__ const uint8_t* row_ptr(const uint8_t* data, int row, int K) {
     if (FMT == EO_W_BF16) return data + (size_t)row * K * 2;
@@ -318,7 +326,7 @@ __device__ __forceinline__ void rows_dot(const uint8_t* data, const uint8_t* sca
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int i = 0; i < NC; ++i)
-            wq[r][i] = *(const uint4*)(row_ptr<FMT>(data, rows[r], K) + (size_t)(gl + G * i) * 16);
+            wq[r][i] = load_stream(row_ptr<FMT>(data, rows[r], K) + (size_t)(gl + G * i) * 16);
 #pragma unroll
     for (int i = 0; i < NC; ++i)
 #pragma unroll

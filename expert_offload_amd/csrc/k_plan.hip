@@ -16,9 +16,12 @@
 // The slot table is staged in LDS for the call (C <= kMaxSlotsLds) and
 // written back; key2slot (L*E entries) stays in global memory, each entry
 // touched by one thread only.
+#include <algorithm>
+
 #include "dev_common.h"
 #include "eo_internal.h"
 #include "route_dev.h"
+#include "entry_dev.h"
 
 namespace eo {
 
@@ -417,73 +420,94 @@ __device__ __forceinline__ uint64_t wave_min_u64_1(uint64_t v) {
     return v;
 }
 
-__global__ __launch_bounds__(kThreads1) void k_plan1(
-    int layer, const int32_t* ids_in, const float* w_in, const uint8_t* __restrict__ x,
-    int x_bytes, int k, int E, int C, int32_t* __restrict__ g_slot_key,
-    int64_t* __restrict__ g_slot_stamp, int32_t* __restrict__ key2slot,
-    DevState* __restrict__ st, DevPlan* __restrict__ dp, DevPlan* __restrict__ hp,
-    int32_t* __restrict__ h_ids, float* __restrict__ h_w, uint8_t* __restrict__ h_x,
-    PlanRoute rt) {
-    extern __shared__ int64_t smem64[];
+// The one-token plan for one workgroup of kThreads1 threads; smem64 holds
+// 12*C bytes of LDS.
+__device__ __forceinline__ void plan1_body(
+    int64_t* smem64, int layer, const int32_t* ids_in, const float* w_in,
+    const uint8_t* __restrict__ x, int x_bytes, int k, int E, int C,
+    int32_t* __restrict__ g_slot_key, int64_t* __restrict__ g_slot_stamp,
+    int32_t* __restrict__ key2slot, DevState* __restrict__ st, DevPlan* __restrict__ dp,
+    DevPlan* __restrict__ hp, int32_t* __restrict__ h_ids, float* __restrict__ h_w,
+    uint8_t* __restrict__ h_x, PlanRoute rt) {
     int64_t* s_stamp = smem64;                // [C]
     int32_t* s_key = (int32_t*)(smem64 + C);  // [C]
     __shared__ int32_t s_ids[kMaxK];
     __shared__ float s_w[kMaxK];
     __shared__ int32_t s_fill_slot[kMaxK];
-    __shared__ int s_err, s_nhost, s_qfill, s_empty, s_vslot;
+    __shared__ int32_t s_k2s[kMaxE];  // this layer's row of key2slot
+    __shared__ int s_err, s_nhost, s_qfill, s_empty;
     __shared__ long long s_clock0, s_credit0;
     __shared__ int s_bp, s_bh, s_seq0, s_frozen;
     __shared__ int red[kThreads1 / 64];
-    __shared__ uint64_t red64[kThreads1 / 64];
+    __shared__ uint64_t red64[2][kThreads1 / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // each thread owns a contiguous range of slots (empty-slot order is by index)
+    // after the load, each thread owns a contiguous range of slots (empty-slot
+    // order is by index)
     const int per = (C + kThreads1 - 1) / kThreads1;
     const int s_lo = min(C, tid * per), s_hi = min(C, s_lo + per);
 
-    // slot table into LDS in batches whose loads are all issued before their
-    // stores, empty slots counted on the way; the first wavefront takes the
-    // token's experts meanwhile
+    // wavefronts 1.. load the slot table into LDS (coalesced, in batches whose
+    // loads are all issued before their stores, empty slots counted on the
+    // way) while wavefront 0 loads the state and this layer's key2slot row and
+    // takes the token's experts; no wavefront's loads queue behind another's
     if (tid == 0) s_empty = 0;
     if (tid < kMaxK) s_fill_slot[tid] = -1;
     int my_empty = 0;
-    constexpr int kB = 16;
-    for (int b0 = 0; b0 == 0 || b0 < per; b0 += kB) {
-        int32_t kr[kB];
-        int64_t sr[kB];
+    constexpr int kB = 16, kLoaders = kThreads1 - 64, kRowPer = kMaxE / 64;
+    if (wave == 0) {
+        int32_t k2[kRowPer];
 #pragma unroll
-        for (int i = 0; i < kB; ++i) {
-            const int sl = s_lo + b0 + i;
-            if (sl < s_hi) {
-                kr[i] = g_slot_key[sl];
-                sr[i] = g_slot_stamp[sl];
-            }
+        for (int i = 0; i < kRowPer; ++i)
+            if (lane + 64 * i < E) k2[i] = key2slot[layer * E + lane + 64 * i];
+        long long c0 = 0, c1 = 0;
+        int v0 = 0, v1 = 0, v2 = 0, v3 = 0;
+        if (lane == 0) {
+            c0 = st->clock;
+            c1 = st->credit;
+            v0 = st->bp;
+            v1 = st->bh;
+            v2 = st->seq;
+            v3 = st->frozen;
         }
-        if (b0 == 0) {
-            if (tid == 0) {
-                s_clock0 = st->clock;
-                s_credit0 = st->credit;
-                s_bp = st->bp;
-                s_bh = st->bh;
-                s_seq0 = st->seq;
-                s_frozen = st->frozen;
-                s_err = 0;
-            }
-            if (wave == 0) {
-                if (rt.z) {
-                    topk_token(rt.z, E, k, rt.forced, s_ids, s_w);
-                } else if (lane < k) {
-                    s_ids[lane] = ids_in[lane];
-                    s_w[lane] = w_in ? w_in[lane] : 0.0f;
+        if (rt.z) {
+            topk_token(rt.z, E, k, rt.forced, s_ids, s_w);
+        } else if (lane < k) {
+            s_ids[lane] = ids_in[lane];
+            s_w[lane] = w_in ? w_in[lane] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < kRowPer; ++i)
+            if (lane + 64 * i < E) s_k2s[lane + 64 * i] = k2[i];
+        if (lane == 0) {
+            s_clock0 = c0;
+            s_credit0 = c1;
+            s_bp = v0;
+            s_bh = v1;
+            s_seq0 = v2;
+            s_frozen = v3;
+            s_err = 0;
+        }
+    } else {
+        const int lt = tid - 64;
+        for (int b0 = 0; b0 * kLoaders < C; b0 += kB) {
+            int32_t kr[kB];
+            int64_t sr[kB];
+#pragma unroll
+            for (int i = 0; i < kB; ++i) {
+                const int sl = lt + kLoaders * (b0 + i);
+                if (sl < C) {
+                    kr[i] = g_slot_key[sl];
+                    sr[i] = g_slot_stamp[sl];
                 }
             }
-        }
 #pragma unroll
-        for (int i = 0; i < kB; ++i) {
-            const int sl = s_lo + b0 + i;
-            if (sl < s_hi) {
-                s_key[sl] = kr[i];
-                s_stamp[sl] = sr[i];
-                my_empty += kr[i] < 0;
+            for (int i = 0; i < kB; ++i) {
+                const int sl = lt + kLoaders * (b0 + i);
+                if (sl < C) {
+                    s_key[sl] = kr[i];
+                    s_stamp[sl] = sr[i];
+                    my_empty += kr[i] < 0;
+                }
             }
         }
     }
@@ -508,7 +532,7 @@ __global__ __launch_bounds__(kThreads1) void k_plan1(
         if (mbad | mdup) {
             if (lane == 0) s_err = mbad ? 1 : 2;
         } else {
-            slot = act ? key2slot[key] : -1;
+            slot = act ? s_k2s[e] : -1;
             hit = act && slot >= 0;
             miss = act && slot < 0;
             const uint64_t mh = __ballot(hit), mm = __ballot(miss);
@@ -552,52 +576,71 @@ __global__ __launch_bounds__(kThreads1) void k_plan1(
     int n_ev = 0;
     if (q_fill > 0) {  // block-uniform
         // victims (stamp asc, key asc) among occupied slots not touched in
-        // this call, one per missing empty slot
-        for (int r = 0; r < q_fill - s_empty; ++r, ++n_ev) {
-            uint64_t best = ~0ull;
-            int best_slot = -1;
+        // this call, one per missing empty slot: each thread keeps the oldest
+        // of its own range, one workgroup minimum per victim, and only the
+        // owner of the victim looks at its range again
+        const int n_vic = q_fill - s_empty;  // workgroup-uniform
+        uint64_t mine = ~0ull;
+        int mine_slot = -1;
+        auto oldest = [&]() {
+            mine = ~0ull;
             for (int sl = s_lo; sl < s_hi; ++sl)
                 if (s_key[sl] >= 0 && s_stamp[sl] < clock) {
                     const uint64_t v = ((uint64_t)s_stamp[sl] << 24) | (uint64_t)s_key[sl];
-                    if (v < best) {
-                        best = v;
-                        best_slot = sl;
+                    if (v < mine) {
+                        mine = v;
+                        mine_slot = sl;
                     }
                 }
-            const uint64_t mine = best;
-            best = wave_min_u64_1(best);
-            if (lane == 0) red64[wave] = best;
+        };
+        if (n_vic > 0) oldest();
+        for (int r = 0; r < n_vic; ++r) {
+            uint64_t best = wave_min_u64_1(mine);
+            if (lane == 0) red64[r & 1][wave] = best;  // two buffers: one barrier per round
             __syncthreads();
-            best = red64[0];
+            best = red64[r & 1][0];
 #pragma unroll
-            for (int i = 1; i < kThreads1 / 64; ++i) best = red64[i] < best ? red64[i] : best;
+            for (int i = 1; i < kThreads1 / 64; ++i)
+                best = red64[r & 1][i] < best ? red64[r & 1][i] : best;
             if (best == ~0ull) break;  // no candidate (cannot happen on a consistent table)
-            if (mine == best) s_vslot = best_slot;  // keys are unique
-            __syncthreads();
-            if (tid == 0) {
+            if (mine == best) {        // exactly one thread: keys are unique
                 const int vkey = (int)(best & 0xFFFFFFull);
                 dp->evict_key[r] = hp->evict_key[r] = vkey;
                 key2slot[vkey] = -1;
-                s_key[s_vslot] = -1;  // refilled below
+                s_key[mine_slot] = -1;  // refilled below
+                s_fill_slot[r] = mine_slot;
+                if (r + 1 < n_vic) oldest();
             }
+            ++n_ev;
+        }
+        __syncthreads();
+        // empty and freed slots in ascending order go to the fills in rank order
+        if (s_empty == 0) {  // no empty slot: the freed ones, sorted
+            if (tid == 0)
+                for (int i = 1; i < n_ev; ++i)
+                    for (int j = i; j > 0 && s_fill_slot[j - 1] > s_fill_slot[j]; --j) {
+                        const int t = s_fill_slot[j];
+                        s_fill_slot[j] = s_fill_slot[j - 1];
+                        s_fill_slot[j - 1] = t;
+                    }
+            __syncthreads();
+        } else {
+            int mine_empty = 0;
+            for (int sl = s_lo; sl < s_hi; ++sl) mine_empty += s_key[sl] < 0;
+            int incl = mine_empty;
+#pragma unroll
+            for (int s = 1; s < 64; s <<= 1) {
+                const int o = __shfl_up(incl, s, 64);
+                if (lane >= s) incl += o;
+            }
+            if (lane == 63) red[wave] = incl;
+            __syncthreads();
+            int r0 = incl - mine_empty;
+            for (int i = 0; i < wave; ++i) r0 += red[i];
+            for (int sl = s_lo; sl < s_hi && r0 < q_fill; ++sl)
+                if (s_key[sl] < 0) s_fill_slot[r0++] = sl;
             __syncthreads();
         }
-        // empty and freed slots in ascending order go to the fills in rank order
-        int mine_empty = 0;
-        for (int sl = s_lo; sl < s_hi; ++sl) mine_empty += s_key[sl] < 0;
-        int incl = mine_empty;
-#pragma unroll
-        for (int s = 1; s < 64; s <<= 1) {
-            const int o = __shfl_up(incl, s, 64);
-            if (lane >= s) incl += o;
-        }
-        if (lane == 63) red[wave] = incl;
-        __syncthreads();
-        int r0 = incl - mine_empty;
-        for (int i = 0; i < wave; ++i) r0 += red[i];
-        for (int sl = s_lo; sl < s_hi && r0 < q_fill; ++sl)
-            if (s_key[sl] < 0) s_fill_slot[r0++] = sl;
-        __syncthreads();
         if (miss && rank < q_fill && s_fill_slot[rank] >= 0) {
             const int sl = s_fill_slot[rank];
             g_slot_key[sl] = key;
@@ -654,6 +697,43 @@ __global__ __launch_bounds__(kThreads1) void k_plan1(
     }
 }
 
+__global__ __launch_bounds__(kThreads1) void k_plan1(
+    int layer, const int32_t* ids_in, const float* w_in, const uint8_t* __restrict__ x,
+    int x_bytes, int k, int E, int C, int32_t* __restrict__ g_slot_key,
+    int64_t* __restrict__ g_slot_stamp, int32_t* __restrict__ key2slot,
+    DevState* __restrict__ st, DevPlan* __restrict__ dp, DevPlan* __restrict__ hp,
+    int32_t* __restrict__ h_ids, float* __restrict__ h_w, uint8_t* __restrict__ h_x,
+    PlanRoute rt) {
+    extern __shared__ int64_t smem64[];
+    plan1_body(smem64, layer, ids_in, w_in, x, x_bytes, k, E, C, g_slot_key, g_slot_stamp,
+               key2slot, st, dp, hp, h_ids, h_w, h_x, rt);
+}
+
+// Layer entry and one-token plan in one launch. Every workgroup runs the
+// entry (residual, norm, its experts' logits); the last one to finish, found
+// with a ticket counter after a device-scope release of its logits, runs the
+// plan on the complete logit vector. No workgroup waits for another, and the
+// last one resets the counter for the next launch.
+__global__ __launch_bounds__(kThreads1) void k_entry_plan1(
+    EntryArgs ea, int layer, int k, int C, int32_t* __restrict__ g_slot_key,
+    int64_t* __restrict__ g_slot_stamp, int32_t* __restrict__ key2slot,
+    DevState* __restrict__ st, DevPlan* __restrict__ dp, DevPlan* __restrict__ hp,
+    int32_t* __restrict__ h_ids, float* __restrict__ h_w, uint8_t* __restrict__ h_x,
+    PlanRoute rt) {
+    extern __shared__ int64_t smem64[];
+    __shared__ int s_last;
+    entry_body(ea, (float*)smem64);
+    __threadfence();  // this workgroup's logits (and workgroup 0's u) reach device scope
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomicAdd(&st->ticket, 1) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();  // acquire: every other workgroup's logits are visible
+    if (threadIdx.x == 0) st->ticket = 0;
+    plan1_body(smem64, layer, nullptr, nullptr, (const uint8_t*)ea.u, ea.H * 2, k, ea.E, C,
+               g_slot_key, g_slot_stamp, key2slot, st, dp, hp, h_ids, h_w, h_x, rt);
+}
+
 }  // namespace
 
 int plan_max_slots() { return kMaxSlotsLds; }
@@ -687,6 +767,30 @@ hipError_t launch_plan(int layer, const int32_t* ids, const float* w, const void
     k_plan<<<1, kThreads, lds, s>>>(layer, ids, w, (const uint8_t*)x, (int)x_bytes, T, k, E,
                                     (int)C, slot_key, slot_stamp, key2slot, st, d_plan, h_plan,
                                     h_ids, h_w, (uint8_t*)h_x, rt);
+    return hipGetLastError();
+}
+
+bool entry_plan_ok(int T, int k, int E, int H, int64_t C, int act_bf16) {
+    return T == 1 && k <= 64 && C <= kMaxSlotsLds && entry_ok(E, H, act_bf16);
+}
+
+hipError_t launch_entry_plan(const EntryArgs& a, int layer, int k, int64_t C, int32_t* slot_key,
+                             int64_t* slot_stamp, int32_t* key2slot, DevState* st,
+                             DevPlan* d_plan, DevPlan* h_plan, int32_t* h_ids, float* h_w,
+                             void* h_x, hipStream_t s, PlanRoute rt) {
+    if (!rt.z || rt.z != a.z || !entry_plan_ok(1, k, a.E, a.H, C, 1)) return hipErrorInvalidValue;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_entry_plan1,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)std::max<size_t>(12 * kMaxSlotsLds, 4 * 16384));
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const size_t lds = std::max<size_t>(12 * (size_t)C, 4 * (size_t)a.H);
+    k_entry_plan1<<<a.E / 4, kThreads1, lds, s>>>(a, layer, k, (int)C, slot_key, slot_stamp,
+                                                   key2slot, st, d_plan, h_plan, h_ids, h_w,
+                                                   (uint8_t*)h_x, rt);
     return hipGetLastError();
 }
 

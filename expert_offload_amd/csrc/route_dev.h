@@ -57,27 +57,36 @@ __device__ __forceinline__ void topk_select(const float* __restrict__ zt, int E,
     }
 }
 
-// All 64 lanes of the wavefront call this; lane 0 writes ids[0..k) and w[0..k).
+// All 64 lanes of the wavefront call this; lane j < k writes ids[j] and w[j].
+// w = softmax over the k selected logits: max, exponentials, their sum in
+// j order, then one division per weight.
 __device__ __forceinline__ void topk_token(const float* __restrict__ zt, int E, int k,
                                            const int32_t* __restrict__ forced_t,
                                            int32_t* __restrict__ ids_t, float* __restrict__ w_t) {
     const int lane = threadIdx.x & 63;
-    float zs[kMaxK];
-    int is[kMaxK];
+    int my_i = 0;  // lane j < k: the j-th selected expert and its logit
+    float my_z = -INFINITY;
+    __shared__ float s_zw[4][256];  // per wavefront of the workgroup (up to 4)
+    __shared__ int32_t s_selw[4][kMaxK];
+    float* s_z = s_zw[(threadIdx.x >> 6) & 3];
+    int32_t* s_sel = s_selw[(threadIdx.x >> 6) & 3];
     if (forced_t) {
-        for (int j = 0; j < k; ++j) {
-            is[j] = forced_t[j];
-            // out-of-range ids are reported by the lookup; read in bounds here
-            zs[j] = zt[min(max(is[j], 0), E - 1)];
+        // the ids and the logits are loaded together (one round trip); an
+        // out-of-range id is reported by the lookup, its logit read in bounds
+        if (lane < k) my_i = forced_t[lane];
+        if (E <= 256) {
+            for (int e = lane; e < E; e += 64) s_z[e] = zt[e];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            if (lane < k) my_z = s_z[min(max(my_i, 0), E - 1)];
+        } else if (lane < k) {
+            my_z = zt[min(max(my_i, 0), E - 1)];
         }
     } else if (E <= 256) {
         // each logit's rank = how many logits beat it (larger, or equal with a
         // smaller id); the k of rank < k are the selection, in (z desc, id asc)
         // order: the same result as k rounds of selection
-        __shared__ float s_zw[4][256];  // per wavefront of the workgroup (up to 4)
-        __shared__ int32_t s_selw[4][kMaxK];
-        float* s_z = s_zw[(threadIdx.x >> 6) & 3];
-        int32_t* s_sel = s_selw[(threadIdx.x >> 6) & 3];
         for (int e = lane; e < E; e += 64) s_z[e] = zt[e];
         if (lane < k) s_sel[lane] = -1;  // stays -1 only for unordered (NaN) logits
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -95,25 +104,30 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ zt, int E, 
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        for (int j = 0; j < k; ++j) {
-            is[j] = s_sel[j];
-            zs[j] = is[j] >= 0 ? s_z[is[j]] : -INFINITY;
+        if (lane < k) {
+            my_i = s_sel[lane];
+            my_z = my_i >= 0 ? s_z[my_i] : -INFINITY;
         }
     } else {
+        float zs[kMaxK];
+        int is[kMaxK];
         topk_select<kMaxE / 64>(zt, E, k, zs, is);
+        for (int j = 0; j < k; ++j)
+            if (lane == j) {
+                my_z = zs[j];
+                my_i = is[j];
+            }
     }
-    if (lane == 0) {
-        float zmax = zs[0];
-        for (int j = 1; j < k; ++j) zmax = fmaxf(zmax, zs[j]);
-        float ex[kMaxK], sum = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            ex[j] = expf(zs[j] - zmax);
-            sum += ex[j];
-        }
-        for (int j = 0; j < k; ++j) {
-            ids_t[j] = is[j];
-            w_t[j] = ex[j] / sum;
-        }
+    float zmax = my_z;  // lanes >= k hold -inf
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) zmax = fmaxf(zmax, __shfl_xor(zmax, m, 64));
+    const float ex = expf(my_z - zmax);
+    float sum = 0.0f;
+    for (int j = 0; j < k; ++j)
+        sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+    if (lane < k) {
+        ids_t[lane] = my_i;
+        w_t[lane] = ex / sum;
     }
 }
 

@@ -221,20 +221,28 @@ def test_decode_stack_against_oracle_chain(fmt):
         eo.eo_destroy(e)
 
 
-def _decode_capture(shape, seed, steps, forced, env):
-    """Decode `steps` tokens (fresh engine, EO_FUSED_ENTRY=env); returns the
-    final streams and every capture as bytes."""
+def _decode_capture(shape, seed, steps, forced, env, cache_slots=7):
+    """Decode `steps` tokens on a fresh engine with EO_FUSED_ENTRY=env (a string)
+    or with the variables of env (a dict) set throughout; returns the final
+    streams, every capture as bytes, the statistics and the cache snapshot."""
     import os
     L, k, H = shape.layers, shape.top_k, shape.hidden
-    old = os.environ.get("EO_FUSED_ENTRY")
-    os.environ["EO_FUSED_ENTRY"] = env
+    env = {"EO_FUSED_ENTRY": env} if isinstance(env, str) else env
+    saved = {v: os.environ.get(v) for v in env}
+    os.environ.update(env)
     try:
-        e = make_engine(shape, seed, cache_slots=7, max_tokens=1)
+        return _decode_capture_run(shape, seed, steps, forced, cache_slots)
     finally:
-        if old is None:
-            del os.environ["EO_FUSED_ENTRY"]
-        else:
-            os.environ["EO_FUSED_ENTRY"] = old
+        for v, old in saved.items():
+            if old is None:
+                del os.environ[v]
+            else:
+                os.environ[v] = old
+
+
+def _decode_capture_run(shape, seed, steps, forced, cache_slots):
+    L, k, H = shape.layers, shape.top_k, shape.hidden
+    e = make_engine(shape, seed, cache_slots=cache_slots, max_tokens=1)
     out = []
     try:
         eo.eo_set_bandwidth(e, 3, 5)
@@ -254,6 +262,9 @@ def _decode_capture(shape, seed, steps, forced, env):
                         cx.cpu().numpy().view(np.uint16).copy(), cy.cpu().numpy().copy(),
                         ci.cpu().numpy().copy(), cw.cpu().numpy().copy()))
         out.append(eo.eo_stats_get(e))
+        keys = np.zeros(max(cache_slots, 1), dtype=np.int32)
+        stamps = np.zeros(max(cache_slots, 1), dtype=np.int64)
+        out.append((eo.eo_cache_snapshot(e, keys, stamps), keys.tolist(), stamps.tolist()))
     finally:
         eo.eo_destroy(e)
     return out
@@ -270,7 +281,22 @@ def test_decode_fused_entry_matches_separate_kernels(forced):
     for s in range(4):
         for i in range(1, 6):
             assert np.array_equal(a[s][i], b[s][i]), (s, i)
-    assert a[-1] == b[-1]
+    assert a[-2:] == b[-2:]
+
+
+@pytest.mark.parametrize("experts,top_k,slots", [(16, 4, 7), (128, 8, 90), (128, 8, 0)])
+@pytest.mark.parametrize("forced", [True, False])
+def test_decode_entry_and_plan_in_one_launch(experts, top_k, slots, forced):
+    # the layer entry and the one-token plan in one launch (the last workgroup
+    # to finish its logits plans) against separate entry and plan launches:
+    # streams, captures, routed ids, statistics and the slot table identical
+    shape = dataclasses.replace(small_shape("bf16", layers=3), experts=experts, top_k=top_k)
+    a = _decode_capture(shape, 15, 5, forced, {"EO_ENTRY_PLAN": "1"}, slots)
+    b = _decode_capture(shape, 15, 5, forced, {"EO_ENTRY_PLAN": "0"}, slots)
+    for s in range(5):
+        for i in range(1, 6):
+            assert np.array_equal(a[s][i], b[s][i]), (s, i)
+    assert a[-2:] == b[-2:]
 
 
 def test_decode_routed_ids_bit_exact():

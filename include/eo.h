@@ -201,7 +201,15 @@ eo_status eo_moe_layer(eo_engine* e, int32_t layer, const void* x, float* y, int
  * dtype) is the residual stream r: layer l takes u_l = r_l / sqrt(mean(r_l^2)
  * + 1e-6) per token (stored in the activation dtype; a parameter-free RMS
  * normalisation, as in pre-norm transformer blocks) and r_{l+1} = r_l + y_l(u_l)
- * (stored in the activation dtype). forced_ids: device [L, T, k] or NULL. */
+ * (stored in the activation dtype). forced_ids: device [L, T, k] or NULL.
+ * One token with bf16 activations runs four kernels per layer and no host wait
+ * between layers other than the plan readback for the host-list experts:
+ * layer entry + plan (one launch), fill, gate/up GEMV, down GEMV. The results
+ * do not depend on which kernels run; the environment switches EO_ENTRY_PLAN=0
+ * (entry and plan as two launches), EO_PLAN1=0 (the general plan kernel for
+ * one token), EO_FUSED_ENTRY=0 (separate norm, router and top-k kernels, read
+ * at engine creation) and EO_GEMV_FAST=0 (the generic GEMV, read at engine
+ * creation) select the alternatives that the tests compare. */
 eo_status eo_decode_step(eo_engine* e, void* x_inout, int32_t T, const int32_t* forced_ids,
                          void* stream);
 

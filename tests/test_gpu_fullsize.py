@@ -2,10 +2,10 @@
 bench.py times, on outputs the oracle can compute one by one.
 
 * bf16, 48 layers, hidden 2048, 128 experts, top-8, inter 768, 37% cache,
-  8192-token prefill capacity (the engine bench.py builds): decode steps of the
+  16384-token prefill capacity (the engine bench.py builds): decode steps of the
   bench's trace with every layer captured, the cache state bit-exact against
   the oracle's replay after each step, and sampled layers checked; then an
-  8192-token prefill, sampled tokens of sampled layers checked.
+  8192-token and a 16384-token prefill, sampled tokens of sampled layers checked.
 * MXFP4 decode (hidden 4096, 256 experts + shared, inter 2048, 11% cache) and
   NVFP4 prefill + decode (hidden 6144, 256 experts + shared, inter 2048) at full
   per-layer shape with fewer layers.
@@ -106,7 +106,7 @@ def _prefill_and_check(e, shape, seed, T, layers, ntok):
 def test_bf16_48_layers_as_benchmarked():
     shape = synth.SHAPES["decode_bf16_48L"]
     pshape = synth.SHAPES["prefill_bf16_48L"]
-    e = make_engine(shape, 0, max_tokens=pshape.tokens)
+    e = make_engine(shape, 0, max_tokens=2 * pshape.tokens)
     try:
         eo.eo_set_bandwidth(e, BP, BH)
         _decode_and_check(e, shape, 0, 6, lambda s: (0, 23, 47) if s < 5 else range(48),
@@ -114,6 +114,8 @@ def test_bf16_48_layers_as_benchmarked():
         st = eo.eo_stats_get(e)
         assert st["fills"] > 0 and st["host_experts"] > 0  # both miss lanes exercised
         _prefill_and_check(e, pshape, 0, pshape.tokens, (0, 31, 47), 24)
+        # the prefill configuration's other chunk size
+        _prefill_and_check(e, pshape, 0, 2 * pshape.tokens, (0, 47), 16)
     finally:
         eo.eo_destroy(e)
 

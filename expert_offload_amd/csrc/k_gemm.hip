@@ -598,11 +598,27 @@ bool run_v3(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hi
 // s ^ ((r >> 2) & 3). With that XOR swizzle the 16 lanes of each ds_read_b128
 // quarter (16 rows, one logical segment) hit 16 distinct 16-byte bank groups.
 // Barriers are raw s_barrier with explicit vmcnt waits, so outstanding tile
-// loads are not drained at each K step.
-constexpr int V4S = 3;                                   // stages
-constexpr size_t kV4Stage = (size_t)(V3M + V3N) * 64;     // 24 KB
-constexpr size_t kV4Pipe = V4S * kV4Stage;                // 72 KB
-constexpr size_t kV4Lds = (kV4Pipe > kV3Out ? kV4Pipe : kV3Out) + 2 * V3M * sizeof(int32_t);
+// loads are not drained at each K step, and each step's six tile loads are
+// issued between its MFMAs rather than in one burst after the barrier.
+// Two workgroups share a CU: measured on the prefill shapes, a 128 x 512 tile
+// (one workgroup per CU, 4 x 4 MFMA blocks per wavefront) and rings of 4-6
+// stages at one workgroup per CU are 7-20% slower; the second, unsynchronised
+// workgroup covers each workgroup's barrier waits.
+constexpr int kV4Ring = 3;                                // stages: two tiles in flight
+constexpr size_t kV4Stage = (size_t)(V3M + V3N) * 64;     // 24 KB per stage
+template <int S>
+constexpr size_t v4_pipe() { return S * kV4Stage; }
+template <int S>
+constexpr size_t v4_lds() {
+    return (v4_pipe<S>() > kV3Out ? v4_pipe<S>() : kV3Out) + 2 * V3M * sizeof(int32_t);
+}
+
+// Wait until at most N of this thread's vector-memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -631,11 +647,11 @@ __device__ __forceinline__ void v4_issue(const GemmArgs& a, const uint16_t* wdat
     }
 }
 
-template <int MODE>
+template <int MODE, int S>
 __global__ __launch_bounds__(256, 2) void k_gemm_v4(GemmArgs a, int nN) {
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint8_t* sb = (uint8_t*)smem;
-    int32_t* s_pair = (int32_t*)(sb + (kV4Pipe > kV3Out ? kV4Pipe : kV3Out));
+    int32_t* s_pair = (int32_t*)(sb + (v4_pipe<S>() > kV3Out ? v4_pipe<S>() : kV3Out));
     float* s_wp = (float*)(s_pair + V3M);
 
     const int real = a.tile_off[a.G] * nN;
@@ -667,8 +683,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v4(GemmArgs a, int nN) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    v4_issue<MODE>(a, wdata, m0, m_end, n0, 0, sb, wave, lane);
-    if (nk > 1) v4_issue<MODE>(a, wdata, m0, m_end, n0, V3K, sb + kV4Stage, wave, lane);
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t)
+        v4_issue<MODE>(a, wdata, m0, m_end, n0, min(t, nk - 1) * V3K, sb + t * kV4Stage, wave, lane);
 
     int arow[2], aseg[2][2];  // A rows read by this lane and their swizzled slots
 #pragma unroll
@@ -686,33 +703,47 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v4(GemmArgs a, int nN) {
         for (int ks = 0; ks < 2; ++ks) bseg[j][ks] = swz(brow_[j], 2 * ks + (lane >> 5));
     }
 
+    // Every step issues one tile (past the end, the last tile again), so
+    // S - 1 tiles are always in flight at the wait and the body is one
+    // block: the loads of tile kt + S - 1 are spread between this step's
+    // MFMAs instead of stalling the wavefront in one burst.
     for (int kt = 0; kt < nk; ++kt) {
-        // this thread's 6 loads of tile kt are done once at most the 6 of
-        // tile kt+1 are outstanding; the barrier makes every thread's visible
-        if (kt + 1 < nk)
-            __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6), expcnt/lgkmcnt not waited
-        else
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        wait_vm<(S - 2) * 6>();
         __builtin_amdgcn_s_barrier();
-        if (kt + 2 < nk)
-            v4_issue<MODE>(a, wdata, m0, m_end, n0, (kt + 2) * V3K, sb + ((kt + 2) % V4S) * kV4Stage,
-                           wave, lane);
-        const uint8_t* st = sb + (kt % V4S) * kV4Stage;
+        const uint8_t* st = sb + (kt % S) * kV4Stage;
+        bf16x8 av[2][2], bv[2][4];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 av[2], bv[4];
+        for (int i = 0; i < 2; ++i) av[0][i] = *(const bf16x8*)(st + arow[i] * 64 + aseg[i][0] * 16);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) av[i] = *(const bf16x8*)(st + arow[i] * 64 + aseg[i][ks] * 16);
+        for (int j = 0; j < 4; ++j)
+            bv[0][j] = *(const bf16x8*)(st + V3M * 64 + brow_[j] * 64 + bseg[j][0] * 16);
+        v4_issue<MODE>(a, wdata, m0, m_end, n0, min(kt + S - 1, nk - 1) * V3K,
+                       sb + ((kt + S - 1) % S) * kV4Stage, wave, lane);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bv[j] = *(const bf16x8*)(st + V3M * 64 + brow_[j] * 64 + bseg[j][ks] * 16);
+        for (int i = 0; i < 2; ++i) av[1][i] = *(const bf16x8*)(st + arow[i] * 64 + aseg[i][1] * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            bv[1][j] = *(const bf16x8*)(st + V3M * 64 + brow_[j] * 64 + bseg[j][1] * 16);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks][i], bv[ks][j],
+                                                                        acc[i][j], 0, 0, 0);
+        // order: first half step's 6 operand reads; then 6 x (MFMA, tile
+        // load, operand read of the second half); then the other 10 MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int q = 0; q < 6; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
     }
+    wait_vm<0>();
     __syncthreads();  // all tile loads landed and all LDS reads done: reuse as the epilogue tile
 
     uint16_t* ot = smem;
@@ -763,29 +794,31 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v4(GemmArgs a, int nN) {
     }
 }
 
+template <int S>
 bool run_v4(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hipEvent_t* ev) {
+    static_assert(v4_lds<S>() <= 160 * 1024, "v4 LDS");
     if (I % 128 || H % 256 || H % V3K || I % V3K) return false;
     static bool attr = false;
     if (!attr) {
-        if (hipFuncSetAttribute((const void*)k_gemm_v4<0>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kV4Lds) != hipSuccess ||
-            hipFuncSetAttribute((const void*)k_gemm_v4<1>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kV4Lds) != hipSuccess)
+        if (hipFuncSetAttribute((const void*)k_gemm_v4<0, S>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, v4_lds<S>()) != hipSuccess ||
+            hipFuncSetAttribute((const void*)k_gemm_v4<1, S>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, v4_lds<S>()) != hipSuccess)
             return false;
         attr = true;
     }
     const int n1 = I / 128, n2 = H / 256;
     auto grid = [&](int nN) { return ((tiles * nN + 7) / 8) * 8; };
-    hipExtLaunchKernelGGL(k_gemm_v4<0>, dim3(grid(n1)), dim3(256), (uint32_t)kV4Lds, s, ev[0],
-                          ev[1], 0, a1, n1);
-    hipExtLaunchKernelGGL(k_gemm_v4<1>, dim3(grid(n2)), dim3(256), (uint32_t)kV4Lds, s, ev[2],
-                          ev[3], 0, a2, n2);
+    hipExtLaunchKernelGGL((k_gemm_v4<0, S>), dim3(grid(n1)), dim3(256), (uint32_t)v4_lds<S>(), s,
+                          ev[0], ev[1], 0, a1, n1);
+    hipExtLaunchKernelGGL((k_gemm_v4<1, S>), dim3(grid(n2)), dim3(256), (uint32_t)v4_lds<S>(), s,
+                          ev[2], ev[3], 0, a2, n2);
     return true;
 }
 
 template <int FMT>
 void run_mfma(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hipEvent_t* ev) {
-    if (FMT == EO_W_BF16 && g_gemm_tiles >= 2 && run_v4(a1, a2, tiles, I, H, s, ev)) return;
+    if (FMT == EO_W_BF16 && g_gemm_tiles >= 2 && run_v4<kV4Ring>(a1, a2, tiles, I, H, s, ev)) return;
     if (g_gemm_tiles && run_v3<FMT>(a1, a2, tiles, I, H, s, ev)) return;
     hipExtLaunchKernelGGL(k_gemm_mfma<FMT, 0>, dim3(tiles, I / 64), dim3(256), 0, s, ev[0], ev[1],
                           0, a1);

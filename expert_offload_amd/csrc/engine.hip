@@ -199,7 +199,7 @@ eo_status ensure_gemm(eo_engine* e, int T, hipStream_t s) {
     HIPCHK(hipStreamSynchronize(s));
     auto fr = [](void* p) { if (p) (void)hipFree(p); };
     fr(e->pb.counts); fr(e->pb.offsets); fr(e->pb.tile_off); fr(e->pb.perm_pair);
-    fr(e->pb.chunk_cnt); fr(e->pb.x_perm); fr(e->d_hbuf); fr(e->d_opairs);
+    fr(e->pb.chunk_cnt); fr(e->d_hbuf); fr(e->d_opairs);
     e->pb = PermuteBufs{};
     e->d_hbuf = nullptr;
     e->d_opairs = nullptr;
@@ -211,7 +211,6 @@ eo_status ensure_gemm(eo_engine* e, int T, hipStream_t s) {
     HIPCHK(hipMalloc(&e->pb.tile_off, sizeof(int32_t) * (e->E + 2)));
     HIPCHK(hipMalloc(&e->pb.perm_pair, sizeof(int32_t) * P));
     HIPCHK(hipMalloc(&e->pb.chunk_cnt, sizeof(int32_t) * nchunks * e->E));
-    HIPCHK(hipMalloc(&e->pb.x_perm, (size_t)e->act_size * P * e->H));
     HIPCHK(hipMalloc(&e->d_hbuf, sizeof(float) * P * e->I));
     HIPCHK(hipMalloc(&e->d_opairs, sizeof(float) * P * e->H));
     e->gemm_T = T;
@@ -426,11 +425,10 @@ eo_status do_ffn_device(eo_engine* e, int layer, const void* x, const int32_t* i
         if (e->timing) e->gemv_ev.push_back(ts);
     } else {
         EOCHK(ensure_gemm(e, T, s));
-        he = launch_permute(ids, e->d_plan->e2slot, 0, T, e->k, e->E, e->shared, x, e->act_bf16,
-                            e->H, e->pb, s);
+        he = launch_permute(ids, e->d_plan->e2slot, 0, T, e->k, e->E, e->shared, e->pb, s);
         if (he == hipSuccess)
             he = launch_ffn_gemm(e->fmt, e->lay, gw, e->E, e->shared, e->H, e->I,
-                                 T * e->k + T, e->pb.offsets, e->pb.tile_off, e->pb.x_perm,
+                                 T * e->k + T, e->pb.offsets, e->pb.tile_off, x,
                                  e->d_hbuf, e->pb.perm_pair, ids, w, e->k, T, e->d_opairs, s,
                                  ev ? ev : none);
         if (e->timing) e->gemm_ev.push_back(ts);
@@ -564,7 +562,7 @@ void destroy_all(eo_engine* e) {
     fr(e->d_key2slot); fr(e->d_state); fr(e->d_plan); fr(e->d_ids); fr(e->d_w); fr(e->d_z);
     fr(e->d_y); fr(e->d_u); fr(e->d_r); fr(e->d_hgemv); fr(e->d_yparts); fr(e->d_yhost);
     fr(e->pb.counts); fr(e->pb.offsets); fr(e->pb.tile_off); fr(e->pb.perm_pair);
-    fr(e->pb.chunk_cnt); fr(e->pb.x_perm); fr(e->d_hbuf); fr(e->d_opairs);
+    fr(e->pb.chunk_cnt); fr(e->d_hbuf); fr(e->d_opairs);
     fr(e->d_staging[0]); fr(e->d_staging[1]); fr((void*)e->d_gbase);
     fh(e->h_plan); fh(e->h_ids); fh(e->h_w); fh(e->h_x); fh(e->h_yhost);
     if (e->copy_stream) (void)hipStreamDestroy(e->copy_stream);
@@ -1075,8 +1073,7 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t flags, void
         he = launch_route(e->d_u, e->act_bf16, e->d_router + roff, e->d_router_t + roff, T, e->E,
                           e->H, e->k, nullptr, ids, w, e->d_z, e->d_xt, s);
         if (he == hipSuccess)
-            he = launch_permute(ids, nullptr, 1, T, e->k, e->E, e->shared, e->d_u, e->act_bf16,
-                                e->H, e->pb, s);
+            he = launch_permute(ids, nullptr, 1, T, e->k, e->E, e->shared, e->pb, s);
         TimedSet ts{};
         if (e->timing) EOCHK(get_set(e, &ts));
         hipEvent_t none[4] = {nullptr, nullptr, nullptr, nullptr};
@@ -1088,7 +1085,7 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t flags, void
             gw.shared_w = e->shared ? e->d_shared + (uint64_t)l * e->S_pad : nullptr;
             gw.gbase = skip ? e->d_gbase + (size_t)l * e->E : nullptr;
             he = launch_ffn_gemm(e->fmt, e->lay, gw, e->E, e->shared, e->H, e->I, T * e->k + T,
-                                 e->pb.offsets, e->pb.tile_off, e->pb.x_perm, e->d_hbuf,
+                                 e->pb.offsets, e->pb.tile_off, e->d_u, e->d_hbuf,
                                  e->pb.perm_pair, ids, w, e->k, T, e->d_opairs, s,
                                  e->timing ? ts.ev : none);
         }

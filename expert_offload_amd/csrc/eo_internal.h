@@ -105,18 +105,17 @@ hipError_t launch_copy_expert(const uint8_t* src_dev, uint8_t* dst, uint64_t S, 
 
 // Permute: group the (token, k) pairs whose expert is resident by expert,
 // stable in pair order; the shared expert (when present) is group E holding
-// every token. Produces offsets [E+2], tile offsets, perm_pair, x_perm.
+// every token. Produces offsets [E+2], tile offsets and perm_pair; the grouped
+// GEMM gathers each permuted row's input row through perm_pair itself.
 struct PermuteBufs {
     int32_t* counts;     // [E+1]
     int32_t* offsets;    // [E+2]
     int32_t* tile_off;   // [E+2], tiles of kTileM rows per group
     int32_t* perm_pair;  // [P_max], pair index t*k+j (shared rows: T*k + t)
     int32_t* chunk_cnt;  // [nchunks, E]
-    void* x_perm;        // [P_max, H]
 };
 hipError_t launch_permute(const int32_t* ids, const int32_t* e2slot, int all_resident, int T,
-                          int k, int E, int has_shared, const void* x, int act_bf16, int H,
-                          PermuteBufs b, hipStream_t s);
+                          int k, int E, int has_shared, PermuteBufs b, hipStream_t s);
 
 // Grouped SwiGLU FFN (GEMM path). Weight base of group g: shared_w for g == E,
 // else (e2slot ? slots + e2slot[g]*stride : slots + g*stride).
@@ -129,7 +128,8 @@ struct GroupW {
 };
 hipError_t launch_ffn_gemm(int fmt, const Layout& lay, GroupW gw, int E, int has_shared, int H,
                            int I, int P_max, const int32_t* offsets, const int32_t* tile_off,
-                           const void* x_perm, void* h_buf, const int32_t* perm_pair,
+                           const void* x /*[T, H] layer input*/, void* h_buf,
+                           const int32_t* perm_pair,
                            const int32_t* ids, const float* w, int k, int T, void* o_pairs,
                            hipStream_t s,
                            hipEvent_t* ev /*[4]: start/stop of each kernel, entries may be null*/);

@@ -1,6 +1,7 @@
 // Grouped SwiGLU expert FFN for many tokens (prefill, and any call with T > 1).
 //
-// Per expert e with its M_e permuted rows X_e (bf16):
+// Per expert e with its M_e grouped rows X_e (bf16; each row is read from the
+// layer input through perm_pair, so the input is never copied in grouped order):
 //   GEMM1: G = X_e . W13^T, h = silu(G_gate) * G_up  -> bf16 [M_e, I]
 //   GEMM2: O = h . W2^T, scaled by the pair's routing weight -> o_pairs (bf16;
 //          fp32 on the fp32-weight path)
@@ -47,13 +48,23 @@ struct GemmArgs {
     int H, I;
     const int32_t* offsets;
     const int32_t* tile_off;
-    const uint16_t* A;    // [rows, K] bf16
+    const uint16_t* A;    // GEMM1: layer input [T, H]; GEMM2: h [rows, I]
     uint16_t* h_out;      // GEMM1 output [rows, I] bf16
     const int32_t* perm_pair;
     const float* w;
-    int Tk;
+    int Tk, k;
     void* o_pairs;        // GEMM2 output [Tk + T, H]: bf16 (MFMA path) or fp32
 };
+
+// Row of A that grouped row r multiplies. GEMM1 reads the layer input row of the
+// token of r's (token, slot) pair, or of the token itself for a shared-expert
+// row, so no permuted copy of the input is made; GEMM2 reads row r of h.
+template <int MODE>
+__device__ __forceinline__ int a_row(const GemmArgs& a, int r) {
+    if (MODE == 1) return r;
+    const int pair = a.perm_pair[r];
+    return pair < a.Tk ? pair / a.k : pair - a.Tk;
+}
 
 __device__ __forceinline__ int find_group(const int32_t* tile_off, int G, int tile) {
     int lo = 0, hi = G;  // tile_off[lo] <= tile < tile_off[hi]
@@ -133,7 +144,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
             int c = tid + 256 * it, r = c >> 3, seg = c & 7;
             uint4 v = make_uint4(0, 0, 0, 0);
             if (m0 + r < m_end)
-                v = *(const uint4*)(a.A + (size_t)(m0 + r) * K + k0 + seg * 8);
+                v = *(const uint4*)(a.A + (size_t)a_row<MODE>(a, m0 + r) * K + k0 + seg * 8);
             *(uint4*)(As + r * LDK + seg * 8) = v;
         }
         // B tile: 128 weight rows x 64 elements, decoded to bf16
@@ -271,7 +282,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs a, const float* __res
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
             int c = tid + 256 * it, r = c >> 4, kk = c & 15;
-            As[kk][r] = (m0 + r < m_end) ? Af[(size_t)(m0 + r) * K + k0 + kk] : 0.0f;
+            As[kk][r] = (m0 + r < m_end) ? Af[(size_t)a_row<MODE>(a, m0 + r) * K + k0 + kk] : 0.0f;
         }
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
@@ -357,7 +368,7 @@ __device__ __forceinline__ void v3_load(const GemmArgs& a, const uint8_t* wdata,
     for (int it = 0; it < 2; ++it) {  // A: 128 rows x 32 bf16 = 512 chunks
         int c = tid + 256 * it, row = c >> 2, seg = c & 3;
         r.a[it] = (m0 + row < m_end)
-                      ? *(const uint4*)(a.A + (size_t)(m0 + row) * K + k0 + seg * 8)
+                      ? *(const uint4*)(a.A + (size_t)a_row<MODE>(a, m0 + row) * K + k0 + seg * 8)
                       : make_uint4(0, 0, 0, 0);
     }
     if (FMT == EO_W_BF16) {  // B: 256 rows x 32 bf16 = 1024 chunks
@@ -608,9 +619,16 @@ constexpr int kV4Ring = 3;                                // stages: two tiles i
 constexpr size_t kV4Stage = (size_t)(V3M + V3N) * 64;     // 24 KB per stage
 template <int S>
 constexpr size_t v4_pipe() { return S * kV4Stage; }
-template <int S>
+// Epilogue tile row stride: at three workgroups per CU (OCC 3) the down
+// kernel's 128 x 256 outputs leave through LDS in two 128-column halves.
+template <int OCC>
+constexpr int v4_old() { return OCC >= 3 ? 128 + 8 : V3_OUT_LD; }
+template <int S, int OCC>
+constexpr size_t v4_out() { return (size_t)V3M * v4_old<OCC>() * sizeof(uint16_t); }
+template <int S, int OCC>
 constexpr size_t v4_lds() {
-    return (v4_pipe<S>() > kV3Out ? v4_pipe<S>() : kV3Out) + 2 * V3M * sizeof(int32_t);
+    return (v4_pipe<S>() > v4_out<S, OCC>() ? v4_pipe<S>() : v4_out<S, OCC>()) +
+           2 * V3M * sizeof(int32_t);
 }
 
 // Wait until at most N of this thread's vector-memory loads are outstanding.
@@ -624,19 +642,29 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int swz(int row, int seg) { return seg ^ ((row >> 2) & 3); }
 
+// This lane's two A source rows (tile rows (it*4 + wave)*16 + lane/4, rows past
+// the group's end repeat its last row), at the lane's swizzled segment.
 template <int MODE>
-__device__ __forceinline__ void v4_issue(const GemmArgs& a, const uint16_t* wdata, int m0,
-                                         int m_end, int n0, int k0, uint8_t* stage, int wave,
-                                         int lane) {
+__device__ __forceinline__ void v4_arows(const GemmArgs& a, int m0, int m_end, int wave, int lane,
+                                         const uint16_t* (&ap)[2]) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int row = (it * 4 + wave) * 16 + (lane >> 2);
+        const int gr = min(m0 + row, m_end - 1);
+        ap[it] = a.A + (size_t)a_row<MODE>(a, gr) * a.K + swz(row, lane & 3) * 8;
+    }
+}
+
+template <int MODE>
+__device__ __forceinline__ void v4_issue(const GemmArgs& a, const uint16_t* wdata,
+                                         const uint16_t* const (&ap)[2], int n0, int k0,
+                                         uint8_t* stage, int wave, int lane) {
     const int K = a.K;
     const int lrow = lane >> 2, slot = lane & 3;
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {  // A: 8 x 1 KB, rows (it*4 + wave)*16 ..
-        const int row = (it * 4 + wave) * 16 + lrow;
-        const int gr = min(m0 + row, m_end - 1);
-        const uint16_t* src = a.A + (size_t)gr * K + k0 + swz(row, slot) * 8;
-        __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + (it * 4 + wave) * 1024), 16, 0, 0);
-    }
+    for (int it = 0; it < 2; ++it)  // A: 8 x 1 KB, rows (it*4 + wave)*16 ..
+        __builtin_amdgcn_global_load_lds(ap[it] + k0, (lds_void*)(stage + (it * 4 + wave) * 1024),
+                                         16, 0, 0);
 #pragma unroll
     for (int it = 0; it < 4; ++it) {  // B: 16 x 1 KB
         const int row = (it * 4 + wave) * 16 + lrow;
@@ -647,11 +675,14 @@ __device__ __forceinline__ void v4_issue(const GemmArgs& a, const uint16_t* wdat
     }
 }
 
-template <int MODE, int S>
-__global__ __launch_bounds__(256, 2) void k_gemm_v4(GemmArgs a, int nN) {
+template <int MODE, int S, int OCC>
+__global__ __launch_bounds__(256, OCC) void k_gemm_v4(GemmArgs a, int nN) {
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint8_t* sb = (uint8_t*)smem;
-    int32_t* s_pair = (int32_t*)(sb + (v4_pipe<S>() > kV3Out ? v4_pipe<S>() : kV3Out));
+    int32_t* s_pair =
+        (int32_t*)(sb + (v4_pipe<S>() > v4_out<S, OCC>() ? v4_pipe<S>() : v4_out<S, OCC>()));
+    constexpr int OLD = v4_old<OCC>();
+    constexpr bool HALF = OCC >= 3;
     float* s_wp = (float*)(s_pair + V3M);
 
     const int real = a.tile_off[a.G] * nN;
@@ -683,9 +714,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v4(GemmArgs a, int nN) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+    const uint16_t* ap[2];
+    v4_arows<MODE>(a, m0, m_end, wave, lane, ap);
 #pragma unroll
     for (int t = 0; t < S - 1; ++t)
-        v4_issue<MODE>(a, wdata, m0, m_end, n0, min(t, nk - 1) * V3K, sb + t * kV4Stage, wave, lane);
+        v4_issue<MODE>(a, wdata, ap, n0, min(t, nk - 1) * V3K, sb + t * kV4Stage, wave, lane);
 
     int arow[2], aseg[2][2];  // A rows read by this lane and their swizzled slots
 #pragma unroll
@@ -717,7 +750,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v4(GemmArgs a, int nN) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             bv[0][j] = *(const bf16x8*)(st + V3M * 64 + brow_[j] * 64 + bseg[j][0] * 16);
-        v4_issue<MODE>(a, wdata, m0, m_end, n0, min(kt + S - 1, nk - 1) * V3K,
+        v4_issue<MODE>(a, wdata, ap, n0, min(kt + S - 1, nk - 1) * V3K,
                        sb + ((kt + S - 1) % S) * kV4Stage, wave, lane);
 #pragma unroll
         for (int i = 0; i < 2; ++i) av[1][i] = *(const bf16x8*)(st + arow[i] * 64 + aseg[i][1] * 16);
@@ -757,7 +790,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v4(GemmArgs a, int nN) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                    ot[row * V3_OUT_LD + c] =
+                    ot[row * OLD + c] =
                         (uint16_t)f32_bf16_rne(silu_f32(acc[i][jj][v]) * acc[i][2 + jj][v]);
                 }
         }
@@ -767,58 +800,70 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v4(GemmArgs a, int nN) {
             int cidx = tid + 256 * it, row = cidx >> 4, seg = cidx & 15;
             if (m0 + row < m_end)
                 *(uint4*)(a.h_out + (size_t)(m0 + row) * a.I + n0 + seg * 8) =
-                    *(const uint4*)(ot + row * V3_OUT_LD + seg * 8);
+                    *(const uint4*)(ot + row * OLD + seg * 8);
         }
     } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = wn * 128 + j * 32 + col;
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                    ot[row * V3_OUT_LD + c] = (uint16_t)f32_bf16_rne(acc[i][j][v] * s_wp[row]);
-                }
-        }
-        __syncthreads();
+        constexpr int NH = HALF ? 2 : 1, CW = 256 / NH;  // column passes and their width
         uint16_t* op = (uint16_t*)a.o_pairs;
 #pragma unroll
-        for (int it = 0; it < 16; ++it) {
-            int cidx = tid + 256 * it, row = cidx >> 5, seg = cidx & 31;
-            int pair = s_pair[row];
-            if (pair >= 0)
-                *(uint4*)(op + (size_t)pair * a.H + n0 + seg * 8) =
-                    *(const uint4*)(ot + row * V3_OUT_LD + seg * 8);
+        for (int h = 0; h < NH; ++h) {
+            if (!HALF || wn == h) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = (HALF ? 0 : wn * 128) + j * 32 + col;
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                            ot[row * OLD + c] = (uint16_t)f32_bf16_rne(acc[i][j][v] * s_wp[row]);
+                        }
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int it = 0; it < V3M * (CW / 8) / 256; ++it) {
+                int cidx = tid + 256 * it, row = cidx / (CW / 8), seg = cidx % (CW / 8);
+                int pair = s_pair[row];
+                if (pair >= 0)
+                    *(uint4*)(op + (size_t)pair * a.H + n0 + h * CW + seg * 8) =
+                        *(const uint4*)(ot + row * OLD + seg * 8);
+            }
+            if (h + 1 < NH) __syncthreads();  // the next pass overwrites the tile
         }
     }
 }
 
-template <int S>
+template <int S, int OCC>
 bool run_v4(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hipEvent_t* ev) {
-    static_assert(v4_lds<S>() <= 160 * 1024, "v4 LDS");
+    static_assert(OCC * v4_lds<S, OCC>() <= 160 * 1024, "v4 LDS");
     if (I % 128 || H % 256 || H % V3K || I % V3K) return false;
     static bool attr = false;
     if (!attr) {
-        if (hipFuncSetAttribute((const void*)k_gemm_v4<0, S>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, v4_lds<S>()) != hipSuccess ||
-            hipFuncSetAttribute((const void*)k_gemm_v4<1, S>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, v4_lds<S>()) != hipSuccess)
+        if (hipFuncSetAttribute((const void*)k_gemm_v4<0, S, OCC>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, v4_lds<S, OCC>()) != hipSuccess ||
+            hipFuncSetAttribute((const void*)k_gemm_v4<1, S, OCC>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, v4_lds<S, OCC>()) != hipSuccess)
             return false;
         attr = true;
     }
     const int n1 = I / 128, n2 = H / 256;
     auto grid = [&](int nN) { return ((tiles * nN + 7) / 8) * 8; };
-    hipExtLaunchKernelGGL((k_gemm_v4<0, S>), dim3(grid(n1)), dim3(256), (uint32_t)v4_lds<S>(), s,
-                          ev[0], ev[1], 0, a1, n1);
-    hipExtLaunchKernelGGL((k_gemm_v4<1, S>), dim3(grid(n2)), dim3(256), (uint32_t)v4_lds<S>(), s,
-                          ev[2], ev[3], 0, a2, n2);
+    hipExtLaunchKernelGGL((k_gemm_v4<0, S, OCC>), dim3(grid(n1)), dim3(256),
+                          (uint32_t)v4_lds<S, OCC>(), s, ev[0], ev[1], 0, a1, n1);
+    hipExtLaunchKernelGGL((k_gemm_v4<1, S, OCC>), dim3(grid(n2)), dim3(256),
+                          (uint32_t)v4_lds<S, OCC>(), s, ev[2], ev[3], 0, a2, n2);
     return true;
 }
 
 template <int FMT>
 void run_mfma(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hipEvent_t* ev) {
-    if (FMT == EO_W_BF16 && g_gemm_tiles >= 2 && run_v4<kV4Ring>(a1, a2, tiles, I, H, s, ev)) return;
+    if (FMT == EO_W_BF16 && g_gemm_tiles >= 2) {
+        bool ok = false;
+        if (g_gemm_tiles == 3) ok = run_v4<2, 3>(a1, a2, tiles, I, H, s, ev);
+        if (g_gemm_tiles == 4) ok = run_v4<2, 2>(a1, a2, tiles, I, H, s, ev);
+        if (ok || run_v4<kV4Ring, 2>(a1, a2, tiles, I, H, s, ev)) return;
+    }
     if (g_gemm_tiles && run_v3<FMT>(a1, a2, tiles, I, H, s, ev)) return;
     hipExtLaunchKernelGGL(k_gemm_mfma<FMT, 0>, dim3(tiles, I / 64), dim3(256), 0, s, ev[0], ev[1],
                           0, a1);
@@ -830,7 +875,7 @@ void run_mfma(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, 
 
 hipError_t launch_ffn_gemm(int fmt, const Layout& lay, GroupW gw, int E, int has_shared, int H,
                            int I, int P_max, const int32_t* offsets, const int32_t* tile_off,
-                           const void* x_perm, void* h_buf, const int32_t* perm_pair,
+                           const void* x, void* h_buf, const int32_t* perm_pair,
                            const int32_t* ids, const float* w, int k, int T, void* o_pairs,
                            hipStream_t s, hipEvent_t* ev) {
     (void)ids;
@@ -851,17 +896,18 @@ hipError_t launch_ffn_gemm(int fmt, const Layout& lay, GroupW gw, int E, int has
     a1.perm_pair = perm_pair;
     a1.w = w;
     a1.Tk = T * k;
+    a1.k = k;
     a1.o_pairs = o_pairs;
     GemmArgs a2 = a1;
     a1.K = H;
-    a1.A = (const uint16_t*)x_perm;
+    a1.A = (const uint16_t*)x;
     a1.h_out = (uint16_t*)h_buf;
     a2.K = I;
     a2.A = (const uint16_t*)h_buf;
     switch (fmt) {
     case EO_W_FP32:
         hipExtLaunchKernelGGL(k_gemm_f32<0>, dim3(tiles, I / 32), dim3(256), 0, s, ev[0], ev[1],
-                              0, a1, (const float*)x_perm, (float*)h_buf);
+                              0, a1, (const float*)x, (float*)h_buf);
         hipExtLaunchKernelGGL(k_gemm_f32<1>, dim3(tiles, H / 64), dim3(256), 0, s, ev[2], ev[3], 0,
                               a2, (const float*)h_buf, (float*)nullptr);
         break;

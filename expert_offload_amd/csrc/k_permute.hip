@@ -3,7 +3,8 @@
 //
 // Grouped expert execution needs each expert's tokens contiguous: the (token,
 // slot) pairs whose expert is device-resident are grouped by expert, stable in
-// pair order (t*k + j), and their rows of X gathered into x_perm. The shared
+// pair order (t*k + j), into perm_pair; the grouped GEMM reads each grouped
+// row's input row of X through it (no permuted copy of X is made). The shared
 // expert (papers.ananclaw.com explainer, "core method" section 4, names it as
 // an architecture axis) is one more group holding every token. After the
 // grouped FFN, each pair's weighted output sits at o_pairs[t*k + j] (shared:
@@ -79,17 +80,13 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ chunk_cnt, 
 // its destination row; rows of x are copied by whole wavefronts (16 B/lane).
 __global__ __launch_bounds__(1024) void k_scatter(const int32_t* __restrict__ ids,
                                                   const int32_t* __restrict__ e2slot,
-                                                  int all_resident, int P, int k, int E,
+                                                  int all_resident, int P, int E,
                                                   const int32_t* __restrict__ chunk_base,
                                                   const int32_t* __restrict__ offsets,
-                                                  int32_t* __restrict__ perm_pair,
-                                                  const uint8_t* __restrict__ x, int row_bytes,
-                                                  uint8_t* __restrict__ x_perm) {
+                                                  int32_t* __restrict__ perm_pair) {
     __shared__ int se[kChunk];
-    __shared__ int dst[kChunk];
     const int tid = threadIdx.x;
-    const int p0 = blockIdx.x * kChunk;
-    const int p = p0 + tid;
+    const int p = blockIdx.x * kChunk + tid;
     int e = -1;
     if (p < P) {
         int ee = ids[p];
@@ -97,39 +94,18 @@ __global__ __launch_bounds__(1024) void k_scatter(const int32_t* __restrict__ id
     }
     se[tid] = e;
     __syncthreads();
-    int d = -1;
     if (e >= 0) {
         int r = 0;
         for (int i = 0; i < tid; ++i) r += (se[i] == e);
-        d = offsets[e] + chunk_base[(size_t)blockIdx.x * E + e] + r;
-        perm_pair[d] = p;
-    }
-    dst[tid] = d;
-    __syncthreads();
-    const int lane = tid & 63, wave = tid >> 6;
-    const int n = min(kChunk, P - p0);
-    for (int i = wave; i < n; i += 16) {
-        int di = dst[i];
-        if (di < 0) continue;
-        const uint4* src = (const uint4*)(x + (size_t)((p0 + i) / k) * row_bytes);
-        uint4* out = (uint4*)(x_perm + (size_t)di * row_bytes);
-        for (int c = lane; c < row_bytes / 16; c += 64) out[c] = src[c];
+        perm_pair[offsets[e] + chunk_base[(size_t)blockIdx.x * E + e] + r] = p;
     }
 }
 
 // Shared-expert group: rows offsets[E] + t hold token t.
 __global__ __launch_bounds__(256) void k_shared_rows(int T, int Tk, const int32_t* __restrict__ offsets,
-                                                     int E, int32_t* __restrict__ perm_pair,
-                                                     const uint8_t* __restrict__ x, int row_bytes,
-                                                     uint8_t* __restrict__ x_perm) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const int d = offsets[E] + t;
-    if (lane == 0) perm_pair[d] = Tk + t;
-    const uint4* src = (const uint4*)(x + (size_t)t * row_bytes);
-    uint4* out = (uint4*)(x_perm + (size_t)d * row_bytes);
-    for (int c = lane; c < row_bytes / 16; c += 64) out[c] = src[c];
+                                                     int E, int32_t* __restrict__ perm_pair) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < T) perm_pair[offsets[E] + t] = Tk + t;
 }
 
 // Four consecutive pair outputs as fp32 (bf16 storage with bf16 activations).
@@ -252,23 +228,18 @@ hipError_t launch_rmsnorm(const void* r, void* u, int T, int H, int act_bf16, hi
 }
 
 hipError_t launch_permute(const int32_t* ids, const int32_t* e2slot, int all_resident, int T,
-                          int k, int E, int has_shared, const void* x, int act_bf16, int H,
-                          PermuteBufs b, hipStream_t s) {
+                          int k, int E, int has_shared, PermuteBufs b, hipStream_t s) {
     const int P = T * k;
     const int nchunks = (P + kChunk - 1) / kChunk;
-    const int row_bytes = H * (act_bf16 ? 2 : 4);
     if (nchunks > 0)
         k_hist<<<nchunks, 1024, 0, s>>>(ids, e2slot, all_resident, P, E, b.chunk_cnt);
     k_scan<<<1, 1024, 0, s>>>(b.chunk_cnt, nchunks, E, has_shared, T, b.counts, b.offsets,
                               b.tile_off);
     if (nchunks > 0)
-        k_scatter<<<nchunks, 1024, 0, s>>>(ids, e2slot, all_resident, P, k, E, b.chunk_cnt,
-                                           b.offsets, b.perm_pair, (const uint8_t*)x, row_bytes,
-                                           (uint8_t*)b.x_perm);
+        k_scatter<<<nchunks, 1024, 0, s>>>(ids, e2slot, all_resident, P, E, b.chunk_cnt,
+                                           b.offsets, b.perm_pair);
     if (has_shared)
-        k_shared_rows<<<(T + 3) / 4, 256, 0, s>>>(T, P, b.offsets, E, b.perm_pair,
-                                                  (const uint8_t*)x, row_bytes,
-                                                  (uint8_t*)b.x_perm);
+        k_shared_rows<<<(T + 255) / 256, 256, 0, s>>>(T, P, b.offsets, E, b.perm_pair);
     return hipGetLastError();
 }
 

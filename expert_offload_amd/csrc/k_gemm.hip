@@ -612,23 +612,17 @@ bool run_v3(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hi
 // loads are not drained at each K step, and each step's six tile loads are
 // issued between its MFMAs rather than in one burst after the barrier.
 // Two workgroups share a CU: measured on the prefill shapes, a 128 x 512 tile
-// (one workgroup per CU, 4 x 4 MFMA blocks per wavefront) and rings of 4-6
-// stages at one workgroup per CU are 7-20% slower; the second, unsynchronised
-// workgroup covers each workgroup's barrier waits.
+// (one workgroup per CU, 4 x 4 MFMA blocks per wavefront), rings of 4-6 stages
+// at one workgroup per CU, and one eight-wavefront workgroup whose two halves
+// alternate between multiplying and loading are 7-20% slower; the second,
+// unsynchronised workgroup covers each workgroup's barrier waits.
 constexpr int kV4Ring = 3;                                // stages: two tiles in flight
 constexpr size_t kV4Stage = (size_t)(V3M + V3N) * 64;     // 24 KB per stage
 template <int S>
 constexpr size_t v4_pipe() { return S * kV4Stage; }
-// Epilogue tile row stride: at three workgroups per CU (OCC 3) the down
-// kernel's 128 x 256 outputs leave through LDS in two 128-column halves.
-template <int OCC>
-constexpr int v4_old() { return OCC >= 3 ? 128 + 8 : V3_OUT_LD; }
-template <int S, int OCC>
-constexpr size_t v4_out() { return (size_t)V3M * v4_old<OCC>() * sizeof(uint16_t); }
-template <int S, int OCC>
+template <int S>
 constexpr size_t v4_lds() {
-    return (v4_pipe<S>() > v4_out<S, OCC>() ? v4_pipe<S>() : v4_out<S, OCC>()) +
-           2 * V3M * sizeof(int32_t);
+    return (v4_pipe<S>() > kV3Out ? v4_pipe<S>() : kV3Out) + 2 * V3M * sizeof(int32_t);
 }
 
 // Wait until at most N of this thread's vector-memory loads are outstanding.
@@ -675,14 +669,11 @@ __device__ __forceinline__ void v4_issue(const GemmArgs& a, const uint16_t* wdat
     }
 }
 
-template <int MODE, int S, int OCC>
-__global__ __launch_bounds__(256, OCC) void k_gemm_v4(GemmArgs a, int nN) {
+template <int MODE, int S>
+__global__ __launch_bounds__(256, 2) void k_gemm_v4(GemmArgs a, int nN) {
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint8_t* sb = (uint8_t*)smem;
-    int32_t* s_pair =
-        (int32_t*)(sb + (v4_pipe<S>() > v4_out<S, OCC>() ? v4_pipe<S>() : v4_out<S, OCC>()));
-    constexpr int OLD = v4_old<OCC>();
-    constexpr bool HALF = OCC >= 3;
+    int32_t* s_pair = (int32_t*)(sb + (v4_pipe<S>() > kV3Out ? v4_pipe<S>() : kV3Out));
     float* s_wp = (float*)(s_pair + V3M);
 
     const int real = a.tile_off[a.G] * nN;
@@ -790,7 +781,7 @@ __global__ __launch_bounds__(256, OCC) void k_gemm_v4(GemmArgs a, int nN) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                    ot[row * OLD + c] =
+                    ot[row * V3_OUT_LD + c] =
                         (uint16_t)f32_bf16_rne(silu_f32(acc[i][jj][v]) * acc[i][2 + jj][v]);
                 }
         }
@@ -800,69 +791,59 @@ __global__ __launch_bounds__(256, OCC) void k_gemm_v4(GemmArgs a, int nN) {
             int cidx = tid + 256 * it, row = cidx >> 4, seg = cidx & 15;
             if (m0 + row < m_end)
                 *(uint4*)(a.h_out + (size_t)(m0 + row) * a.I + n0 + seg * 8) =
-                    *(const uint4*)(ot + row * OLD + seg * 8);
+                    *(const uint4*)(ot + row * V3_OUT_LD + seg * 8);
         }
     } else {
-        constexpr int NH = HALF ? 2 : 1, CW = 256 / NH;  // column passes and their width
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = wn * 128 + j * 32 + col;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    ot[row * V3_OUT_LD + c] = (uint16_t)f32_bf16_rne(acc[i][j][v] * s_wp[row]);
+                }
+        }
+        __syncthreads();
         uint16_t* op = (uint16_t*)a.o_pairs;
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            if (!HALF || wn == h) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int c = (HALF ? 0 : wn * 128) + j * 32 + col;
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                            ot[row * OLD + c] = (uint16_t)f32_bf16_rne(acc[i][j][v] * s_wp[row]);
-                        }
-                }
-            }
-            __syncthreads();
-#pragma unroll
-            for (int it = 0; it < V3M * (CW / 8) / 256; ++it) {
-                int cidx = tid + 256 * it, row = cidx / (CW / 8), seg = cidx % (CW / 8);
-                int pair = s_pair[row];
-                if (pair >= 0)
-                    *(uint4*)(op + (size_t)pair * a.H + n0 + h * CW + seg * 8) =
-                        *(const uint4*)(ot + row * OLD + seg * 8);
-            }
-            if (h + 1 < NH) __syncthreads();  // the next pass overwrites the tile
+        for (int it = 0; it < 16; ++it) {
+            int cidx = tid + 256 * it, row = cidx >> 5, seg = cidx & 31;
+            int pair = s_pair[row];
+            if (pair >= 0)
+                *(uint4*)(op + (size_t)pair * a.H + n0 + seg * 8) =
+                    *(const uint4*)(ot + row * V3_OUT_LD + seg * 8);
         }
     }
 }
 
-template <int S, int OCC>
+template <int S>
 bool run_v4(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hipEvent_t* ev) {
-    static_assert(OCC * v4_lds<S, OCC>() <= 160 * 1024, "v4 LDS");
+    static_assert(2 * v4_lds<S>() <= 160 * 1024, "v4 LDS: two workgroups per CU");
     if (I % 128 || H % 256 || H % V3K || I % V3K) return false;
     static bool attr = false;
     if (!attr) {
-        if (hipFuncSetAttribute((const void*)k_gemm_v4<0, S, OCC>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, v4_lds<S, OCC>()) != hipSuccess ||
-            hipFuncSetAttribute((const void*)k_gemm_v4<1, S, OCC>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, v4_lds<S, OCC>()) != hipSuccess)
+        if (hipFuncSetAttribute((const void*)k_gemm_v4<0, S>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, v4_lds<S>()) != hipSuccess ||
+            hipFuncSetAttribute((const void*)k_gemm_v4<1, S>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, v4_lds<S>()) != hipSuccess)
             return false;
         attr = true;
     }
     const int n1 = I / 128, n2 = H / 256;
     auto grid = [&](int nN) { return ((tiles * nN + 7) / 8) * 8; };
-    hipExtLaunchKernelGGL((k_gemm_v4<0, S, OCC>), dim3(grid(n1)), dim3(256),
-                          (uint32_t)v4_lds<S, OCC>(), s, ev[0], ev[1], 0, a1, n1);
-    hipExtLaunchKernelGGL((k_gemm_v4<1, S, OCC>), dim3(grid(n2)), dim3(256),
-                          (uint32_t)v4_lds<S, OCC>(), s, ev[2], ev[3], 0, a2, n2);
+    hipExtLaunchKernelGGL((k_gemm_v4<0, S>), dim3(grid(n1)), dim3(256), (uint32_t)v4_lds<S>(), s,
+                          ev[0], ev[1], 0, a1, n1);
+    hipExtLaunchKernelGGL((k_gemm_v4<1, S>), dim3(grid(n2)), dim3(256), (uint32_t)v4_lds<S>(), s,
+                          ev[2], ev[3], 0, a2, n2);
     return true;
 }
 
 template <int FMT>
 void run_mfma(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hipEvent_t* ev) {
     if (FMT == EO_W_BF16 && g_gemm_tiles >= 2) {
-        bool ok = false;
-        if (g_gemm_tiles == 3) ok = run_v4<2, 3>(a1, a2, tiles, I, H, s, ev);
-        if (g_gemm_tiles == 4) ok = run_v4<2, 2>(a1, a2, tiles, I, H, s, ev);
-        if (ok || run_v4<kV4Ring, 2>(a1, a2, tiles, I, H, s, ev)) return;
+        if (run_v4<kV4Ring>(a1, a2, tiles, I, H, s, ev)) return;
     }
     if (g_gemm_tiles && run_v3<FMT>(a1, a2, tiles, I, H, s, ev)) return;
     hipExtLaunchKernelGGL(k_gemm_mfma<FMT, 0>, dim3(tiles, I / 64), dim3(256), 0, s, ev[0], ev[1],

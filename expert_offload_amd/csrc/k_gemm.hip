@@ -82,21 +82,32 @@ __device__ __forceinline__ const uint8_t* group_base(const GroupW& gw, int g, in
     return gw.slots + (uint64_t)s * gw.stride;
 }
 
+// Two fp4 codes (byte B of w, even element in the low nibble) as a bf16 pair,
+// times sc. The scaled convert applies only the power of two of its scale
+// operand, so it takes MXFP4's e8m0 scales whole; an NVFP4 e4m3 scale is
+// applied to the converted pair in fp32. Either way the product is exact in
+// bf16: an e2m1 value has at most 2 significant bits, an e4m3 scale at most 4.
+template <int FMT, int B>
+__device__ __forceinline__ uint32_t fp4x2_bf16(uint32_t w, float sc) {
+    if (FMT == EO_W_MXFP4)
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, B));
+    const uint32_t p = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, B));
+    return bf_hi(__uint_as_float(p << 16) * sc) | (bf_hi(__uint_as_float(p & 0xFFFF0000u) * sc) << 16);
+}
+
 // Decode 32 fp4 codes (16 bytes) with per-16 multipliers sc0 (elements 0..15)
-// and sc1 (16..31) into 32 bf16 at dst (exact: at most 6 significant bits).
+// and sc1 (16..31) into 32 bf16 at dst.
+template <int FMT>
 __device__ __forceinline__ void fp4x32_to_lds(uint4 q, float sc0, float sc1, uint16_t* dst) {
-    uint32_t words[4] = {q.x, q.y, q.z, q.w};
+    const uint32_t words[4] = {q.x, q.y, q.z, q.w};
     uint32_t out[16];
 #pragma unroll
     for (int wi = 0; wi < 4; ++wi) {
-        float sc = wi < 2 ? sc0 : sc1;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            uint32_t byte = (words[wi] >> (8 * b)) & 0xFFu;
-            uint32_t lo = bf_hi(e2m1_f32(byte & 0xFu) * sc);
-            uint32_t hi = bf_hi(e2m1_f32(byte >> 4) * sc);
-            out[wi * 4 + b] = lo | (hi << 16);
-        }
+        const float sc = wi < 2 ? sc0 : sc1;
+        out[wi * 4 + 0] = fp4x2_bf16<FMT, 0>(words[wi], sc);
+        out[wi * 4 + 1] = fp4x2_bf16<FMT, 1>(words[wi], sc);
+        out[wi * 4 + 2] = fp4x2_bf16<FMT, 2>(words[wi], sc);
+        out[wi * 4 + 3] = fp4x2_bf16<FMT, 3>(words[wi], sc);
     }
     uint4* d = (uint4*)dst;
     d[0] = make_uint4(out[0], out[1], out[2], out[3]);
@@ -185,7 +196,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
                 sc0 = e4m3_f32(sp[0]);
                 sc1 = e4m3_f32(sp[1]);
             }
-            fp4x32_to_lds(q, sc0, sc1, Bs + r * LDK + half * 32);
+            fp4x32_to_lds<FMT>(q, sc0, sc1, Bs + r * LDK + half * 32);
         }
         __syncthreads();
 #pragma unroll
@@ -433,7 +444,7 @@ __device__ __forceinline__ void v3_store(uint16_t* As, uint16_t* Bs, int tid, co
             sc0 = e4m3_f32(r.sc & 0xFF);
             sc1 = e4m3_f32(r.sc >> 8);
         }
-        fp4x32_to_lds(r.b[0], sc0, sc1, Bs + tid * V3L);
+        fp4x32_to_lds<FMT>(r.b[0], sc0, sc1, Bs + tid * V3L);
     }
 }
 

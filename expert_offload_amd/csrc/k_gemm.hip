@@ -357,11 +357,18 @@ constexpr size_t kV3Pipe = 2 * (V3M + V3N) * V3L * sizeof(uint16_t);     // 61,4
 constexpr size_t kV3Out = (size_t)V3M * V3_OUT_LD * sizeof(uint16_t);     // 67,584 B
 constexpr size_t kV3Lds = (kV3Pipe > kV3Out ? kV3Pipe : kV3Out) + 2 * V3M * sizeof(int32_t);
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <int FMT>
 struct V3Regs {  // one K tile of global data held by a thread
     uint4 a[2];
     uint4 b[FMT == EO_W_BF16 ? 4 : (FMT == EO_W_FP8 ? 2 : 1)];
     uint32_t sc;  // fp4 block scales of this thread's B chunk
+    // fp4: the thread's weight row over four K tiles (64 contiguous bytes) and
+    // their block scales, loaded together every fourth tile, so one row's
+    // 128-byte line is requested twice per 8 tiles instead of 8 times
+    u32x4 s0, s1, s2, s3;
+    uint32_t ss0, ss1;
 };
 
 template <int FMT, int MODE>
@@ -396,13 +403,29 @@ __device__ __forceinline__ void v3_load(const GemmArgs& a, const uint8_t* wdata,
             r.b[it] = *(const uint4*)(wdata + (size_t)v3_wrow<FMT, MODE>(a, n0, row) * K + k0 +
                                       seg * 16);
         }
-    } else {  // fp4: 256 rows x 16 bytes = 256 chunks, one per thread
+    } else {  // fp4: 256 rows x 16 bytes = 256 chunks, one per thread (K % 128 == 0)
         const int row = tid, wr = v3_wrow<FMT, MODE>(a, n0, row);
-        r.b[0] = *(const uint4*)(wdata + (size_t)wr * (K / 2) + k0 / 2);
+        const int u = (k0 / V3K) & 3;  // this tile's place in the thread's span
+        if (u == 0) {
+            const u32x4* rp = (const u32x4*)(wdata + (size_t)wr * (K / 2) + k0 / 2);
+            r.s0 = rp[0];
+            r.s1 = rp[1];
+            r.s2 = rp[2];
+            r.s3 = rp[3];
+            if (FMT == EO_W_MXFP4) {
+                r.ss0 = *(const uint32_t*)(wscal + (size_t)wr * (K / 32) + k0 / 32);
+            } else {
+                const uint2 q = *(const uint2*)(wscal + (size_t)wr * (K / 16) + k0 / 16);
+                r.ss0 = q.x;
+                r.ss1 = q.y;
+            }
+        }
+        const u32x4 v = u == 0 ? r.s0 : u == 1 ? r.s1 : u == 2 ? r.s2 : r.s3;
+        r.b[0] = make_uint4(v[0], v[1], v[2], v[3]);
         if (FMT == EO_W_MXFP4)
-            r.sc = wscal[(size_t)wr * (K / 32) + k0 / 32];
+            r.sc = (r.ss0 >> (8 * u)) & 0xFFu;
         else
-            r.sc = *(const uint16_t*)(wscal + (size_t)wr * (K / 16) + k0 / 16);
+            r.sc = ((u < 2 ? r.ss0 : r.ss1) >> (16 * (u & 1))) & 0xFFFFu;
     }
 }
 

@@ -267,6 +267,67 @@ EO_AVX512BF16 void dot4_bf16_avx512(const uint16_t* a, size_t ld, const uint16_t
     out[3] = _mm512_reduce_add_ps(s3);
 }
 
+// fp4 weights (MXFP4 / NVFP4) against bf16 activations on the same pair dot
+// product: 32 codes (16 bytes, even element in the low nibble) become 32 bf16
+// by widening each byte to a dword whose low word is its low nibble and whose
+// high word is its high nibble, and looking both up in a 16-entry table of the
+// e2m1 values (vpermw). One vdpbf16ps then gives 16 fp32 partial sums of a
+// 32-code group, lane l holding codes 2l and 2l+1; the group's block scales
+// multiply those partials (MXFP4: one e8m0 scale per 32 codes; NVFP4: one
+// e4m3 scale per 16 codes, lanes 0-7 and 8-15). Every weight is exact in bf16.
+alignas(64) const uint16_t kE2m1Bf16[32] = {
+    0x0000, 0x3F00, 0x3F80, 0x3FC0, 0x4000, 0x4040, 0x4080, 0x40C0,   // 0 0.5 1 1.5 2 3 4 6
+    0x8000, 0xBF00, 0xBF80, 0xBFC0, 0xC000, 0xC040, 0xC080, 0xC0C0};  // the same, negative
+
+// Block-scale codes as fp32: e8m0 (MXFP4) and e4m3 (NVFP4), all 256 codes.
+const float* scale_table(int fmt) {
+    static const std::vector<float> e8m0 = [] {
+        std::vector<float> t(256);
+        for (int c = 0; c < 256; ++c) t[c] = e8m0_val(c);
+        return t;
+    }();
+    static const std::vector<float> e4m3 = [] {
+        std::vector<float> t(256);
+        for (int c = 0; c < 256; ++c) t[c] = e4m3_val(c);
+        return t;
+    }();
+    return fmt == EO_W_MXFP4 ? e8m0.data() : e4m3.data();
+}
+
+EO_AVX512BF16 inline __m512i fp4x32_bf16(const uint8_t* p, __m512i lut) {
+    const __m512i d = _mm512_cvtepu8_epi32(_mm_loadu_si128((const __m128i*)p));
+    const __m512i idx = _mm512_or_si512(
+        _mm512_and_si512(d, _mm512_set1_epi32(0xF)),
+        _mm512_slli_epi32(_mm512_and_si512(d, _mm512_set1_epi32(0xF0)), 12));
+    return _mm512_permutexvar_epi16(idx, lut);
+}
+
+// NR fp4 rows of K codes (K % 32 == 0; row r's codes at rows[r], its block
+// scale codes at scal[r]) against the bf16 vector x, block scales applied.
+template <int FMT, int NR>
+EO_AVX512BF16 void dot_fp4_avx512(const uint8_t* const (&rows)[NR],
+                                  const uint8_t* const (&scal)[NR], const uint16_t* x, int K,
+                                  const float* st, float (&out)[NR]) {
+    const __m512i lut = _mm512_load_si512(kE2m1Bf16);
+    __m512 acc[NR];
+    for (int r = 0; r < NR; ++r) acc[r] = _mm512_setzero_ps();
+    for (int g = 0; g < K / 32; ++g) {
+        const __m512bh xv = as_bh(_mm512_loadu_si512(x + 32 * g));
+        for (int r = 0; r < NR; ++r) {
+            const __m512 p = _mm512_dpbf16_ps(_mm512_setzero_ps(),
+                                              as_bh(fp4x32_bf16(rows[r] + 16 * g, lut)), xv);
+            __m512 sv;
+            if (FMT == EO_W_MXFP4)
+                sv = _mm512_set1_ps(st[scal[r][g]]);
+            else
+                sv = _mm512_mask_mov_ps(_mm512_set1_ps(st[scal[r][2 * g]]), (__mmask16)0xFF00,
+                                        _mm512_set1_ps(st[scal[r][2 * g + 1]]));
+            acc[r] = _mm512_fmadd_ps(p, sv, acc[r]);
+        }
+    }
+    for (int r = 0; r < NR; ++r) out[r] = _mm512_reduce_add_ps(acc[r]);
+}
+
 uint16_t bf16_rne(float f) {
     uint32_t u;
     std::memcpy(&u, &f, 4);
@@ -324,7 +385,9 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
 
     constexpr int RB = 16;
     const int nb1_fp32 = (I + RB - 1) / RB;
-    if (fmt == EO_W_BF16 && jb.xb && H % 128 == 0 && I % 64 == 0 && cpu_has_avx512bf16()) {
+    const bool fp4 = fmt == EO_W_MXFP4 || fmt == EO_W_NVFP4;
+    if ((fmt == EO_W_BF16 || fp4) && jb.xb && H % 128 == 0 && I % 64 == 0 &&
+        cpu_has_avx512bf16()) {
         // task sizes: two tasks per thread and expert in each phase, so that
         // every thread streams the same share (measured on the 16-core host:
         // smaller tasks cost dispatch, uneven counts leave threads idle)
@@ -356,6 +419,38 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
         std::vector<int> seg_start(seg.size() + 1, 0);
         for (size_t q = 0; q < seg.size(); ++q)
             seg_start[q + 1] = seg_start[q] + (seg[q].first == 1 ? nb1 : nb2);
+        // fp4 rows: gate row r and up row I + r of W13 (K = H), or four rows of
+        // W2 (K = I); NVFP4's per-tensor scales (gate, up, down) multiply the dots
+        const int blk = fmt == EO_W_MXFP4 ? 32 : 16;
+        const float* st = fp4 ? scale_table(fmt) : nullptr;
+        auto fp4_gate_up = [&](const uint8_t* b, int r, const uint16_t* xt, float* g, float* u) {
+            const uint8_t* d = b + lay.d13;
+            const uint8_t* sc = b + lay.s13;
+            const uint8_t* const rows[2] = {d + (size_t)r * (H / 2), d + (size_t)(I + r) * (H / 2)};
+            const uint8_t* const scs[2] = {sc + (size_t)r * (H / blk), sc + (size_t)(I + r) * (H / blk)};
+            float o2[2];
+            if (fmt == EO_W_MXFP4)
+                dot_fp4_avx512<EO_W_MXFP4, 2>(rows, scs, xt, H, st, o2);
+            else
+                dot_fp4_avx512<EO_W_NVFP4, 2>(rows, scs, xt, H, st, o2);
+            *g = o2[0] * gl(b, 0);
+            *u = o2[1] * gl(b, 1);
+        };
+        auto fp4_down4 = [&](const uint8_t* b, int o, const uint16_t* ht, float* out) {
+            const uint8_t* d = b + lay.d2;
+            const uint8_t* sc = b + lay.s2;
+            const uint8_t* const rows[4] = {d + (size_t)o * (I / 2), d + (size_t)(o + 1) * (I / 2),
+                                            d + (size_t)(o + 2) * (I / 2), d + (size_t)(o + 3) * (I / 2)};
+            const uint8_t* const scs[4] = {sc + (size_t)o * (I / blk), sc + (size_t)(o + 1) * (I / blk),
+                                           sc + (size_t)(o + 2) * (I / blk), sc + (size_t)(o + 3) * (I / blk)};
+            float o4[4];
+            if (fmt == EO_W_MXFP4)
+                dot_fp4_avx512<EO_W_MXFP4, 4>(rows, scs, ht, I, st, o4);
+            else
+                dot_fp4_avx512<EO_W_NVFP4, 4>(rows, scs, ht, I, st, o4);
+            const float g2 = gl(b, 2);
+            for (int q = 0; q < 4; ++q) out[q] = o4[q] * g2;
+        };
         std::unique_ptr<std::atomic<int>[]> done1(new std::atomic<int>[ne]);
         for (int i = 0; i < ne; ++i) done1[i].store(0, std::memory_order_relaxed);
         pool->run(seg_start.back(), [&](int task) {
@@ -369,8 +464,12 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
                 for (int r = blk * RB1; r < std::min(I, blk * RB1 + RB1); ++r)
                     for (size_t ti = 0; ti < nt; ++ti) {
                         float g, u;
-                        dot2_bf16_avx512(W + (size_t)r * H, W + (size_t)(I + r) * H,
-                                         jb.xb + (size_t)toks[ei][ti] * H, H, &g, &u);
+                        const uint16_t* xt = jb.xb + (size_t)toks[ei][ti] * H;
+                        if (fp4)
+                            fp4_gate_up(b, r, xt, &g, &u);
+                        else
+                            dot2_bf16_avx512(W + (size_t)r * H, W + (size_t)(I + r) * H, xt, H,
+                                             &g, &u);
                         hb[hoff[ei] + ti * I + r] = bf16_rne(g / (1.0f + std::exp(-g)) * u);
                     }
                 done1[ei].fetch_add(1, std::memory_order_release);
@@ -380,7 +479,11 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
                 for (int o = blk * RB2; o < std::min(H, blk * RB2 + RB2); o += 4)  // H % 4 == 0
                     for (size_t ti = 0; ti < nt; ++ti) {
                         float out[4];
-                        dot4_bf16_avx512(W2 + (size_t)o * I, I, hb + hoff[ei] + ti * I, I, out);
+                        if (fp4)
+                            fp4_down4(b, o, hb + hoff[ei] + ti * I, out);
+                        else
+                            dot4_bf16_avx512(W2 + (size_t)o * I, I, hb + hoff[ei] + ti * I, I,
+                                             out);
                         float* vo = v + voff[ei] + ti * H + o;
                         vo[0] = out[0];
                         vo[1] = out[1];

@@ -45,9 +45,11 @@ def _cpu_has_avx512bf16():
 @pytest.mark.parametrize("fmt", ["fp32", "bf16", "mxfp4", "nvfp4", "fp8"])
 def test_host_ffn_matches_oracle(driver, tmp_path, fmt, isa):
     # avx2: fp32 route (h kept in fp32), within 1e-5 of the oracle. native: on a
-    # CPU with AVX512_BF16, bf16 experts take the bf16 pair-dot route, which
+    # CPU with AVX512_BF16, bf16, MXFP4 and NVFP4 experts take the bf16 pair-dot
+    # route (fp4 codes looked up as bf16, block scales on the partial sums), which
     # rounds h to bf16 as the device does (bound: the layer tolerance, 2e-2)
-    if isa == "native" and fmt == "bf16" and not _cpu_has_avx512bf16():
+    pair_route = fmt in ("bf16", "mxfp4", "nvfp4")
+    if isa == "native" and pair_route and not _cpu_has_avx512bf16():
         pytest.skip("CPU without AVX512_BF16")
     f = synth.FMT_NAMES[fmt]
     H, I, E, k, T = 256, 128, 6, 2, 9
@@ -67,7 +69,7 @@ def test_host_ffn_matches_oracle(driver, tmp_path, fmt, isa):
     y = np.fromfile(os.path.join(d, "y.bin"), dtype=np.float32).reshape(T, H)
     ref = OM.layer_output(xf, ids, w, lambda e: OF.dequant_expert(blocks[e], H, I, f))
     err = np.max(np.abs(y - ref)) / np.max(np.abs(ref))
-    bf16_route = isa == "native" and fmt == "bf16"
+    bf16_route = isa == "native" and pair_route
     assert err <= (2e-2 if bf16_route else 1e-5), err
     if bf16_route:
         assert err > 1e-7  # the bf16 route did run (h is rounded)

@@ -647,9 +647,10 @@ bool run_v3(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hi
 // issued between its MFMAs rather than in one burst after the barrier.
 // Two workgroups share a CU: measured on the prefill shapes, a 128 x 512 tile
 // (one workgroup per CU, 4 x 4 MFMA blocks per wavefront), rings of 4-6 stages
-// at one workgroup per CU, and one eight-wavefront workgroup whose two halves
-// alternate between multiplying and loading are 7-20% slower; the second,
-// unsynchronised workgroup covers each workgroup's barrier waits.
+// at one workgroup per CU, one eight-wavefront workgroup whose two halves
+// alternate between multiplying and loading, a K step of 64 with A fragments in
+// registers, and 64-row tiles at three workgroups per CU are 7-24% slower; the
+// second, unsynchronised workgroup covers each workgroup's barrier waits.
 constexpr int kV4Ring = 3;                                // stages: two tiles in flight
 constexpr size_t kV4Stage = (size_t)(V3M + V3N) * 64;     // 24 KB per stage
 template <int S>

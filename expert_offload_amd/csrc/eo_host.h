@@ -35,9 +35,13 @@ struct HostJob {
     float* y;                       // [T,H] accumulated (zeroed by the caller)
 };
 void host_ffn(ThreadPool* pool, const HostJob& job, std::vector<float>& scratch);
-// True when host_ffn takes the AVX512_BF16 route for bf16 experts (CPU support,
-// unless the environment sets EO_HOST_ISA=avx2).
+// True when host_ffn takes the AVX512_BF16 route for bf16, MXFP4, NVFP4 and FP8
+// experts (CPU support, unless the environment sets EO_HOST_ISA=avx2).
 bool host_ffn_uses_avx512bf16();
+// The weight decode of that route, for tests: 32 codes of `fmt` (FP8: 32 bytes,
+// giving value / 256; MXFP4 / NVFP4: 16 bytes, giving the unscaled e2m1 values)
+// as 32 bf16 bit patterns in out. False when the route is not available.
+bool host_decode_codes(int fmt, const uint8_t* codes, uint16_t* out);
 ThreadPool* threadpool_create(int n);
 void threadpool_destroy(ThreadPool* p);
 int threadpool_size(ThreadPool* p);

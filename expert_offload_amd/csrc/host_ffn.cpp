@@ -328,6 +328,36 @@ EO_AVX512BF16 void dot_fp4_avx512(const uint8_t* const (&rows)[NR],
     for (int r = 0; r < NR; ++r) out[r] = _mm512_reduce_add_ps(acc[r]);
 }
 
+// fp8 (e4m3fn) weights on the same pair dot product: a code's 7 magnitude bits
+// shifted left by 7 are the fp16 encoding of value / 256 (exponent bias 15
+// against 7; e4m3 subnormals land on fp16 subnormals), so 32 codes become bf16
+// through fp16 -> fp32 -> bf16, every step exact; the dot is scaled by 256 and
+// the row scale afterwards. (0x7F / 0xFF, e4m3fn's NaN, is never stored.)
+EO_AVX512BF16 inline __m512i fp8x32_bf16(const uint8_t* p) {
+    const __m512i w = _mm512_cvtepu8_epi16(_mm256_loadu_si256((const __m256i*)p));
+    const __m512i h = _mm512_or_si512(
+        _mm512_slli_epi16(_mm512_and_si512(w, _mm512_set1_epi16(0x7F)), 7),
+        _mm512_slli_epi16(_mm512_and_si512(w, _mm512_set1_epi16(0x80)), 8));
+    const __m512 lo = _mm512_cvtph_ps(_mm512_castsi512_si256(h));
+    const __m512 hi = _mm512_cvtph_ps(_mm512_extracti64x4_epi64(h, 1));
+    return (__m512i)_mm512_cvtne2ps_pbh(hi, lo);
+}
+
+// NR fp8 rows of K codes (K % 32 == 0) against the bf16 vector x, times 256
+// (the row scales are the caller's).
+template <int NR>
+EO_AVX512BF16 void dot_fp8_avx512(const uint8_t* const (&rows)[NR], const uint16_t* x, int K,
+                                  float (&out)[NR]) {
+    __m512 acc[NR];
+    for (int r = 0; r < NR; ++r) acc[r] = _mm512_setzero_ps();
+    for (int g = 0; g < K / 32; ++g) {
+        const __m512bh xv = as_bh(_mm512_loadu_si512(x + 32 * g));
+        for (int r = 0; r < NR; ++r)
+            acc[r] = _mm512_dpbf16_ps(acc[r], as_bh(fp8x32_bf16(rows[r] + 32 * g)), xv);
+    }
+    for (int r = 0; r < NR; ++r) out[r] = _mm512_reduce_add_ps(acc[r]) * 256.0f;
+}
+
 uint16_t bf16_rne(float f) {
     uint32_t u;
     std::memcpy(&u, &f, 4);
@@ -347,6 +377,21 @@ bool cpu_has_avx512bf16() {
 }  // namespace
 
 bool host_ffn_uses_avx512bf16() { return cpu_has_avx512bf16(); }
+
+namespace {
+EO_AVX512BF16 void decode_codes_avx512(int fmt, const uint8_t* codes, uint16_t* out) {
+    const __m512i v = fmt == EO_W_FP8 ? fp8x32_bf16(codes)
+                                      : fp4x32_bf16(codes, _mm512_load_si512(kE2m1Bf16));
+    _mm512_storeu_si512(out, v);
+}
+}  // namespace
+
+bool host_decode_codes(int fmt, const uint8_t* codes, uint16_t* out) {
+    if (!cpu_has_avx512bf16() || (fmt != EO_W_FP8 && fmt != EO_W_MXFP4 && fmt != EO_W_NVFP4))
+        return false;
+    decode_codes_avx512(fmt, codes, out);
+    return true;
+}
 
 void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) {
     const int H = jb.H, I = jb.I, T = jb.T, k = jb.k;
@@ -386,7 +431,8 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
     constexpr int RB = 16;
     const int nb1_fp32 = (I + RB - 1) / RB;
     const bool fp4 = fmt == EO_W_MXFP4 || fmt == EO_W_NVFP4;
-    if ((fmt == EO_W_BF16 || fp4) && jb.xb && H % 128 == 0 && I % 64 == 0 &&
+    const bool coded = fp4 || fmt == EO_W_FP8;  // weights decoded to bf16 in registers
+    if ((fmt == EO_W_BF16 || coded) && jb.xb && H % 128 == 0 && I % 64 == 0 &&
         cpu_has_avx512bf16()) {
         // task sizes: two tasks per thread and expert in each phase, so that
         // every thread streams the same share (measured on the 16-core host:
@@ -425,6 +471,15 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
         const float* st = fp4 ? scale_table(fmt) : nullptr;
         auto fp4_gate_up = [&](const uint8_t* b, int r, const uint16_t* xt, float* g, float* u) {
             const uint8_t* d = b + lay.d13;
+            if (fmt == EO_W_FP8) {
+                const uint8_t* const rows[2] = {d + (size_t)r * H, d + (size_t)(I + r) * H};
+                const float* rs = (const float*)(b + lay.s13);
+                float o2[2];
+                dot_fp8_avx512<2>(rows, xt, H, o2);
+                *g = o2[0] * rs[r];
+                *u = o2[1] * rs[I + r];
+                return;
+            }
             const uint8_t* sc = b + lay.s13;
             const uint8_t* const rows[2] = {d + (size_t)r * (H / 2), d + (size_t)(I + r) * (H / 2)};
             const uint8_t* const scs[2] = {sc + (size_t)r * (H / blk), sc + (size_t)(I + r) * (H / blk)};
@@ -438,6 +493,15 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
         };
         auto fp4_down4 = [&](const uint8_t* b, int o, const uint16_t* ht, float* out) {
             const uint8_t* d = b + lay.d2;
+            if (fmt == EO_W_FP8) {
+                const uint8_t* const rows[4] = {d + (size_t)o * I, d + (size_t)(o + 1) * I,
+                                                d + (size_t)(o + 2) * I, d + (size_t)(o + 3) * I};
+                const float* rs = (const float*)(b + lay.s2);
+                float o4[4];
+                dot_fp8_avx512<4>(rows, ht, I, o4);
+                for (int q = 0; q < 4; ++q) out[q] = o4[q] * rs[o + q];
+                return;
+            }
             const uint8_t* sc = b + lay.s2;
             const uint8_t* const rows[4] = {d + (size_t)o * (I / 2), d + (size_t)(o + 1) * (I / 2),
                                             d + (size_t)(o + 2) * (I / 2), d + (size_t)(o + 3) * (I / 2)};
@@ -465,7 +529,7 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
                     for (size_t ti = 0; ti < nt; ++ti) {
                         float g, u;
                         const uint16_t* xt = jb.xb + (size_t)toks[ei][ti] * H;
-                        if (fp4)
+                        if (coded)
                             fp4_gate_up(b, r, xt, &g, &u);
                         else
                             dot2_bf16_avx512(W + (size_t)r * H, W + (size_t)(I + r) * H, xt, H,
@@ -479,7 +543,7 @@ void host_ffn(ThreadPool* pool, const HostJob& jb, std::vector<float>& scratch) 
                 for (int o = blk * RB2; o < std::min(H, blk * RB2 + RB2); o += 4)  // H % 4 == 0
                     for (size_t ti = 0; ti < nt; ++ti) {
                         float out[4];
-                        if (fp4)
+                        if (coded)
                             fp4_down4(b, o, hb + hoff[ei] + ti * I, out);
                         else
                             dot4_bf16_avx512(W2 + (size_t)o * I, I, hb + hoff[ei] + ti * I, I,

@@ -1,5 +1,8 @@
 // Test driver for the host-core expert routine and its thread pool (CPU only).
 //   host_driver pool            : create a pool and run at once, many times
+//   host_driver decode <fmt>    : the AVX512-BF16 route's weight decode of every code
+//                                 (FP8: bytes 0..255; fp4: the 256 byte values, two codes
+//                                 each), bf16 bit patterns as text, one per line
 //   host_driver ffn <dir>       : read meta.txt, block.bin, x.bin, ids.bin, w.bin from <dir>,
 //                                 run host_ffn with every routed expert on the host,
 //                                 write y.bin (fp32 [T,H])
@@ -52,6 +55,18 @@ int main(int argc, char** argv) {
             if (sum != 666 + 10) { printf("BAD SUM %d\n", (int)sum); return 4; }
         }
         printf("ok\n");
+        return 0;
+    }
+    if (argc >= 3 && !strcmp(argv[1], "decode")) {
+        const int fmt = atoi(argv[2]);
+        uint8_t codes[256];
+        for (int i = 0; i < 256; ++i) codes[i] = (uint8_t)i;
+        const int step = fmt == 4 ? 32 : 16;  // bytes per call
+        for (int b = 0; b < 256; b += step) {
+            uint16_t out[32];
+            if (!eo::host_decode_codes(fmt, codes + b, out)) return 3;
+            for (int i = 0; i < 32; ++i) printf("%u\n", out[i]);
+        }
         return 0;
     }
     if (argc >= 3 && !strcmp(argv[1], "ffn")) {

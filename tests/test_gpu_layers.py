@@ -74,7 +74,7 @@ def test_moe_layer_formats(fmt, T):
         eo.eo_destroy(e)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "mxfp4", "nvfp4"])
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4", "nvfp4", "fp8"])
 def test_moe_layer_with_host_execution(fmt):
     # small cache and B_P << B_H: most misses run in the host routine
     shape = small_shape(fmt)

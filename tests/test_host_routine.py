@@ -45,10 +45,11 @@ def _cpu_has_avx512bf16():
 @pytest.mark.parametrize("fmt", ["fp32", "bf16", "mxfp4", "nvfp4", "fp8"])
 def test_host_ffn_matches_oracle(driver, tmp_path, fmt, isa):
     # avx2: fp32 route (h kept in fp32), within 1e-5 of the oracle. native: on a
-    # CPU with AVX512_BF16, bf16, MXFP4 and NVFP4 experts take the bf16 pair-dot
-    # route (fp4 codes looked up as bf16, block scales on the partial sums), which
-    # rounds h to bf16 as the device does (bound: the layer tolerance, 2e-2)
-    pair_route = fmt in ("bf16", "mxfp4", "nvfp4")
+    # CPU with AVX512_BF16, bf16, MXFP4, NVFP4 and FP8 experts take the bf16
+    # pair-dot route (fp4 codes looked up as bf16 with block scales on the partial
+    # sums, fp8 codes converted through fp16), which rounds h to bf16 as the
+    # device does (bound: the layer tolerance, 2e-2)
+    pair_route = fmt in ("bf16", "mxfp4", "nvfp4", "fp8")
     if isa == "native" and pair_route and not _cpu_has_avx512bf16():
         pytest.skip("CPU without AVX512_BF16")
     f = synth.FMT_NAMES[fmt]
@@ -73,3 +74,30 @@ def test_host_ffn_matches_oracle(driver, tmp_path, fmt, isa):
     assert err <= (2e-2 if bf16_route else 1e-5), err
     if bf16_route:
         assert err > 1e-7  # the bf16 route did run (h is rounded)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "nvfp4"])
+def test_host_route_weight_decode_is_exact(driver, fmt):
+    # the AVX512-BF16 route's decode of every code against the oracle's tables:
+    # fp8 codes 0..255 give value / 256 (the dot is rescaled by 256 afterwards),
+    # fp4 bytes 0..255 give their two e2m1 values (low nibble first), unscaled;
+    # bit-exact, signed zeros included; e4m3fn's NaN codes are never stored
+    if not _cpu_has_avx512bf16():
+        pytest.skip("CPU without AVX512_BF16")
+    f = synth.FMT_NAMES[fmt]
+    r = subprocess.run([driver, "decode", str(f)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    bits = np.array([int(v) for v in r.stdout.split()], dtype=np.uint32)
+    got = (bits << 16).view(np.float32).astype(np.float64)
+    if f == synth.FMT_FP8:
+        assert got.size == 256
+        want = OF.E4M3 / 256.0
+        ok = ~np.isnan(want)
+        assert ok.sum() == 254
+    else:
+        assert got.size == 512
+        byte = np.arange(256)
+        want = np.stack([OF.E2M1[byte & 0xF], OF.E2M1[byte >> 4]], axis=1).reshape(-1)
+        ok = np.ones(512, dtype=bool)
+    assert np.array_equal(got[ok], want[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(want[ok]))

@@ -82,6 +82,14 @@ __device__ __forceinline__ const uint8_t* group_base(const GroupW& gw, int g, in
     return gw.slots + (uint64_t)s * gw.stride;
 }
 
+// Four e4m3fn codes (one word, first code in the low byte) as two bf16 pairs:
+// the scaled convert at scale 1, exact (an e4m3 value has at most 4 significant
+// bits).
+__device__ __forceinline__ void fp8x4_bf16(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+
 // Two fp4 codes (byte B of w, even element in the low nibble) as a bf16 pair,
 // times sc. The scaled convert applies only the power of two of its scale
 // operand, so it takes MXFP4's e8m0 scales whole; an NVFP4 e4m3 scale is
@@ -173,12 +181,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
                 uint4 q = *(const uint4*)(wdata + (size_t)wrow(r) * K + k0 + seg * 16);
                 uint32_t words[4] = {q.x, q.y, q.z, q.w}, out[8];
 #pragma unroll
-                for (int wi = 0; wi < 4; ++wi) {
-                    uint32_t wv = words[wi];
-                    out[2 * wi] = bf_hi(e4m3_f32(wv & 0xFF)) | (bf_hi(e4m3_f32((wv >> 8) & 0xFF)) << 16);
-                    out[2 * wi + 1] =
-                        bf_hi(e4m3_f32((wv >> 16) & 0xFF)) | (bf_hi(e4m3_f32(wv >> 24)) << 16);
-                }
+                for (int wi = 0; wi < 4; ++wi) fp8x4_bf16(words[wi], out[2 * wi], out[2 * wi + 1]);
                 uint4* d = (uint4*)(Bs + r * LDK + seg * 16);
                 d[0] = make_uint4(out[0], out[1], out[2], out[3]);
                 d[1] = make_uint4(out[4], out[5], out[6], out[7]);
@@ -449,12 +452,7 @@ __device__ __forceinline__ void v3_store(uint16_t* As, uint16_t* Bs, int tid, co
             const uint4 q = r.b[it];
             uint32_t words[4] = {q.x, q.y, q.z, q.w}, out[8];
 #pragma unroll
-            for (int wi = 0; wi < 4; ++wi) {
-                uint32_t wv = words[wi];
-                out[2 * wi] = bf_hi(e4m3_f32(wv & 0xFF)) | (bf_hi(e4m3_f32((wv >> 8) & 0xFF)) << 16);
-                out[2 * wi + 1] =
-                    bf_hi(e4m3_f32((wv >> 16) & 0xFF)) | (bf_hi(e4m3_f32(wv >> 24)) << 16);
-            }
+            for (int wi = 0; wi < 4; ++wi) fp8x4_bf16(words[wi], out[2 * wi], out[2 * wi + 1]);
             uint4* d = (uint4*)(Bs + row * V3L + seg * 16);
             d[0] = make_uint4(out[0], out[1], out[2], out[3]);
             d[1] = make_uint4(out[4], out[5], out[6], out[7]);

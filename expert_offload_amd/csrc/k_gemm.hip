@@ -12,15 +12,17 @@
 // scale — are applied to the fp32 accumulators in the epilogue. The format
 // list is the juejin.cn overview's (section 5).
 //
-// Tiles: 128 x 128 outputs per 256-thread workgroup (2 x 2 wavefronts of 64 x 64,
-// each 2 x 2 MFMA blocks of 32 x 32), K step 64. A flat tile index runs over the
-// groups' row tiles (tile_off, 128-row tiles); the N tiles are blockIdx.y.
-// GEMM1's N tile is 64 gate columns plus the same 64 up columns, split so that
-// each wavefront holds matching gate and up accumulators and forms h in
-// registers.
-//
-// fp32 weights with fp32 activations (small test models) use a plain VALU
-// kernel with the same grouping and epilogues.
+// Three kernels share the grouping (128-row tiles per group from tile_off) and
+// the GEMM1 split (each wavefront holds matching gate and up accumulators and
+// forms h in registers):
+//   v4 (bf16, the default): 128 x 256 tiles, a three-stage direct-to-LDS ring,
+//      two workgroups per CU;
+//   v3 (FP8 / MXFP4 / NVFP4, and bf16 on request): the same tiles with the next
+//      K tile staged through registers, where fp4/fp8 codes are decoded;
+//   k_gemm_mfma: plain 128 x 128 tiles, K step 64 (the reference form).
+// EO_GEMM_PATH selects among them for tests. fp32 weights with fp32 activations
+// (small test models) use a plain VALU kernel with the same grouping and
+// epilogues.
 #include <hip/hip_ext.h>
 
 #include <cstdlib>
@@ -351,7 +353,8 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs a, const float* __res
 // before the current tile's MFMAs; LDS is double-buffered (60 KB) with one
 // barrier per K step, which leaves room for two workgroups (8 wavefronts) per
 // CU. LDS rows are 40 bf16 (80 B): the 16 lanes of each ds_read_b128 quarter
-// hit 16 distinct 16-byte bank groups. The epilogue goes through LDS: scaled
+// hit 16 distinct 16-byte bank groups (the tile writes do not: about 13% of the
+// LDS activity of the fp4 kernels is bank conflicts). The epilogue goes through LDS: scaled
 // bf16 results are written there, then leave as 16-byte row segments; row ->
 // pair index and routing weight are staged once per workgroup.
 constexpr int V3M = 128, V3N = 256, V3K = 32, V3L = V3K + 8;

@@ -17,8 +17,11 @@
 // forms h in registers):
 //   v4 (bf16, the default): 128 x 256 tiles, a three-stage direct-to-LDS ring,
 //      two workgroups per CU;
-//   v3 (FP8 / MXFP4 / NVFP4, and bf16 on request): the same tiles with the next
-//      K tile staged through registers, where fp4/fp8 codes are decoded;
+//   v4q (FP8 / MXFP4 / NVFP4 GEMM1, the default): v4's ring for the activation
+//      tile, with the weight codes loaded into registers a tile ahead and decoded
+//      into the ring between the two halves of each step's MFMAs;
+//   v3 (FP8 / MXFP4 / NVFP4 GEMM2, and any GEMM on request): the same tiles with
+//      the next K tile staged through registers, where fp4/fp8 codes are decoded;
 //   k_gemm_mfma: plain 128 x 128 tiles, K step 64 (the reference form).
 // EO_GEMM_PATH selects among them for tests. fp32 weights with fp32 activations
 // (small test models) use a plain VALU kernel with the same grouping and
@@ -39,8 +42,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;  // LDS row stride in bf16
 
-// 2: bf16 weights use the async-ring kernel (v4), other formats v3; 1: v3 for all;
-// 0: the plain 128 x 128 kernel. EO_GEMM_PATH overrides.
+// 2: the async-ring kernels (v4 for bf16; for fp8 / fp4 v4q on GEMM1 and v3 on
+// GEMM2); 3: as 2 with v4q on GEMM2 too; 1: v3 for all; 0: the plain 128 x 128
+// kernel. EO_GEMM_PATH overrides.
 int g_gemm_tiles = 2;
 
 struct GemmArgs {
@@ -876,11 +880,277 @@ bool run_v4(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hi
     return true;
 }
 
+// ------------------------------------------------------------------ v4q (fp8 / fp4)
+// The v4 ring for quantised weights: the A tile arrives by direct-to-LDS loads
+// two K tiles ahead; the weight tile's codes (and fp4 block scales) are loaded
+// into registers one tile ahead, decoded exactly to bf16 (the scaled converts)
+// and written into the next stage in the ring's XOR-swizzled 64-byte rows. Each
+// thread has 2 A and 2 weight loads in flight per tile, so the wait at the top
+// of a step leaves the previous step's 4 outstanding. The decode and the next
+// codes' loads sit between the two K halves' MFMAs: placed before the first
+// half, GEMM1 ran 10-20% slower.
+template <int FMT>
+struct QRegs {
+    uint4 b[FMT == EO_W_FP8 ? 2 : 1];
+    uint32_t sc;
+};
+
+template <int FMT, int MODE>
+__device__ __forceinline__ void q_load(const GemmArgs& a, const uint8_t* wdata,
+                                       const uint8_t* wscal, int n0, int k0, int tid,
+                                       QRegs<FMT>& r) {
+    const int K = a.K;
+    if (FMT == EO_W_FP8) {  // 256 rows x 32 bytes: 512 chunks of 16 B
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int c = tid + 256 * it, row = c >> 1, seg = c & 1;
+            r.b[it] = *(const uint4*)(wdata + (size_t)v3_wrow<FMT, MODE>(a, n0, row) * K + k0 +
+                                      seg * 16);
+        }
+    } else {  // 256 rows x 16 bytes, one per thread, and the row's block scales
+        const int wr = v3_wrow<FMT, MODE>(a, n0, tid);
+        r.b[0] = *(const uint4*)(wdata + (size_t)wr * (K / 2) + k0 / 2);
+        if (FMT == EO_W_MXFP4)
+            r.sc = wscal[(size_t)wr * (K / 32) + k0 / 32];
+        else
+            r.sc = *(const uint16_t*)(wscal + (size_t)wr * (K / 16) + k0 / 16);
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void q_store(uint8_t* bst, int tid, const QRegs<FMT>& r) {
+    if (FMT == EO_W_FP8) {
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {  // 16 codes = logical segments 2*seg, 2*seg + 1
+            const int c = tid + 256 * it, row = c >> 1, seg = c & 1;
+            const uint32_t words[4] = {r.b[it].x, r.b[it].y, r.b[it].z, r.b[it].w};
+            uint32_t out[8];
+#pragma unroll
+            for (int wi = 0; wi < 4; ++wi) fp8x4_bf16(words[wi], out[2 * wi], out[2 * wi + 1]);
+            *(uint4*)(bst + row * 64 + swz(row, 2 * seg) * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+            *(uint4*)(bst + row * 64 + swz(row, 2 * seg + 1) * 16) =
+                make_uint4(out[4], out[5], out[6], out[7]);
+        }
+    } else {
+        float sc0, sc1;
+        if (FMT == EO_W_MXFP4) {
+            sc0 = sc1 = e8m0_f32(r.sc);
+        } else {
+            sc0 = e4m3_f32(r.sc & 0xFF);
+            sc1 = e4m3_f32(r.sc >> 8);
+        }
+        const uint32_t words[4] = {r.b[0].x, r.b[0].y, r.b[0].z, r.b[0].w};
+        const int row = tid;
+#pragma unroll
+        for (int wi = 0; wi < 4; ++wi) {  // 8 codes = logical segment wi
+            const float sc = wi < 2 ? sc0 : sc1;
+            *(uint4*)(bst + row * 64 + swz(row, wi) * 16) =
+                make_uint4(fp4x2_bf16<FMT, 0>(words[wi], sc), fp4x2_bf16<FMT, 1>(words[wi], sc),
+                           fp4x2_bf16<FMT, 2>(words[wi], sc), fp4x2_bf16<FMT, 3>(words[wi], sc));
+        }
+    }
+}
+
+template <int FMT, int MODE>
+__global__ __launch_bounds__(256, 2) void k_gemm_v4q(GemmArgs a, int nN) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    uint8_t* sb = (uint8_t*)smem;
+    constexpr int S = kV4Ring;
+    int32_t* s_pair = (int32_t*)(sb + (v4_pipe<S>() > kV3Out ? v4_pipe<S>() : kV3Out));
+    float* s_wp = (float*)(s_pair + V3M);
+
+    const int real = a.tile_off[a.G] * nN;
+    const int per = (real + 7) >> 3;
+    const int logical = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if ((int)(blockIdx.x >> 3) >= per || logical >= real) return;
+    const int tile = logical / nN, ntile = logical - tile * nN;
+    const int g = find_group(a.tile_off, a.G, tile);
+    const int m0 = a.offsets[g] + (tile - a.tile_off[g]) * V3M;
+    const int m_end = a.offsets[g + 1];
+    const uint8_t* wb = group_base(a.gw, g, a.E);
+    const uint8_t* wdata = wb + (MODE == 0 ? a.lay.d13 : a.lay.d2);
+    const uint8_t* wscal = wb + (MODE == 0 ? a.lay.s13 : a.lay.s2);
+    const int n0 = ntile * (MODE == 0 ? 128 : 256);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nk = a.K / V3K;
+
+    if (MODE == 1 && tid < V3M) {
+        int pair = m0 + tid < m_end ? a.perm_pair[m0 + tid] : -1;
+        s_pair[tid] = pair;
+        s_wp[tid] = pair < 0 ? 0.0f : (pair < a.Tk ? a.w[pair] : 1.0f);
+    }
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    const uint16_t* ap[2];
+    v4_arows<MODE>(a, m0, m_end, wave, lane, ap);
+    auto issue_a = [&](int kt, uint8_t* stage) {
+#pragma unroll
+        for (int it = 0; it < 2; ++it)
+            __builtin_amdgcn_global_load_lds(ap[it] + kt * V3K,
+                                             (lds_void*)(stage + (it * 4 + wave) * 1024), 16, 0, 0);
+    };
+
+    int arow[2], aseg[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        arow[i] = wm * 64 + i * 32 + (lane & 31);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) aseg[i][ks] = swz(arow[i], 2 * ks + (lane >> 5));
+    }
+    int brow_[4], bseg[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        brow_[j] = (MODE == 0 ? (j >> 1) * 128 + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32) +
+                   (lane & 31);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) bseg[j][ks] = swz(brow_[j], 2 * ks + (lane >> 5));
+    }
+
+    // prologue: A tiles 0 and 1 in flight, weight tile 0 decoded into stage 0,
+    // weight tile 1's codes in registers
+    QRegs<FMT> qr;
+    issue_a(0, sb);
+    issue_a(min(1, nk - 1), sb + kV4Stage);
+    q_load<FMT, MODE>(a, wdata, wscal, n0, 0, tid, qr);
+    q_store<FMT>(sb + V3M * 64, tid, qr);
+    q_load<FMT, MODE>(a, wdata, wscal, n0, min(1, nk - 1) * V3K, tid, qr);
+
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_vm<4>();  // A tile kt landed (the last step's 2 A + 2 weight loads may be in flight)
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's weight-tile writes done
+        __builtin_amdgcn_s_barrier();
+        issue_a(min(kt + 2, nk - 1), sb + ((kt + 2) % S) * kV4Stage);
+        const uint8_t* st = sb + (kt % S) * kV4Stage;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 av[2], bv[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) av[i] = *(const bf16x8*)(st + arow[i] * 64 + aseg[i][ks] * 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bv[j] = *(const bf16x8*)(st + V3M * 64 + brow_[j] * 64 + bseg[j][ks] * 16);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+            if (ks == 0) {  // decode weight tile kt+1 while the first half's MFMAs run
+                q_store<FMT>(sb + ((kt + 1) % S) * kV4Stage + V3M * 64, tid, qr);
+                q_load<FMT, MODE>(a, wdata, wscal, n0, min(kt + 2, nk - 1) * V3K, tid, qr);
+            }
+        }
+    }
+    wait_vm<0>();
+    __syncthreads();  // all tile loads landed and all LDS reads done: reuse as the epilogue tile
+
+    uint16_t* ot = smem;
+    const int col = lane & 31;
+    if (MODE == 0) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int c = wn * 64 + jj * 32 + col;
+            const int n = n0 + c;
+            float sg = 1.0f, su = 1.0f;
+            if (FMT == EO_W_FP8) {
+                sg = ((const float*)wscal)[n];
+                su = ((const float*)wscal)[a.I + n];
+            } else if (FMT == EO_W_NVFP4) {
+                const float* gl = (const float*)(wb + a.lay.gl);
+                sg = gl[0];
+                su = gl[1];
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    float gv = acc[i][jj][v] * sg, uv = acc[i][2 + jj][v] * su;
+                    ot[row * V3_OUT_LD + c] = (uint16_t)f32_bf16_rne(silu_f32(gv) * uv);
+                }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            int cidx = tid + 256 * it, row = cidx >> 4, seg = cidx & 15;
+            if (m0 + row < m_end)
+                *(uint4*)(a.h_out + (size_t)(m0 + row) * a.I + n0 + seg * 8) =
+                    *(const uint4*)(ot + row * V3_OUT_LD + seg * 8);
+        }
+    } else {
+        const float gs = FMT == EO_W_NVFP4 ? ((const float*)(wb + a.lay.gl))[2] : 1.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = wn * 128 + j * 32 + col;
+            const float sc = FMT == EO_W_FP8 ? ((const float*)wscal)[n0 + c] : gs;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    ot[row * V3_OUT_LD + c] = (uint16_t)f32_bf16_rne(acc[i][j][v] * sc * s_wp[row]);
+                }
+        }
+        __syncthreads();
+        uint16_t* op = (uint16_t*)a.o_pairs;
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            int cidx = tid + 256 * it, row = cidx >> 5, seg = cidx & 31;
+            int pair = s_pair[row];
+            if (pair >= 0)
+                *(uint4*)(op + (size_t)pair * a.H + n0 + seg * 8) =
+                    *(const uint4*)(ot + row * V3_OUT_LD + seg * 8);
+        }
+    }
+}
+
+// GEMM1 on v4q; GEMM2 on v4q too when `down_too`, else on v3, which measured
+// 6-14% faster for the down projection of the fp4 and FP8 prefill shapes (v4q
+// is 5-39% faster on GEMM1).
+template <int FMT>
+bool run_v4q(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, bool down_too, hipStream_t s,
+             hipEvent_t* ev) {
+    if (I % 128 || H % 256 || H % V3K || I % V3K) return false;
+    static bool attr = false;
+    if (!attr) {
+        const uint32_t lds = (uint32_t)v4_lds<kV4Ring>();
+        if (hipFuncSetAttribute((const void*)k_gemm_v4q<FMT, 0>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess ||
+            hipFuncSetAttribute((const void*)k_gemm_v4q<FMT, 1>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess ||
+            hipFuncSetAttribute((const void*)k_gemm_v3<FMT, 1>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kV3Lds) != hipSuccess)
+            return false;
+        attr = true;
+    }
+    const int n1 = I / 128, n2 = H / 256;
+    auto grid = [&](int nN) { return ((tiles * nN + 7) / 8) * 8; };
+    hipExtLaunchKernelGGL((k_gemm_v4q<FMT, 0>), dim3(grid(n1)), dim3(256), (uint32_t)v4_lds<kV4Ring>(),
+                          s, ev[0], ev[1], 0, a1, n1);
+    if (down_too)
+        hipExtLaunchKernelGGL((k_gemm_v4q<FMT, 1>), dim3(grid(n2)), dim3(256),
+                              (uint32_t)v4_lds<kV4Ring>(), s, ev[2], ev[3], 0, a2, n2);
+    else
+        hipExtLaunchKernelGGL(k_gemm_v3<FMT, 1>, dim3(grid(n2)), dim3(256), (uint32_t)kV3Lds, s,
+                              ev[2], ev[3], 0, a2, n2);
+    return true;
+}
+
 template <int FMT>
 void run_mfma(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hipEvent_t* ev) {
     if (FMT == EO_W_BF16 && g_gemm_tiles >= 2) {
         if (run_v4<kV4Ring>(a1, a2, tiles, I, H, s, ev)) return;
     }
+    if constexpr (FMT != EO_W_BF16)
+        if (g_gemm_tiles >= 2 && run_v4q<FMT>(a1, a2, tiles, I, H, g_gemm_tiles == 3, s, ev))
+            return;
     if (g_gemm_tiles && run_v3<FMT>(a1, a2, tiles, I, H, s, ev)) return;
     hipExtLaunchKernelGGL(k_gemm_mfma<FMT, 0>, dim3(tiles, I / 64), dim3(256), 0, s, ev[0], ev[1],
                           0, a1);

@@ -17,11 +17,11 @@
 // forms h in registers):
 //   v4 (bf16, the default): 128 x 256 tiles, a three-stage direct-to-LDS ring,
 //      two workgroups per CU;
-//   v4q (FP8 / MXFP4 / NVFP4 GEMM1, the default): v4's ring for the activation
-//      tile, with the weight codes loaded into registers a tile ahead and decoded
-//      into the ring between the two halves of each step's MFMAs;
-//   v3 (FP8 / MXFP4 / NVFP4 GEMM2, and any GEMM on request): the same tiles with
-//      the next K tile staged through registers, where fp4/fp8 codes are decoded;
+//   v4q (FP8 / MXFP4 / NVFP4, the default): v4's ring for the activation tile,
+//      with each weight row's next 64-byte span of codes in registers, decoded
+//      into the ring one tile per step between the two halves of its MFMAs;
+//   v3 (any format, on request): the same tiles with the next K tile staged
+//      through registers, where fp4/fp8 codes are decoded;
 //   k_gemm_mfma: plain 128 x 128 tiles, K step 64 (the reference form).
 // EO_GEMM_PATH selects among them for tests. fp32 weights with fp32 activations
 // (small test models) use a plain VALU kernel with the same grouping and
@@ -42,9 +42,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;  // LDS row stride in bf16
 
-// 2: the async-ring kernels (v4 for bf16; for fp8 / fp4 v4q on GEMM1 and v3 on
-// GEMM2); 3: as 2 with v4q on GEMM2 too; 1: v3 for all; 0: the plain 128 x 128
-// kernel. EO_GEMM_PATH overrides.
+// 2: the async-ring kernels (v4 for bf16, v4q for fp8 / fp4); 1: v3 for all;
+// 0: the plain 128 x 128 kernel. EO_GEMM_PATH overrides.
 int g_gemm_tiles = 2;
 
 struct GemmArgs {
@@ -882,71 +881,103 @@ bool run_v4(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hi
 
 // ------------------------------------------------------------------ v4q (fp8 / fp4)
 // The v4 ring for quantised weights: the A tile arrives by direct-to-LDS loads
-// two K tiles ahead; the weight tile's codes (and fp4 block scales) are loaded
-// into registers one tile ahead, decoded exactly to bf16 (the scaled converts)
-// and written into the next stage in the ring's XOR-swizzled 64-byte rows. Each
-// thread has 2 A and 2 weight loads in flight per tile, so the wait at the top
-// of a step leaves the previous step's 4 outstanding. The decode and the next
-// codes' loads sit between the two K halves' MFMAs: placed before the first
-// half, GEMM1 ran 10-20% slower.
+// two K tiles ahead; each thread holds one weight row's next 64-byte span of
+// codes (two FP8 tiles, four fp4 tiles, with the fp4 block scales) in
+// registers, decodes one tile of it per step exactly to bf16 (the scaled
+// converts) and writes it into the next stage in the ring's XOR-swizzled
+// 64-byte rows. The decode and the next span's loads sit between the two K
+// halves' MFMAs (placed before the first half, GEMM1 ran 10-20% slower). The K
+// loop is unrolled by the span so that each step's wait for its A tile is a
+// constant.
+
+// A load through a global (address space 1) pointer. The weight pointers come
+// out of a table, so the compiler cannot tell they are global and would emit
+// flat loads; while a flat load is outstanding it waits for vmcnt(0) before
+// every LDS access, which drains the ring's activation loads each step.
+// T is a scalar or clang vector type (HIP's struct vector types still become
+// flat loads).
+template <typename T>
+__device__ __forceinline__ T gload(const void* p) {
+    return *(const __attribute__((address_space(1))) T*)p;
+}
+
+// A 16-byte LDS store that the compiler's wait insertion does not see. The
+// decoded weight rows go to a stage's B region while the ring's direct-to-LDS
+// loads are in flight to A regions; the compiler cannot tell the addresses
+// apart and would wait for every outstanding load before a plain LDS store,
+// i.e. for the activation tile issued at the top of the same step. The store
+// has no outputs; its completion is covered by the lgkmcnt(0) before each
+// step's barrier, and one wavefront's LDS operations complete in order.
+__device__ __forceinline__ void lds_store16(uint8_t* p, u32x4 v) {
+    const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)p;
+    asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+// One weight row's next 64 contiguous bytes per thread (row = thread): two K
+// tiles of FP8 codes, or four of fp4 codes with their block scales. Requested
+// together, so a row's 128-byte line is fetched once per span, not once per tile.
 template <int FMT>
 struct QRegs {
-    uint4 b[FMT == EO_W_FP8 ? 2 : 1];
-    uint32_t sc;
+    u32x4 s0, s1, s2, s3;
+    uint32_t ss0, ss1;
 };
 
 template <int FMT, int MODE>
 __device__ __forceinline__ void q_load(const GemmArgs& a, const uint8_t* wdata,
                                        const uint8_t* wscal, int n0, int k0, int tid,
                                        QRegs<FMT>& r) {
+    // row tid's span from k0 (k0 % 64 == 0 for FP8, % 128 for fp4): 4 loads,
+    // plus 1 for the fp4 block scales
     const int K = a.K;
-    if (FMT == EO_W_FP8) {  // 256 rows x 32 bytes: 512 chunks of 16 B
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int c = tid + 256 * it, row = c >> 1, seg = c & 1;
-            r.b[it] = *(const uint4*)(wdata + (size_t)v3_wrow<FMT, MODE>(a, n0, row) * K + k0 +
-                                      seg * 16);
-        }
-    } else {  // 256 rows x 16 bytes, one per thread, and the row's block scales
-        const int wr = v3_wrow<FMT, MODE>(a, n0, tid);
-        r.b[0] = *(const uint4*)(wdata + (size_t)wr * (K / 2) + k0 / 2);
-        if (FMT == EO_W_MXFP4)
-            r.sc = wscal[(size_t)wr * (K / 32) + k0 / 32];
-        else
-            r.sc = *(const uint16_t*)(wscal + (size_t)wr * (K / 16) + k0 / 16);
+    const int wr = v3_wrow<FMT, MODE>(a, n0, tid);
+    const uint8_t* rp = wdata + (FMT == EO_W_FP8 ? (size_t)wr * K + k0 : (size_t)wr * (K / 2) + k0 / 2);
+    r.s0 = gload<u32x4>(rp);
+    r.s1 = gload<u32x4>(rp + 16);
+    r.s2 = gload<u32x4>(rp + 32);
+    r.s3 = gload<u32x4>(rp + 48);
+    if (FMT == EO_W_MXFP4) {
+        r.ss0 = gload<uint32_t>(wscal + (size_t)wr * (K / 32) + k0 / 32);
+    } else if (FMT == EO_W_NVFP4) {
+        const uint64_t q = gload<uint64_t>(wscal + (size_t)wr * (K / 16) + k0 / 16);
+        r.ss0 = (uint32_t)q;
+        r.ss1 = (uint32_t)(q >> 32);
     }
 }
 
-template <int FMT>
+// Decodes tile U of the span (fp4) or the loaded tile (FP8) into the stage's
+// weight rows.
+template <int FMT, int U>
 __device__ __forceinline__ void q_store(uint8_t* bst, int tid, const QRegs<FMT>& r) {
     if (FMT == EO_W_FP8) {
+        const int row = tid;
 #pragma unroll
-        for (int it = 0; it < 2; ++it) {  // 16 codes = logical segments 2*seg, 2*seg + 1
-            const int c = tid + 256 * it, row = c >> 1, seg = c & 1;
-            const uint32_t words[4] = {r.b[it].x, r.b[it].y, r.b[it].z, r.b[it].w};
+        for (int h = 0; h < 2; ++h) {  // 16 codes = logical segments 2h, 2h + 1
+            const u32x4 v = U == 0 ? (h == 0 ? r.s0 : r.s1) : (h == 0 ? r.s2 : r.s3);
             uint32_t out[8];
 #pragma unroll
-            for (int wi = 0; wi < 4; ++wi) fp8x4_bf16(words[wi], out[2 * wi], out[2 * wi + 1]);
-            *(uint4*)(bst + row * 64 + swz(row, 2 * seg) * 16) = make_uint4(out[0], out[1], out[2], out[3]);
-            *(uint4*)(bst + row * 64 + swz(row, 2 * seg + 1) * 16) =
-                make_uint4(out[4], out[5], out[6], out[7]);
+            for (int wi = 0; wi < 4; ++wi) fp8x4_bf16(v[wi], out[2 * wi], out[2 * wi + 1]);
+            lds_store16(bst + row * 64 + swz(row, 2 * h) * 16, u32x4{out[0], out[1], out[2], out[3]});
+            lds_store16(bst + row * 64 + swz(row, 2 * h + 1) * 16,
+                        u32x4{out[4], out[5], out[6], out[7]});
         }
     } else {
+        const u32x4 v = U == 0 ? r.s0 : U == 1 ? r.s1 : U == 2 ? r.s2 : r.s3;
         float sc0, sc1;
         if (FMT == EO_W_MXFP4) {
-            sc0 = sc1 = e8m0_f32(r.sc);
+            sc0 = sc1 = e8m0_f32((r.ss0 >> (8 * U)) & 0xFFu);
         } else {
-            sc0 = e4m3_f32(r.sc & 0xFF);
-            sc1 = e4m3_f32(r.sc >> 8);
+            const uint32_t sc = ((U < 2 ? r.ss0 : r.ss1) >> (16 * (U & 1))) & 0xFFFFu;
+            sc0 = e4m3_f32(sc & 0xFF);
+            sc1 = e4m3_f32(sc >> 8);
         }
-        const uint32_t words[4] = {r.b[0].x, r.b[0].y, r.b[0].z, r.b[0].w};
+        const uint32_t words[4] = {v[0], v[1], v[2], v[3]};
         const int row = tid;
 #pragma unroll
         for (int wi = 0; wi < 4; ++wi) {  // 8 codes = logical segment wi
             const float sc = wi < 2 ? sc0 : sc1;
-            *(uint4*)(bst + row * 64 + swz(row, wi) * 16) =
-                make_uint4(fp4x2_bf16<FMT, 0>(words[wi], sc), fp4x2_bf16<FMT, 1>(words[wi], sc),
-                           fp4x2_bf16<FMT, 2>(words[wi], sc), fp4x2_bf16<FMT, 3>(words[wi], sc));
+            lds_store16(bst + row * 64 + swz(row, wi) * 16,
+                        u32x4{fp4x2_bf16<FMT, 0>(words[wi], sc), fp4x2_bf16<FMT, 1>(words[wi], sc),
+                              fp4x2_bf16<FMT, 2>(words[wi], sc), fp4x2_bf16<FMT, 3>(words[wi], sc)});
         }
     }
 }
@@ -1014,37 +1045,86 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v4q(GemmArgs a, int nN) {
         for (int ks = 0; ks < 2; ++ks) bseg[j][ks] = swz(brow_[j], 2 * ks + (lane >> 5));
     }
 
-    // prologue: A tiles 0 and 1 in flight, weight tile 0 decoded into stage 0,
-    // weight tile 1's codes in registers
+    auto mma_half = [&](const uint8_t* st, int ks) {
+        bf16x8 av[2], bv[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) av[i] = *(const bf16x8*)(st + arow[i] * 64 + aseg[i][ks] * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            bv[j] = *(const bf16x8*)(st + V3M * 64 + brow_[j] * 64 + bseg[j][ks] * 16);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    };
+    auto bstage = [&](int kt) { return sb + (kt % S) * kV4Stage + V3M * 64; };
+
     QRegs<FMT> qr;
     issue_a(0, sb);
     issue_a(min(1, nk - 1), sb + kV4Stage);
-    q_load<FMT, MODE>(a, wdata, wscal, n0, 0, tid, qr);
-    q_store<FMT>(sb + V3M * 64, tid, qr);
-    q_load<FMT, MODE>(a, wdata, wscal, n0, min(1, nk - 1) * V3K, tid, qr);
-
-    for (int kt = 0; kt < nk; ++kt) {
-        wait_vm<4>();  // A tile kt landed (the last step's 2 A + 2 weight loads may be in flight)
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's weight-tile writes done
-        __builtin_amdgcn_s_barrier();
-        issue_a(min(kt + 2, nk - 1), sb + ((kt + 2) % S) * kV4Stage);
-        const uint8_t* st = sb + (kt % S) * kV4Stage;
+    if constexpr (FMT == EO_W_FP8) {
+        // nk % 2 == 0: the span of tiles 2j, 2j+1 is decoded during steps 2j-1
+        // and 2j; span j+1 is requested at step 2j, right after its last decode,
+        // and first used at step 2j+1. Loads issued after A tile kt at the top of
+        // step kt: 2 (A tile kt+1), plus the 4 of the span requested at step kt-1
+        // when kt is odd (when kt is even that span was consumed by the previous
+        // step's decode, so it is done).
+        q_load<FMT, MODE>(a, wdata, wscal, n0, 0, tid, qr);
+        q_store<FMT, 0>(bstage(0), tid, qr);
+        for (int kt0 = 0; kt0 < nk; kt0 += 2) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 av[2], bv[4];
+            for (int u = 0; u < 2; ++u) {
+                const int kt = kt0 + u;
+                if (u == 1)
+                    wait_vm<6>();
+                else
+                    wait_vm<2>();
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's weight-tile writes done
+                __builtin_amdgcn_s_barrier();
+                issue_a(min(kt + 2, nk - 1), sb + ((kt + 2) % S) * kV4Stage);
+                const uint8_t* st = sb + (kt % S) * kV4Stage;
+                mma_half(st, 0);
+                // decode weight tile kt+1 while the first half's MFMAs run
+                if (u == 0) {
+                    q_store<FMT, 1>(bstage(kt + 1), tid, qr);
+                    q_load<FMT, MODE>(a, wdata, wscal, n0, min(kt0 + 2, nk - 2) * V3K, tid, qr);
+                } else {
+                    q_store<FMT, 0>(bstage(kt + 1), tid, qr);
+                }
+                mma_half(st, 1);
+            }
+        }
+    } else {
+        // fp4 (nk % 4 == 0): the span of tiles 4j..4j+3 is decoded one tile per
+        // step during steps 4j-1..4j+2; span j+1 is requested at step 4j+2, right
+        // after its last decode, and first used at step 4j+3. Loads issued after
+        // A tile kt at the top of step kt: 2 (A tile kt+1) in general, plus the 5
+        // of the span requested at step kt-1 when kt % 4 == 3 (at kt % 4 == 0
+        // that span was consumed by the previous step's decode, so it is done).
+        q_load<FMT, MODE>(a, wdata, wscal, n0, 0, tid, qr);
+        q_store<FMT, 0>(bstage(0), tid, qr);
+        for (int kt0 = 0; kt0 < nk; kt0 += 4) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) av[i] = *(const bf16x8*)(st + arow[i] * 64 + aseg[i][ks] * 16);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bv[j] = *(const bf16x8*)(st + V3M * 64 + brow_[j] * 64 + bseg[j][ks] * 16);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-            if (ks == 0) {  // decode weight tile kt+1 while the first half's MFMAs run
-                q_store<FMT>(sb + ((kt + 1) % S) * kV4Stage + V3M * 64, tid, qr);
-                q_load<FMT, MODE>(a, wdata, wscal, n0, min(kt + 2, nk - 1) * V3K, tid, qr);
+            for (int u = 0; u < 4; ++u) {
+                const int kt = kt0 + u;
+                if (u == 3)
+                    wait_vm<7>();
+                else
+                    wait_vm<2>();
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+                __builtin_amdgcn_s_barrier();
+                issue_a(min(kt + 2, nk - 1), sb + ((kt + 2) % S) * kV4Stage);
+                const uint8_t* st = sb + (kt % S) * kV4Stage;
+                mma_half(st, 0);
+                if (u == 0) q_store<FMT, 1>(bstage(kt + 1), tid, qr);
+                if (u == 1) q_store<FMT, 2>(bstage(kt + 1), tid, qr);
+                if (u == 2) {
+                    q_store<FMT, 3>(bstage(kt + 1), tid, qr);
+                    q_load<FMT, MODE>(a, wdata, wscal, n0, min(kt0 + 4, nk - 4) * V3K, tid, qr);
+                }
+                if (u == 3) q_store<FMT, 0>(bstage(kt + 1), tid, qr);
+                mma_half(st, 1);
             }
         }
     }
@@ -1111,22 +1191,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v4q(GemmArgs a, int nN) {
     }
 }
 
-// GEMM1 on v4q; GEMM2 on v4q too when `down_too`, else on v3, which measured
-// 6-14% faster for the down projection of the fp4 and FP8 prefill shapes (v4q
-// is 5-39% faster on GEMM1).
 template <int FMT>
-bool run_v4q(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, bool down_too, hipStream_t s,
-             hipEvent_t* ev) {
-    if (I % 128 || H % 256 || H % V3K || I % V3K) return false;
+bool run_v4q(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hipEvent_t* ev) {
+    if (I % 128 || H % 256) return false;  // K = H or I: whole 2- or 4-tile spans
     static bool attr = false;
     if (!attr) {
         const uint32_t lds = (uint32_t)v4_lds<kV4Ring>();
         if (hipFuncSetAttribute((const void*)k_gemm_v4q<FMT, 0>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess ||
             hipFuncSetAttribute((const void*)k_gemm_v4q<FMT, 1>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess ||
-            hipFuncSetAttribute((const void*)k_gemm_v3<FMT, 1>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kV3Lds) != hipSuccess)
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
             return false;
         attr = true;
     }
@@ -1134,12 +1208,8 @@ bool run_v4q(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, bool down_too, h
     auto grid = [&](int nN) { return ((tiles * nN + 7) / 8) * 8; };
     hipExtLaunchKernelGGL((k_gemm_v4q<FMT, 0>), dim3(grid(n1)), dim3(256), (uint32_t)v4_lds<kV4Ring>(),
                           s, ev[0], ev[1], 0, a1, n1);
-    if (down_too)
-        hipExtLaunchKernelGGL((k_gemm_v4q<FMT, 1>), dim3(grid(n2)), dim3(256),
-                              (uint32_t)v4_lds<kV4Ring>(), s, ev[2], ev[3], 0, a2, n2);
-    else
-        hipExtLaunchKernelGGL(k_gemm_v3<FMT, 1>, dim3(grid(n2)), dim3(256), (uint32_t)kV3Lds, s,
-                              ev[2], ev[3], 0, a2, n2);
+    hipExtLaunchKernelGGL((k_gemm_v4q<FMT, 1>), dim3(grid(n2)), dim3(256), (uint32_t)v4_lds<kV4Ring>(),
+                          s, ev[2], ev[3], 0, a2, n2);
     return true;
 }
 
@@ -1149,8 +1219,7 @@ void run_mfma(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, 
         if (run_v4<kV4Ring>(a1, a2, tiles, I, H, s, ev)) return;
     }
     if constexpr (FMT != EO_W_BF16)
-        if (g_gemm_tiles >= 2 && run_v4q<FMT>(a1, a2, tiles, I, H, g_gemm_tiles == 3, s, ev))
-            return;
+        if (g_gemm_tiles >= 2 && run_v4q<FMT>(a1, a2, tiles, I, H, s, ev)) return;
     if (g_gemm_tiles && run_v3<FMT>(a1, a2, tiles, I, H, s, ev)) return;
     hipExtLaunchKernelGGL(k_gemm_mfma<FMT, 0>, dim3(tiles, I / 64), dim3(256), 0, s, ev[0], ev[1],
                           0, a1);

@@ -503,14 +503,13 @@ def test_static_placement_then_lru():
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4", "nvfp4"])
 def test_every_gemm_and_gemv_kernel_against_the_oracle(fmt, monkeypatch):
-    # the grouped GEMM's kernels (plain 128x128, register-prefetch 128x256,
-    # async-ring 128x256: v4 for bf16, v4q for quantised weights on GEMM1, and on
-    # GEMM2 too under path 3) and both decode GEMV families on one shape, each
-    # against the oracle
+    # the grouped GEMM's three kernels (plain 128x128, register-prefetch
+    # 128x256, async-ring 128x256: v4 for bf16, v4q for quantised weights) and
+    # both decode GEMV families on one shape, each against the oracle
     shape = small_shape(fmt)
     seed = 19
     x = synth.activations(seed, 77, 300, shape.hidden, 1.0, True)
-    for path in ("0", "1", "2", "3"):
+    for path in ("0", "1", "2"):
         monkeypatch.setenv("EO_GEMM_PATH", path)
         e = make_engine(shape, seed, max_tokens=300)
         try:

@@ -12,7 +12,7 @@
 // scale — are applied to the fp32 accumulators in the epilogue. The format
 // list is the juejin.cn overview's (section 5).
 //
-// Three kernels share the grouping (128-row tiles per group from tile_off) and
+// Four kernels share the grouping (128-row tiles per group from tile_off) and
 // the GEMM1 split (each wavefront holds matching gate and up accumulators and
 // forms h in registers):
 //   v4 (bf16, the default): 128 x 256 tiles, a three-stage direct-to-LDS ring,

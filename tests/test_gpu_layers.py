@@ -502,6 +502,30 @@ def test_static_placement_then_lru():
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4", "nvfp4"])
+def test_grouped_gemm_at_its_shortest_contraction(fmt, monkeypatch):
+    # H 256, I 128: the down projection's K of 128 is a single four-tile fp4 span
+    # (two FP8 spans), so the async-ring kernel's prologue span is its only one
+    # and every span request past it is clamped; gate/up has K 256. Every kernel
+    # path, ragged groups (197 tokens over 8 experts, top-2, one shared expert).
+    shape = synth.LayerShape(f"short_k_{fmt}", "test", 256, 8, 2, 128, 1,
+                             synth.FMT_NAMES[fmt], 197, 8, shared=1)
+    seed = 23
+    x = synth.activations(seed, 91, 197, shape.hidden, 1.0, True)
+    for path in ("0", "1", "2"):
+        monkeypatch.setenv("EO_GEMM_PATH", path)
+        e = make_engine(shape, seed, max_tokens=197)
+        try:
+            eo.eo_set_bandwidth(e, 50, 50)
+            y = torch.zeros((197, shape.hidden), dtype=torch.float32, device="cuda")
+            eo.eo_moe_layer(e, 0, dev(x.view(np.int16)), y, 197, None, _stream())
+            torch.cuda.synchronize()
+            check_layer(shape, seed, 0, x, y.cpu().numpy())
+        finally:
+            eo.eo_destroy(e)
+    monkeypatch.delenv("EO_GEMM_PATH")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4", "nvfp4"])
 def test_every_gemm_and_gemv_kernel_against_the_oracle(fmt, monkeypatch):
     # the grouped GEMM's three kernels (plain 128x128, register-prefetch
     # 128x256, async-ring 128x256: v4 for bf16, v4q for quantised weights) and

@@ -759,16 +759,20 @@ eo_status eo_set_router(eo_engine* e, int32_t layer, const float* host_w) {
     HIPCHK(hipSetDevice(e->cfg.device));
     HIPCHK(hipMemcpy(e->d_router + (size_t)layer * e->E * e->H, host_w,
                      sizeof(float) * e->E * e->H, hipMemcpyHostToDevice));
-    // chain-interleaved copy: Rq[e][j/4][i][j%4] = R[e][i + 64 j]
-    const int J = e->H / 64;
-    std::vector<float> rt((size_t)e->E * e->H);
-    for (int x = 0; x < e->E; ++x)
-        for (int j = 0; j < J; ++j)
-            for (int i = 0; i < 64; ++i)
-                rt[(size_t)x * e->H + ((size_t)(j / 4) * 64 + i) * 4 + (j % 4)] =
-                    host_w[(size_t)x * e->H + i + 64 * j];
-    HIPCHK(hipMemcpy(e->d_router_t + (size_t)layer * e->E * e->H, rt.data(),
-                     sizeof(float) * e->E * e->H, hipMemcpyHostToDevice));
+    // chain-interleaved copy: Rq[e][j/4][i][j%4] = R[e][i + 64 j]. It needs the
+    // chain steps j < H/64 in whole groups of four (H % 256 == 0), or the index
+    // runs past the row; the chained router kernel reads it only when H % 512 == 0.
+    if (e->H % 256 == 0) {
+        const int J = e->H / 64;
+        std::vector<float> rt((size_t)e->E * e->H);
+        for (int x = 0; x < e->E; ++x)
+            for (int j = 0; j < J; ++j)
+                for (int i = 0; i < 64; ++i)
+                    rt[(size_t)x * e->H + ((size_t)(j / 4) * 64 + i) * 4 + (j % 4)] =
+                        host_w[(size_t)x * e->H + i + 64 * j];
+        HIPCHK(hipMemcpy(e->d_router_t + (size_t)layer * e->E * e->H, rt.data(),
+                         sizeof(float) * e->E * e->H, hipMemcpyHostToDevice));
+    }
     return EO_OK;
 }
 

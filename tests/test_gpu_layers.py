@@ -526,6 +526,27 @@ def test_grouped_gemm_at_its_shortest_contraction(fmt, monkeypatch):
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4", "nvfp4"])
+def test_grouped_gemm_falls_back_on_shapes_the_tiled_kernels_reject(fmt):
+    # H 384, I 192: neither dimension fits the 128 x 256 tiles (I % 128, H % 256),
+    # so the default path must hand both projections to the plain 128 x 128 kernel.
+    # H 384 is also an odd multiple of 128: setting the router once wrote its
+    # chain-interleaved copy past the end of the host buffer at such sizes.
+    shape = synth.LayerShape(f"odd_{fmt}", "test", 384, 8, 2, 192, 1,
+                             synth.FMT_NAMES[fmt], 150, 8, shared=1)
+    seed = 29
+    x = synth.activations(seed, 93, 150, shape.hidden, 1.0, True)
+    e = make_engine(shape, seed, max_tokens=150)
+    try:
+        eo.eo_set_bandwidth(e, 50, 50)
+        y = torch.zeros((150, shape.hidden), dtype=torch.float32, device="cuda")
+        eo.eo_moe_layer(e, 0, dev(x.view(np.int16)), y, 150, None, _stream())
+        torch.cuda.synchronize()
+        check_layer(shape, seed, 0, x, y.cpu().numpy())
+    finally:
+        eo.eo_destroy(e)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4", "nvfp4"])
 def test_every_gemm_and_gemv_kernel_against_the_oracle(fmt, monkeypatch):
     # the grouped GEMM's three kernels (plain 128x128, register-prefetch
     # 128x256, async-ring 128x256: v4 for bf16, v4q for quantised weights) and

@@ -546,6 +546,34 @@ def test_grouped_gemm_falls_back_on_shapes_the_tiled_kernels_reject(fmt):
         eo.eo_destroy(e)
 
 
+@pytest.mark.parametrize("lane", ["fill", "host"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4", "nvfp4"])
+def test_one_token_calls_at_an_odd_multiple_of_128(fmt, lane):
+    # H 384, I 192 at T = 1: no tuned GEMV instantiation fits, so the generic
+    # GEMV runs; B_P = B_H fills every miss, B_P << B_H sends every miss to the
+    # host routine (its vector route needs H % 128 and I % 64 only)
+    shape = synth.LayerShape(f"odd1_{fmt}", "test", 384, 8, 2, 192, 1,
+                             synth.FMT_NAMES[fmt], 1, 4, shared=1)
+    seed = 31
+    e = make_engine(shape, seed, max_tokens=1)
+    try:
+        eo.eo_set_bandwidth(e, 50, 50) if lane == "fill" else eo.eo_set_bandwidth(e, 1, 100000)
+        st0 = eo.eo_stats_get(e)
+        for t in range(6):
+            x = synth.activations(seed, 200 + t, 1, shape.hidden, 1.0, True)
+            y = torch.zeros((1, shape.hidden), dtype=torch.float32, device="cuda")
+            eo.eo_moe_layer(e, 0, dev(x.view(np.int16)), y, 1, None, _stream())
+            torch.cuda.synchronize()
+            check_layer(shape, seed, 0, x, y.cpu().numpy())
+        st1 = eo.eo_stats_get(e)
+        if lane == "host":
+            assert st1["host_experts"] > st0["host_experts"] and st1["fills"] == st0["fills"]
+        else:
+            assert st1["fills"] > st0["fills"] and st1["host_experts"] == st0["host_experts"]
+    finally:
+        eo.eo_destroy(e)
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4", "nvfp4"])
 def test_every_gemm_and_gemv_kernel_against_the_oracle(fmt, monkeypatch):
     # the grouped GEMM's three kernels (plain 128x128, register-prefetch

@@ -9,6 +9,8 @@ bench.py times, on outputs the oracle can compute one by one.
 * MXFP4 decode (hidden 4096, 256 experts + shared, inter 2048, 11% cache) and
   NVFP4 prefill + decode (hidden 6144, 256 experts + shared, inter 2048) at full
   per-layer shape with fewer layers.
+* The same decode and prefill checks on a small two-layer model whose hidden size
+  is an odd multiple of 128 (the kernels' generic paths).
 """
 import numpy as np
 import pytest
@@ -145,5 +147,22 @@ def test_nvfp4_prefill_and_decode_full_layer_shape():
         eo.eo_set_bandwidth(e, BP, BH)
         _prefill_and_check(e, shape, 2, base.tokens, range(L), 4)
         _decode_and_check(e, shape, 2, 2, lambda s: range(L), 128)
+    finally:
+        eo.eo_destroy(e)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4", "nvfp4"])
+def test_decode_steps_and_prefill_at_an_odd_multiple_of_128(fmt):
+    # two layers with H 384, I 192: the separate norm / router / plan kernels
+    # (the fused layer entry needs H % 512), the generic GEMV, and a streamed
+    # prefill through the plain grouped GEMM; the cache state is replayed by the
+    # oracle after every decode step
+    shape = synth.LayerShape(f"odd_{fmt}", "prefill+decode", 384, 8, 2, 192, 2,
+                             synth.FMT_NAMES[fmt], 96, 6, shared=1)
+    e = make_engine(shape, 3, max_tokens=96)
+    try:
+        eo.eo_set_bandwidth(e, BP, BH)
+        _decode_and_check(e, shape, 3, 5, lambda s: range(2), shape.cache_slots)
+        _prefill_and_check(e, shape, 3, 96, range(2), 12)
     finally:
         eo.eo_destroy(e)

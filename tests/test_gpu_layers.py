@@ -546,6 +546,29 @@ def test_grouped_gemm_falls_back_on_shapes_the_tiled_kernels_reject(fmt):
         eo.eo_destroy(e)
 
 
+@pytest.mark.parametrize("T", [1, 40])
+@pytest.mark.parametrize("experts,top_k", [(5, 1), (6, 6), (12, 3)])
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+def test_expert_counts_and_top_k_edges(fmt, experts, top_k, T):
+    # expert counts that are not a multiple of 4 (the routers' 4- and 8-wide
+    # groups run past E), top-1, and top-k = E (every token routes to every
+    # expert), no shared expert; cache of 3 slots, half the misses on the host
+    shape = synth.LayerShape(f"edge_{fmt}_{experts}_{top_k}", "test", 256, experts, top_k, 128,
+                             1, synth.FMT_NAMES[fmt], T, 3, shared=0)
+    seed = 37
+    e = make_engine(shape, seed, max_tokens=T)
+    try:
+        eo.eo_set_bandwidth(e, 50, 100)
+        for c in range(3):
+            x = synth.activations(seed, 300 + c, T, shape.hidden, 1.0, True)
+            y = torch.zeros((T, shape.hidden), dtype=torch.float32, device="cuda")
+            eo.eo_moe_layer(e, 0, dev(x.view(np.int16)), y, T, None, _stream())
+            torch.cuda.synchronize()
+            check_layer(shape, seed, 0, x, y.cpu().numpy())
+    finally:
+        eo.eo_destroy(e)
+
+
 @pytest.mark.parametrize("lane", ["fill", "host"])
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4", "nvfp4"])
 def test_one_token_calls_at_an_odd_multiple_of_128(fmt, lane):

@@ -143,3 +143,105 @@ def test_fp8_random_weights_error_bound():
         # the row maximum maps to 448 exactly (up to the fp32 rounding of s)
         rowmax = np.abs(a).max(axis=1).astype(np.float64)
         assert np.allclose(rowmax, np.abs(b).max(axis=1), rtol=2.0 ** -22, atol=0)
+
+
+# ---- NVFP4 global scale: one rounding after the exact code x block-scale product
+
+def _round_f32(x: "Fraction") -> np.float32:
+    """Round a rational to fp32, nearest with ties to even (normal range only)."""
+    from fractions import Fraction
+    if x == 0:
+        return np.float32(0.0)
+    sign, a = (-1, -x) if x < 0 else (1, x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    assert -126 <= e <= 127, "outside the fp32 normal range"
+    ulp = Fraction(2) ** (e - 23)
+    n, rem = divmod(a, ulp)
+    n = int(n)
+    if rem > ulp / 2 or (rem == ulp / 2 and n % 2 == 1):
+        n += 1
+    return np.float32(sign * float(n * ulp))
+
+
+def _nvfp4_block(c13, c2, s13, s2, g):
+    """Pack NVFP4 codes by the documented layout (data | scales | globals),
+    even element in the low nibble."""
+    def nib(c):
+        c = c.reshape(-1, 2).astype(np.uint8)
+        return (c[:, 0] | (c[:, 1] << 4)).astype(np.uint8)
+    return np.concatenate([nib(c13), nib(c2), s13.ravel().astype(np.uint8),
+                           s2.ravel().astype(np.uint8),
+                           np.asarray(g, dtype=np.float32).view(np.uint8)])
+
+
+def test_nvfp4_global_scale_hand_worked():
+    # e2m1 code 3 = 1.5, e4m3 code 0x36 = 2^-1 * 1.75 = 0.875: the product is
+    # 21/16, exact in fp32. g = fp32(1/3) = 11184811 * 2^-25. Then
+    # (21/16) * g = 234881031 * 2^-29 = 0.4375 + 0.4375 ulp (ulp = 2^-25 in
+    # [1/4, 1/2)), which rounds down to 0.4375 = 0x3EE00000. The other order,
+    # 1.5 * fp32(0.875 * g) = 1.5 * 9786710 * 2^-25 = 14680065 * 2^-25, gives
+    # 0x3EE00001: the oracle must produce the first.
+    H, I = 16, 16
+    c13 = np.zeros((2 * I, H), dtype=np.uint8)
+    c2 = np.zeros((H, I), dtype=np.uint8)
+    s13 = np.full((2 * I, H // 16), 0x38, dtype=np.uint8)  # 1.0
+    s2 = np.full((H, I // 16), 0x38, dtype=np.uint8)
+    c13[0, 0] = 3
+    s13[0, 0] = 0x36
+    c2[5, 7] = 3 | 8     # -1.5
+    s2[5, 0] = 0x36
+    g = np.array([1 / 3, 1.0, 1 / 3], dtype=np.float32)
+    assert g[0].view(np.uint32) == 0x3EAAAAAB
+    wg, wu, wd = F.dequant_expert(_nvfp4_block(c13, c2, s13, s2, g), H, I, F.NVFP4)
+    assert wg[0, 0].view(np.uint32) == 0x3EE00000
+    assert wd[5, 7].view(np.uint32) == 0xBEE00000
+    wrong = np.float32(1.5) * (np.float32(0.875) * g[0])
+    assert wrong.view(np.uint32) == 0x3EE00001
+
+
+def test_nvfp4_every_code_and_scale_with_non_power_of_two_globals():
+    """Every e2m1 code against every finite e4m3 block scale, under three
+    global scales that are not powers of two, against exact rational
+    arithmetic rounded once to fp32."""
+    from fractions import Fraction
+    scales = np.array([s for s in range(256) if (s & 0x7F) != 0x7F], dtype=np.uint8)  # 254
+    H = 16 * len(scales)  # one 16-element block per scale code
+    I = 16
+    codes = np.tile(np.arange(16, dtype=np.uint8), H // 16)  # one of each code per block
+    c13 = np.tile(codes, (2 * I, 1))
+    s13 = np.tile(scales, (2 * I, 1))
+    rng = np.random.default_rng(3)
+    c2 = rng.integers(0, 16, size=(H, I)).astype(np.uint8)
+    s2 = rng.choice(scales, size=(H, I // 16)).astype(np.uint8)
+    g = np.array([1 / 3, 0.1, -2.7], dtype=np.float32)
+    wg, wu, wd = F.dequant_expert(_nvfp4_block(c13, c2, s13, s2, g), H, I, F.NVFP4)
+
+    def exact(code, sc, gl):
+        s, e, m = (code >> 3) & 1, (code >> 1) & 3, code & 1
+        v = Fraction(m, 2) if e == 0 else (1 + Fraction(m, 2)) * Fraction(2) ** (e - 1)
+        se, ee, me = (sc >> 7) & 1, (sc >> 3) & 15, sc & 7
+        b = Fraction(me, 8) * Fraction(2) ** -6 if ee == 0 else \
+            (1 + Fraction(me, 8)) * Fraction(2) ** (ee - 7)
+        sign = (-1) ** (s + se)
+        return sign, v * b * Fraction(float(gl))
+
+    differ = 0
+    for row, (w, gl) in ((0, (wg, g[0])), (3, (wu, g[1]))):
+        for col in range(H):
+            sign, x = exact(int(c13[row, col]), int(s13[row, col // 16]), gl)
+            ref = _round_f32(sign * x)
+            got = w[row, col]
+            if x == 0:
+                assert got == 0 and np.signbit(got) == (sign * np.sign(float(gl)) < 0)
+                continue
+            assert got.view(np.uint32) == ref.view(np.uint32), (row, col)
+            p = np.float32(F.E2M1[c13[row, col]]) * (np.float32(F.E4M3[s13[row, col // 16]]) * gl)
+            differ += int(p.view(np.uint32) != ref.view(np.uint32))
+    assert differ > 0  # the multiply order is really exercised
+    for r in range(0, H, 97):
+        for col in range(I):
+            sign, x = exact(int(c2[r, col]), int(s2[r, col // 16]), g[2])
+            if x != 0:
+                assert wd[r, col].view(np.uint32) == _round_f32(sign * x).view(np.uint32)

@@ -250,3 +250,23 @@ def test_static_placement_miss_rate_is_membership():
         assert sorted(e for e, _ in p.hits) == sorted(e for e in ids[0] if l * 16 + e in keys)
         assert p.q_fill == 0 and not p.fills and not p.evicted
     assert sorted(k for k in r.snapshot()[0] if k >= 0) == sorted(int(k) for k in keys)
+
+
+def test_set_bandwidth_clamps_the_credit_hand_worked():
+    """Re-setting B_P / B_H between calls keeps the cache and clock and clips
+    the credit below the new B_H (the split remainder can never reach B_H)."""
+    r = Residency(capacity=100, layers=100, experts=1, bp_mbps=9, bh_mbps=10)
+    p = r.lookup_plan(0, [[0]])        # q = floor((0 + 9) / 10) = 0, credit 9
+    assert (p.q, p.credit) == (0, 9) and p.host == [0]
+    r.set_bandwidth(1, 4)              # credit min(9, 4 - 1) = 3
+    assert r.credit == 3 and r.clock == 1
+    p = r.lookup_plan(1, [[0]])        # q = floor((3 + 1) / 4) = 1, credit 3 + 1 - 4 = 0
+    assert (p.q, p.q_fill, p.credit) == (1, 1, 0)
+    p = r.lookup_plan(2, [[0]])        # q = floor((0 + 1) / 4) = 0, credit 1
+    assert (p.q, p.credit) == (0, 1)
+    # without the clip the credit would have stayed 9: q = 1 with credit 3 at
+    # the second call and q = 1 again at the third
+    r.set_bandwidth(1, 1000)           # a larger B_H leaves the credit as it is
+    assert r.credit == 1
+    assert r.snapshot()[2] == 3        # clock unchanged by the re-split
+    assert r.resident() == {1 * 1 + 0: 0}  # the one filled key (layer 1) kept in slot 0

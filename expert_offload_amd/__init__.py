@@ -82,6 +82,7 @@ _SIGS = {
     "eo_cache_snapshot": [_P, _P, _P, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
     "eo_last_plan": [_P, ctypes.POINTER(eo_plan_host)],
     "eo_dequant": [_P, _I32, _I32, _P],
+    "eo_dequant_with": [_P, _I32, _I32, _I32, _P],
     "eo_stats_get": [_P, ctypes.POINTER(eo_stats)],
     "eo_resize_cache": [_P, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
     "eo_set_static_placement": [_P, _P, _I32],
@@ -250,6 +251,13 @@ def eo_last_plan(e) -> dict:
 
 def eo_dequant(e, layer, expert, out_host) -> None:
     _check(lib().eo_dequant(e, layer, expert, _ptr(out_host)))
+
+
+EO_DECODER_SCALAR, EO_DECODER_GEMM, EO_DECODER_GEMV = 0, 1, 2
+
+
+def eo_dequant_with(e, layer, expert, decoder, out_host) -> None:
+    _check(lib().eo_dequant_with(e, layer, expert, decoder, _ptr(out_host)))
 
 
 def eo_resize_cache(e, slots: int):

@@ -1280,9 +1280,12 @@ eo_status eo_last_plan(eo_engine* e, eo_plan_host* out) {
     return EO_OK;
 }
 
-eo_status eo_dequant(eo_engine* e, int32_t layer, int32_t expert, float* out_host) {
+static eo_status dequant_impl(eo_engine* e, int32_t layer, int32_t expert, int32_t decoder,
+                              float* out_host) {
     EOCHK(check_layer(e, layer));
     if (expert < 0 || expert >= e->E || !out_host) return fail(EO_ERR_INVALID_ARG, "bad expert");
+    if (decoder < EO_DECODER_SCALAR || decoder > EO_DECODER_GEMV)
+        return fail(EO_ERR_INVALID_ARG, "unknown decoder");
     HIPCHK(hipSetDevice(e->cfg.device));
     uint8_t* blk = nullptr;
     float* out = nullptr;
@@ -1294,12 +1297,24 @@ eo_status eo_dequant(eo_engine* e, int32_t layer, int32_t expert, float* out_hos
         return st;
     }
     hipError_t he = hipMemcpy(blk, e->pool[layer] + (uint64_t)expert * e->S_pad, e->S, hipMemcpyHostToDevice);
-    if (he == hipSuccess) he = launch_dequant(e->fmt, e->lay, blk, e->H, e->I, out, nullptr);
+    if (he == hipSuccess)
+        he = decoder == EO_DECODER_SCALAR
+                 ? launch_dequant(e->fmt, e->lay, blk, e->H, e->I, out, nullptr)
+                 : launch_dequant_dec(decoder, e->fmt, e->lay, blk, e->H, e->I, out, nullptr);
     if (he == hipSuccess) he = hipMemcpy(out_host, out, sizeof(float) * n, hipMemcpyDeviceToHost);
     (void)hipFree(blk);
     (void)hipFree(out);
     if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("dequant: ") + hipGetErrorString(he));
     return EO_OK;
+}
+
+eo_status eo_dequant(eo_engine* e, int32_t layer, int32_t expert, float* out_host) {
+    return dequant_impl(e, layer, expert, EO_DECODER_SCALAR, out_host);
+}
+
+eo_status eo_dequant_with(eo_engine* e, int32_t layer, int32_t expert, int32_t decoder,
+                          float* out_host) {
+    return dequant_impl(e, layer, expert, decoder, out_host);
 }
 
 eo_status eo_stats_get(eo_engine* e, eo_stats* out) {

@@ -168,6 +168,10 @@ hipError_t launch_rmsnorm(const void* r, void* u, int T, int H, int act_bf16, hi
 // Debug dequant of one expert block to fp32 (device decoder).
 hipError_t launch_dequant(int fmt, const Layout& lay, const uint8_t* blk, int H, int I, float* out,
                           hipStream_t s);
+// The same through the decoders of the grouped GEMM (dec 1) or the decode GEMV
+// (dec 2), with the factors each applies outside its decode.
+hipError_t launch_dequant_dec(int dec, int fmt, const Layout& lay, const uint8_t* blk, int H,
+                              int I, float* out, hipStream_t s);
 
 constexpr int kTileM = 128;  // grouped GEMM tile rows
 

@@ -30,6 +30,7 @@
 
 #include <cstdlib>
 
+#include "decode_dev.h"
 #include "dev_common.h"
 #include "eo_internal.h"
 
@@ -85,30 +86,6 @@ __device__ __forceinline__ const uint8_t* group_base(const GroupW& gw, int g, in
     if (gw.gbase) return gw.gbase[g];
     int s = gw.e2slot ? gw.e2slot[g] : g;
     return gw.slots + (uint64_t)s * gw.stride;
-}
-
-// Four e4m3fn codes (one word, first code in the low byte) as two bf16 pairs:
-// the scaled convert at scale 1, exact (an e4m3 value has at most 4 significant
-// bits).
-__device__ __forceinline__ void fp8x4_bf16(uint32_t w, uint32_t& lo, uint32_t& hi) {
-    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
-    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
-}
-
-// Two fp4 codes (byte B of w, even element in the low nibble) as a bf16 pair,
-// times sc. The scaled convert applies only the power of two of its scale
-// operand, so it takes MXFP4's e8m0 scales whole; for an NVFP4 e4m3 scale the
-// pair is converted to fp32, multiplied there and packed to bf16 (round to
-// nearest even, which changes nothing here). Either way the product is exact in
-// bf16: an e2m1 value has at most 2 significant bits, an e4m3 scale at most 4.
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-template <int FMT, int B>
-__device__ __forceinline__ uint32_t fp4x2_bf16(uint32_t w, float sc) {
-    if (FMT == EO_W_MXFP4)
-        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, B));
-    const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B) * sc;
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Decode 32 fp4 codes (16 bytes) with per-16 multipliers sc0 (elements 0..15)

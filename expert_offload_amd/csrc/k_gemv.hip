@@ -14,6 +14,7 @@
 
 #include <cstdlib>
 
+#include "decode_dev.h"
 #include "dev_common.h"
 #include "eo_internal.h"
 
@@ -276,8 +277,8 @@ __device__ __forceinline__ float dot8(uint4 w, uint4 x, float acc) {
 // 8 fp4 codes of one 32-bit word (two per byte, low nibble first) times x.
 template <int B>
 __device__ __forceinline__ float fp4_byte(uint32_t w, float sc, uint32_t xw, float acc) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, B),
-                                           as_bf2(xw), acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(as_bf2(fp4x2_bf16_pow2<B>(w, sc)), as_bf2(xw), acc,
+                                           false);
 }
 __device__ __forceinline__ float fp4_word(uint32_t w, float sc, uint4 x, float acc) {
     acc = fp4_byte<0>(w, sc, x.x, acc);
@@ -285,10 +286,6 @@ __device__ __forceinline__ float fp4_word(uint32_t w, float sc, uint4 x, float a
     acc = fp4_byte<2>(w, sc, x.z, acc);
     acc = fp4_byte<3>(w, sc, x.w, acc);
     return acc;
-}
-
-__device__ __forceinline__ uint32_t e4m3x2_bf16(uint32_t two) {
-    return bf_hi(e4m3_f32(two & 0xFF)) | (bf_hi(e4m3_f32((two >> 8) & 0xFF)) << 16);
 }
 
 template <int FMT> struct FastC;  // bf16 x elements per chunk, x uint4 per chunk

@@ -149,16 +149,24 @@ eo_status eo_set_bandwidth(eo_engine* e, uint32_t bp_mbps, uint32_t bh_mbps);
 
 /* ---- step calls (stream-ordered; x, ids, w, y are device pointers) ---- */
 
-/* Router: z = x . R_l^T in fp32 (64 strided fused multiply-add chains, then an
- * xor butterfly), top-k by (z desc, id asc), w = softmax over the k selected.
+/* Route, the first stage of a layer (explainer on papers.ananclaw.com, section
+ * 4, engineering path: softmax top-k routing, the expert count and the shared
+ * expert are the axes on which MoE architectures differ; zhichai.net article,
+ * section 2, LRU paragraph: which experts a token routes to is what the cache
+ * sees). Router: z = x . R_l^T in fp32 (64 strided fused multiply-add chains,
+ * then an xor butterfly), top-k by (z desc, id asc), w = softmax over the k
+ * selected.
  * forced_ids (device [T,k] or NULL): take these ids in this order (routing
  * trace replay) and return the softmax of z at them. ids: int32 [T,k];
  * w: fp32 [T,k]. */
 eo_status eo_route(eo_engine* e, int32_t layer, const void* x, int32_t T,
                    const int32_t* forced_ids, int32_t* ids, float* w, void* stream);
 
-/* Cache lookup, LRU update and miss plan for the distinct experts in ids
- * [T,k] (one LRU clock tick). Runs on the device; the plan is kept by the
+/* Look up the cache and plan the misses (zhichai.net article, section 2:
+ * Decode paragraph, most routed experts hit the device LRU cache and the m
+ * misses are split q* = m*B_P/B_H to PCIe, the rest to the host cores; LRU
+ * paragraph, one global LRU over all layers). Cache lookup, LRU update and miss
+ * plan for the distinct experts in ids [T,k] (one LRU clock tick). Runs on the device; the plan is kept by the
  * engine for eo_fill / eo_host_execute / eo_expert_ffn_combine and returned by
  * eo_last_plan. Split: q = min(m, floor((c + m*B_P)/B_H)),
  * c <- min(c + m*B_P - q*B_H, B_H - 1), q_fill = min(q, C - hits); misses
@@ -178,26 +186,43 @@ eo_status eo_lookup_plan(eo_engine* e, int32_t layer, const int32_t* ids, int32_
  * host reads the plan. */
 eo_status eo_fill(eo_engine* e, void* stream);
 
-/* Run the last plan's host-list experts on the host cores for the tokens
- * routed to them (x, ids, w as passed to the lookup: x device [T,H]) and stage
- * their weighted sum for the next eo_expert_ffn_combine. Waits on the host for
- * the plan and blocks while the host routine runs. */
+/* Host-execute (zhichai.net article, section 2, Decode paragraph: the misses
+ * not filled run in place on the host cores, reading their weights from host
+ * memory at B_H). Run the last plan's host-list experts on the host cores for
+ * the tokens routed to them (x device [T,H], ids [T,k], w [T,k] as passed to
+ * the lookup; copied to the host after a wait on `stream` unless the engine
+ * already mirrored them) and stage their weighted sum for the next
+ * eo_expert_ffn_combine. Waits on the host for the plan and blocks while the
+ * host routine runs. EO_ERR_STATE without a pending plan. */
 eo_status eo_host_execute(eo_engine* e, const void* x, const int32_t* ids, const float* w,
                           void* stream);
 
-/* Device part of the layer for the last plan: permute tokens by expert,
+/* Grouped expert FFN and combine (zhichai.net article, section 2, Decode
+ * paragraph: hits and filled experts are served from device memory; Prefill
+ * paragraph: expert compute of a layer on the device). Device part of the
+ * layer for the last plan: permute tokens by expert,
  * grouped SwiGLU FFN on the resident experts (decode: dequant-GEMV), the
  * shared expert, and the weighted combine plus any staged host results:
  * y fp32 [T,H] = sum_j w[t,j] * FFN_{e_j}(x_t) + FFN_shared(x_t).
- * No residual. Consumes the plan. */
+ * No residual. Consumes the plan. x [T,H] and y device, 16-byte aligned; ids
+ * and w as passed to the lookup. EO_ERR_STATE without a pending plan or when
+ * `layer` is not the plan's. */
 eo_status eo_expert_ffn_combine(eo_engine* e, int32_t layer, const void* x, const int32_t* ids,
                                 const float* w, float* y, void* stream);
 
-/* All of the above for one layer: y fp32 [T,H] (no residual). */
+/* One MoE layer in the method's order, route -> look up -> plan -> fill or
+ * host-execute -> grouped FFN -> combine (zhichai.net article, section 2,
+ * Decode paragraph): all of the above for one layer, y fp32 [T,H] (no
+ * residual). x device [T,H] in the activation dtype, 16-byte aligned;
+ * forced_ids device [T,k] or NULL as for eo_route. */
 eo_status eo_moe_layer(eo_engine* e, int32_t layer, const void* x, float* y, int32_t T,
                        const int32_t* forced_ids, void* stream);
 
-/* One decode step through all layers, in place. x_inout [T,H] (activation
+/* Decode (zhichai.net article, section 2, Decode paragraph: per token, each
+ * layer's routed experts are served from the LRU cache, and its misses are
+ * filled or run on the host by the q* split; LRU paragraph: consecutive tokens
+ * reuse experts, which is what the cache keeps). One decode step through all
+ * layers, in place. x_inout [T,H] (activation
  * dtype) is the residual stream r: layer l takes u_l = r_l / sqrt(mean(r_l^2)
  * + 1e-6) per token (stored in the activation dtype; a parameter-free RMS
  * normalisation, as in pre-norm transformer blocks) and r_{l+1} = r_l + y_l(u_l)
@@ -267,6 +292,19 @@ eo_status eo_last_plan(eo_engine* e, eo_plan_host* out);
 /* Dequantise one pool expert with the device decoder: out_host fp32
  * [W_gate (I*H) | W_up (I*H) | W_down (H*I)]. Synchronous. */
 eo_status eo_dequant(eo_engine* e, int32_t layer, int32_t expert, float* out_host);
+/* The same expert decoded through the weight decoders of one family of expert
+ * kernels, element by element, each value multiplied by the factors that family
+ * applies outside its decode (row scale, NVFP4 global scale) in the same order:
+ * EO_DECODER_GEMM the grouped GEMM's tile decode (scaled converts),
+ * EO_DECODER_GEMV the decode GEMV's, EO_DECODER_SCALAR the scalar decoders of
+ * eo_dequant. Formats as eo_wfmt (juejin.cn overview, section 5); values as
+ * defined there. Synchronous; out_host as for eo_dequant; INVALID_ARG for an
+ * unknown decoder. */
+#define EO_DECODER_SCALAR 0
+#define EO_DECODER_GEMM 1
+#define EO_DECODER_GEMV 2
+eo_status eo_dequant_with(eo_engine* e, int32_t layer, int32_t expert, int32_t decoder,
+                          float* out_host);
 eo_status eo_stats_get(eo_engine* e, eo_stats* out);
 /* Device time of the expert FFN and fill kernels since the last reset, from HIP
  * start/stop events attached to each kernel launch on the compute stream while

@@ -71,6 +71,7 @@ _SIGS = {
     "eo_remeasure_bandwidth": [_P, ctypes.POINTER(_U32), ctypes.POINTER(_U32)],
     "eo_set_bandwidth": [_P, _U32, _U32],
     "eo_route": [_P, _I32, _P, _I32, _P, _P, _P, _P],
+    "eo_route_noalloc": [_P, _I32, _P, _I32, _P, _P, _P, _P],
     "eo_lookup_plan": [_P, _I32, _P, _I32, _P],
     "eo_fill": [_P, _P],
     "eo_host_execute": [_P, _P, _P, _P, _P],
@@ -193,6 +194,11 @@ def eo_set_bandwidth(e: int, bp_mbps: int, bh_mbps: int) -> None:
 def eo_route(e, layer, x, T, forced_ids, ids, w, stream=None) -> None:
     _check(lib().eo_route(e, layer, _ptr(x), T, _ptr(forced_ids), _ptr(ids), _ptr(w),
                           _stream(stream)))
+
+
+def eo_route_noalloc(e, layer, x, T, forced_ids, ids, w, stream=None) -> None:
+    _check(lib().eo_route_noalloc(e, layer, _ptr(x), T, _ptr(forced_ids), _ptr(ids), _ptr(w),
+                                  _stream(stream)))
 
 
 def eo_lookup_plan(e, layer, ids, T, stream=None) -> None:

@@ -125,6 +125,8 @@ struct eo_engine {
 
     eo_stats stats{};
 
+    uint8_t* scratch = nullptr;  // this device's copy of the file-scope scratch array
+
     bool timing = false;
     int gemv_fast = 1;  // EO_GEMV_FAST=0 selects the generic decode GEMV kernels
     std::vector<TimedSet> gemv_ev, gemm_ev, fill_ev, free_ev;
@@ -138,7 +140,34 @@ struct eo_engine {
     int cap_T = 0;
 };
 
+// Device scratch of the allocation-free entry point (eo_route_noalloc): one
+// copy per GPU, held until the process ends. Host code never passes the
+// array's name to a kernel or a copy (on the host it is a stand-in, not a
+// device address); it uses the per-device address taken once below.
+constexpr size_t kScratchBytes = 16u << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's address on `device` (which must be current), looked up
+// once per device.
+eo_status scratch_on_device(int device, uint8_t** out) {
+    if (device < 0 || device >= kMaxDevices) return fail(EO_ERR_UNSUPPORTED, "device ordinal above 63");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void* p = nullptr;
+        hipError_t he = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (he != hipSuccess || !p)
+            return fail(EO_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(he));
+        g_scratch_ptr[device] = (uint8_t*)p;
+    }
+    *out = g_scratch_ptr[device];
+    return EO_OK;
+}
 
 eo_status get_set(eo_engine* e, TimedSet* p) {
     if (!e->free_ev.empty()) {
@@ -679,6 +708,7 @@ eo_status create_impl(const eo_config* cfg, eo_engine* e) {
     if (const char* v = std::getenv("EO_FILL_SDMA")) e->fill_sdma = std::atoi(v) != 0;
     if (const char* v = std::getenv("EO_FUSED_ENTRY")) e->fused_entry = std::atoi(v) != 0;
     e->bp = e->bh = 1;
+    EOCHK(scratch_on_device(cfg->device, &e->scratch));
     EOCHK(reset_cache(e));
     HIPCHK(hipDeviceSynchronize());
     return EO_OK;
@@ -902,6 +932,28 @@ eo_status eo_route(eo_engine* e, int32_t layer, const void* x, int32_t T, const 
     const size_t roff = (size_t)layer * e->E * e->H;
     hipError_t he = launch_route(x, e->act_bf16, e->d_router + roff, e->d_router_t + roff, T, e->E,
                                  e->H, e->k, forced_ids, ids, w, e->d_z, e->d_xt,
+                                 (hipStream_t)stream);
+    if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("route: ") + hipGetErrorString(he));
+    return EO_OK;
+}
+
+eo_status eo_route_noalloc(eo_engine* e, int32_t layer, const void* x, int32_t T,
+                           const int32_t* forced_ids, int32_t* ids, float* w, void* stream) {
+    EOCHK(check_layer(e, layer));
+    EOCHK(check_T(e, T));
+    if (!x || !ids || !w) return fail(EO_ERR_INVALID_ARG, "null pointer");
+    if (!e->scratch) return fail(EO_ERR_STATE, "no scratch address on this engine's device");
+    // logits [T, E] fp32 at the start, then (chain-interleaved kernel) x as
+    // [T][H/512][64][8] bf16 at the next 256-byte boundary
+    const bool chains = route_chains_ok(T, e->E, e->H, e->act_bf16);
+    const uint64_t z_bytes = round_up((uint64_t)T * e->E * 4, 256);
+    const uint64_t need = z_bytes + (chains ? (uint64_t)T * e->H * 2 : 0);
+    if (need > kScratchBytes)
+        return fail(EO_ERR_INVALID_ARG, "T * (4 E + 2 H) bytes exceed the 16 MiB scratch of eo_route_noalloc");
+    const size_t roff = (size_t)layer * e->E * e->H;
+    hipError_t he = launch_route(x, e->act_bf16, e->d_router + roff, e->d_router_t + roff, T, e->E,
+                                 e->H, e->k, forced_ids, ids, w, (float*)e->scratch,
+                                 chains ? (uint16_t*)(e->scratch + z_bytes) : nullptr,
                                  (hipStream_t)stream);
     if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("route: ") + hipGetErrorString(he));
     return EO_OK;

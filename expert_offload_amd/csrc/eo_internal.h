@@ -47,6 +47,10 @@ hipError_t launch_route(const void* x, int act_bf16, const float* R, const float
                         int E, int H, int k, const int32_t* forced, int32_t* ids, float* w,
                         float* z_scratch, uint16_t* xT, hipStream_t s);
 
+// True when launch_route takes the chain-interleaved kernel (then it needs Rt
+// and the xT scratch of T * H bf16).
+bool route_chains_ok(int T, int E, int H, int act_bf16);
+
 // Layer entry of one token in the stacked decode step (bf16 activations):
 // r_out = bf16(r_in + sum_j parts[j] + y_host) (r_in copied when there are no
 // parts), u = bf16(r_out / sqrt(mean(r_out^2) + 1e-6)), z[e] = router logit of

@@ -162,6 +162,20 @@ eo_status eo_set_bandwidth(eo_engine* e, uint32_t bp_mbps, uint32_t bh_mbps);
 eo_status eo_route(eo_engine* e, int32_t layer, const void* x, int32_t T,
                    const int32_t* forced_ids, int32_t* ids, float* w, void* stream);
 
+/* eo_route without any device allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, results and errors as eo_route; its
+ * kernels keep their scratch (logits [T,E] fp32 and, for the chain-interleaved
+ * kernel, x rearranged as [T,H] bf16) in a fixed 16 MiB device array per GPU,
+ * held until the process ends, instead of the engine's buffers. The call
+ * allocates nothing and launches kernels only. EO_ERR_INVALID_ARG when
+ * T * 4 * E (+ T * 2 * H when H % 512 == 0, E % 32 == 0, T >= 32 and
+ * activations are bf16) exceeds 16 MiB. Calls that overlap on one GPU (other
+ * streams, other engines on the same device) share the array and race: order
+ * them on one stream. */
+eo_status eo_route_noalloc(eo_engine* e, int32_t layer, const void* x, int32_t T,
+                           const int32_t* forced_ids, int32_t* ids, float* w, void* stream);
+
 /* Look up the cache and plan the misses (zhichai.net article, section 2:
  * Decode paragraph, most routed experts hit the device LRU cache and the m
  * misses are split q* = m*B_P/B_H to PCIe, the rest to the host cores; LRU

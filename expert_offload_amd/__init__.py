@@ -90,6 +90,8 @@ _SIGS = {
     "eo_clear_static_placement": [_P],
     "eo_kernel_times": [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64), _I32],
     "eo_set_timing": [_P, _I32],
+    "eo_set_plan_log": [_P, _I32],
+    "eo_get_plan_log": [_P, _P, _I64, ctypes.POINTER(_I64)],
     "eo_expert_bytes": [_I32, _I32, _I32],
     "eo_sync": [_P],
     "eo_last_error": [],
@@ -288,6 +290,21 @@ def eo_stats_get(e) -> dict:
     s = eo_stats()
     _check(lib().eo_stats_get(e, ctypes.byref(s)))
     return {n: getattr(s, n) for n, _ in eo_stats._fields_}
+
+
+def eo_set_plan_log(e, enable: bool) -> None:
+    _check(lib().eo_set_plan_log(e, 1 if enable else 0))
+
+
+def eo_get_plan_log(e):
+    """int32 numpy array [n, 4]: {layer, hits, fills, host experts} per lookup."""
+    import numpy as np
+    n = _I64(0)
+    _check(lib().eo_get_plan_log(e, None, 0, ctypes.byref(n)))
+    out = np.zeros((n.value, 4), dtype=np.int32)
+    if n.value:
+        _check(lib().eo_get_plan_log(e, out.ctypes.data, n.value, ctypes.byref(n)))
+    return out
 
 
 def eo_set_timing(e, enable: bool) -> None:

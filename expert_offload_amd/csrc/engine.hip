@@ -127,6 +127,9 @@ struct eo_engine {
 
     uint8_t* scratch = nullptr;  // this device's copy of the file-scope scratch array
 
+    bool plan_log_on = false;
+    std::vector<int32_t> plan_log;  // {layer, hits, fills, host experts} per lookup
+
     bool timing = false;
     int gemv_fast = 1;  // EO_GEMV_FAST=0 selects the generic decode GEMV kernels
     std::vector<TimedSet> gemv_ev, gemm_ev, fill_ev, free_ev;
@@ -294,6 +297,7 @@ eo_status wait_plan(eo_engine* e) {
     e->stats.misses += p.m;
     e->stats.fills += p.q_fill;
     e->stats.pcie_bytes += (int64_t)p.q_fill * (int64_t)e->S;
+    if (e->plan_log_on) e->plan_log.insert(e->plan_log.end(), {p.layer, p.n_hit, p.q_fill, p.n_host});
     e->plan_ready = true;
     return EO_OK;
 }
@@ -650,7 +654,13 @@ eo_status create_impl(const eo_config* cfg, eo_engine* e) {
     e->pool.assign(e->L, nullptr);
     e->pool_dev.assign(e->L, nullptr);
     for (int l = 0; l < e->L; ++l) {
-        EOCHK(hmalloc(&e->pool[l], e->E * e->S_pad, hipHostMallocDefault));
+        if (hmalloc(&e->pool[l], e->E * e->S_pad, hipHostMallocDefault) != EO_OK)
+            return fail(EO_ERR_OOM, g_err + " (pool layer " + std::to_string(l) + " of " +
+                                        std::to_string(e->L) + ", " +
+                                        std::to_string((double)l * e->E * e->S_pad / 1e9) +
+                                        " GB already pinned, " +
+                                        std::to_string((double)e->E * e->S_pad / 1e9) +
+                                        " GB per layer)");
         HIPCHK(hipHostGetDevicePointer((void**)&e->pool_dev[l], e->pool[l], 0));
     }
     EOCHK(dmalloc(&e->d_slots, e->C * e->S_pad));
@@ -1372,6 +1382,23 @@ eo_status eo_dequant_with(eo_engine* e, int32_t layer, int32_t expert, int32_t d
 eo_status eo_stats_get(eo_engine* e, eo_stats* out) {
     if (!e || !out) return fail(EO_ERR_INVALID_ARG, "null argument");
     *out = e->stats;
+    return EO_OK;
+}
+
+eo_status eo_set_plan_log(eo_engine* e, int32_t enable) {
+    if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
+    e->plan_log_on = enable != 0;
+    if (e->plan_log_on) e->plan_log.clear();
+    return EO_OK;
+}
+
+eo_status eo_get_plan_log(eo_engine* e, int32_t* out, int64_t cap, int64_t* n) {
+    if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
+    if (cap < 0 || (cap > 0 && !out)) return fail(EO_ERR_INVALID_ARG, "out must hold cap entries");
+    const int64_t have = (int64_t)e->plan_log.size() / 4;
+    if (out && cap > 0)
+        std::memcpy(out, e->plan_log.data(), sizeof(int32_t) * 4 * std::min(have, cap));
+    if (n) *n = have;
     return EO_OK;
 }
 

@@ -331,6 +331,16 @@ eo_status eo_stats_get(eo_engine* e, eo_stats* out);
  * be NULL; reset != 0 clears after reading. Synchronises on the events. */
 eo_status eo_kernel_times(eo_engine* e, double* ms /*[5]*/, int64_t* launches /*[3]*/,
                           int32_t reset);
+/* Plan sizes of each lookup, recorded on the host when it reads the plan
+ * (zhichai.net article, section 2, Decode paragraph: per layer call, hits are
+ * served from the device, q* misses filled over PCIe, the rest run on the host;
+ * the three lanes bound the call). eo_set_plan_log(e, 1) clears the log and
+ * starts recording, 0 stops. eo_get_plan_log copies the first min(n, cap)
+ * entries, each int32 {layer, hits, fills, host experts} in call order, to out
+ * (host [cap][4]; NULL with cap 0 only counts) and stores the number recorded
+ * in *n (may be NULL). */
+eo_status eo_set_plan_log(eo_engine* e, int32_t enable);
+eo_status eo_get_plan_log(eo_engine* e, int32_t* out, int64_t cap, int64_t* n);
 /* Enable (1) or disable (0) the per-launch timing events behind eo_kernel_times. */
 eo_status eo_set_timing(eo_engine* e, int32_t enable);
 /* Size in bytes of one packed expert block (unpadded). */

@@ -130,6 +130,7 @@ struct eo_engine {
     bool plan_log_on = false;
     std::vector<int32_t> plan_log;  // {layer, hits, fills, host experts} per lookup
 
+    bool debug_sync = false;  // EO_DEBUG_SYNC=1: wait for the device after every stage
     bool timing = false;
     int gemv_fast = 1;  // EO_GEMV_FAST=0 selects the generic decode GEMV kernels
     std::vector<TimedSet> gemv_ev, gemm_ev, fill_ev, free_ev;
@@ -224,6 +225,19 @@ eo_status check_T(eo_engine* e, int T) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Debug mode (EO_DEBUG_SYNC=1 at engine creation): after each stage, wait for
+// the stream and report an asynchronous device error with the stage's name.
+// The kernels and their order are the same, so the results are too.
+eo_status stage_done(eo_engine* e, hipStream_t s, const char* stage, int layer) {
+    if (!e->debug_sync) return EO_OK;
+    hipError_t he = hipStreamSynchronize(s);
+    if (he == hipSuccess) he = hipGetLastError();
+    if (he != hipSuccess)
+        return fail(EO_ERR_HIP, std::string(stage) + " (layer " + std::to_string(layer) + "): " +
+                                    hipGetErrorString(he));
+    return EO_OK;
+}
 
 // Grow the grouped-FFN buffers to hold T tokens.
 eo_status ensure_gemm(eo_engine* e, int T, hipStream_t s) {
@@ -494,11 +508,17 @@ eo_status moe_layer_impl(eo_engine* e, int layer, const void* x, float* y, int T
     hipError_t he = launch_route(x, e->act_bf16, e->d_router + roff, e->d_router_t + roff, T,
                                  e->E, e->H, e->k, forced, ids, w, e->d_z, e->d_xt, s);
     if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("route: ") + hipGetErrorString(he));
+    EOCHK(stage_done(e, s, "route", layer));
     EOCHK(do_plan(e, layer, ids, w, x, T, s));
+    EOCHK(stage_done(e, s, "lookup and plan", layer));
     EOCHK(do_fill(e, s));
+    EOCHK(stage_done(e, s, "fill", layer));
     EOCHK(do_ffn_device(e, layer, x, ids, w, s));
+    EOCHK(stage_done(e, s, "expert FFN", layer));
     EOCHK(do_host(e, x, ids, w, s));
-    return do_combine(e, ids, y, x_res, s);
+    EOCHK(stage_done(e, s, "host-execute", layer));
+    EOCHK(do_combine(e, ids, y, x_res, s));
+    return stage_done(e, s, "combine", layer);
 }
 
 // One token through all layers with the fused layer entry: per layer, one
@@ -544,12 +564,16 @@ eo_status decode_one_token(eo_engine* e, uint16_t* x_inout, const int32_t* force
                 return fail(EO_ERR_HIP, std::string("layer entry: ") + hipGetErrorString(he));
             EOCHK(do_plan(e, l, ids, w, e->d_u, 1, s, rt));
         }
+        EOCHK(stage_done(e, s, "layer entry and plan", l));
         if (cap)  // u is not changed by the plan
             HIPCHK(hipMemcpyAsync((uint8_t*)e->cap_x + (size_t)l * e->cap_T * H * 2, e->d_u,
                                   (size_t)H * 2, hipMemcpyDeviceToDevice, s));
         EOCHK(do_fill(e, s));
+        EOCHK(stage_done(e, s, "fill", l));
         EOCHK(do_ffn_device(e, l, e->d_u, ids, w, s));
+        EOCHK(stage_done(e, s, "expert GEMV", l));
         EOCHK(do_host(e, e->d_u, ids, w, s));
+        EOCHK(stage_done(e, s, "host-execute", l));
         prev_host = e->host_staged ? e->h_yhost_dev : nullptr;
         // the plan is consumed here; its outputs are summed by the next entry
         e->plan_pending = false;
@@ -560,7 +584,7 @@ eo_status decode_one_token(eo_engine* e, uint16_t* x_inout, const int32_t* force
     hipError_t he = launch_gemv_reduce(e->d_yparts, nparts, prev_host, H, y_last, x_inout, 1, s,
                                        e->d_r + (size_t)((e->L - 1) & 1) * H);
     if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("combine: ") + hipGetErrorString(he));
-    return EO_OK;
+    return stage_done(e, s, "final combine", e->L - 1);
 }
 
 eo_status reset_cache(eo_engine* e) {
@@ -717,6 +741,7 @@ eo_status create_impl(const eo_config* cfg, eo_engine* e) {
     if (const char* v = std::getenv("EO_GEMV_FAST")) e->gemv_fast = std::atoi(v) != 0;
     if (const char* v = std::getenv("EO_FILL_SDMA")) e->fill_sdma = std::atoi(v) != 0;
     if (const char* v = std::getenv("EO_FUSED_ENTRY")) e->fused_entry = std::atoi(v) != 0;
+    if (const char* v = std::getenv("EO_DEBUG_SYNC")) e->debug_sync = std::atoi(v) != 0;
     e->bp = e->bh = 1;
     EOCHK(scratch_on_device(cfg->device, &e->scratch));
     EOCHK(reset_cache(e));
@@ -799,20 +824,12 @@ eo_status eo_set_router(eo_engine* e, int32_t layer, const float* host_w) {
     HIPCHK(hipSetDevice(e->cfg.device));
     HIPCHK(hipMemcpy(e->d_router + (size_t)layer * e->E * e->H, host_w,
                      sizeof(float) * e->E * e->H, hipMemcpyHostToDevice));
-    // chain-interleaved copy: Rq[e][j/4][i][j%4] = R[e][i + 64 j]. It needs the
-    // chain steps j < H/64 in whole groups of four (H % 256 == 0), or the index
-    // runs past the row; the chained router kernel reads it only when H % 512 == 0.
-    if (e->H % 256 == 0) {
-        const int J = e->H / 64;
-        std::vector<float> rt((size_t)e->E * e->H);
-        for (int x = 0; x < e->E; ++x)
-            for (int j = 0; j < J; ++j)
-                for (int i = 0; i < 64; ++i)
-                    rt[(size_t)x * e->H + ((size_t)(j / 4) * 64 + i) * 4 + (j % 4)] =
-                        host_w[(size_t)x * e->H + i + 64 * j];
+    // chain-interleaved copy for the many-token router kernel (which reads it only
+    // when H % 512 == 0); shapes its layout does not cover are left zero
+    std::vector<float> rt((size_t)e->E * e->H);
+    if (router_chain_layout(host_w, e->E, e->H, rt.data()))
         HIPCHK(hipMemcpy(e->d_router_t + (size_t)layer * e->E * e->H, rt.data(),
                          sizeof(float) * e->E * e->H, hipMemcpyHostToDevice));
-    }
     return EO_OK;
 }
 
@@ -1160,6 +1177,7 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t flags, void
             he = launch_combine(e->d_opairs, ids, nullptr, 1, e->shared, nullptr, T, e->k, e->H, y,
                                 x_inout, e->act_bf16, s, e->E);
         if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("prefill layer: ") + hipGetErrorString(he));
+        EOCHK(stage_done(e, s, "prefill layer (norm, route, permute, grouped FFN, combine)", l));
         HIPCHK(hipEventRecord(e->ev_comp[b], s));
         if (!double_buffer && l + 1 < e->L) {
             HIPCHK(hipStreamWaitEvent(e->copy_stream, e->ev_comp[b], 0));

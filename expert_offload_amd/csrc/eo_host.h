@@ -20,6 +20,13 @@ struct Layout {
 };
 Layout layout_of(int H, int I, int fmt);
 
+// Router weights R [E, H] fp32 rearranged per accumulation chain for the
+// many-token router kernel: out[e][j/4][i][j%4] = R[e][i + 64 j] (chain i takes
+// h = i, i + 64, ...), so a lane's 16-byte load holds four consecutive steps of
+// its chain. The layout takes the chains' H/64 steps in whole groups of four:
+// false (out untouched) unless H is a multiple of 256.
+bool router_chain_layout(const float* R, int E, int H, float* out);
+
 // Host-core expert routine: for every expert with a non-null `experts` entry,
 // y[t] += w[t,j] * FFN_e(x_t) over the pairs (t, j) routed to it, in fp32.
 class ThreadPool;

@@ -42,4 +42,16 @@ Layout layout_of(int H, int I, int fmt) {
     return l;
 }
 
+bool router_chain_layout(const float* R, int E, int H, float* out) {
+    if (E < 1 || H < 256 || H % 256 != 0) return false;
+    const int J = H / 64;  // steps of each of the 64 chains (h = i + 64 j)
+    for (int e = 0; e < E; ++e) {
+        const float* r = R + (size_t)e * H;
+        float* o = out + (size_t)e * H;
+        for (int j = 0; j < J; ++j)
+            for (int i = 0; i < 64; ++i) o[((size_t)(j / 4) * 64 + i) * 4 + (j % 4)] = r[i + 64 * j];
+    }
+    return true;
+}
+
 }  // namespace eo

@@ -24,6 +24,11 @@
  *   - Asynchronous device errors surface at the next call or at eo_sync() as
  *     EO_ERR_HIP.
  *   - An engine is used from one host thread at a time.
+ *   - Debugging: with EO_DEBUG_SYNC=1 in the environment at eo_create, the step
+ *     calls wait for the device after every stage (route, lookup and plan,
+ *     fill, expert FFN, host-execute, combine; per layer in eo_decode_step and
+ *     eo_prefill) and report an asynchronous device error as EO_ERR_HIP naming
+ *     the stage and layer. Results are the same as without it.
  * Tensor layouts are row-major. Activations are bf16 (act_bf16 = 1) or fp32.
  */
 #ifndef EO_H

@@ -3,6 +3,7 @@
 //   host_driver decode <fmt>    : the AVX512-BF16 route's weight decode of every code
 //                                 (FP8: bytes 0..255; fp4: the 256 byte values, two codes
 //                                 each), bf16 bit patterns as text, one per line
+//   host_driver chains <E> <H> : the router's chain-interleaved layout, checked entry by entry
 //   host_driver ffn <dir>       : read meta.txt, block.bin, x.bin, ids.bin, w.bin from <dir>,
 //                                 run host_ffn with every routed expert on the host,
 //                                 write y.bin (fp32 [T,H])
@@ -67,6 +68,30 @@ int main(int argc, char** argv) {
             if (!eo::host_decode_codes(fmt, codes + b, out)) return 3;
             for (int i = 0; i < 32; ++i) printf("%u\n", out[i]);
         }
+        return 0;
+    }
+    if (argc >= 4 && !strcmp(argv[1], "chains")) {
+        // the router's chain-interleaved layout for E experts of H: every entry
+        // checked against R[e][i + 64 j]; shapes it does not cover must be refused
+        // with the output untouched
+        const int E = atoi(argv[2]), H = atoi(argv[3]);
+        std::vector<float> R((size_t)E * H), out((size_t)E * H, -7.0f);
+        for (size_t i = 0; i < R.size(); ++i) R[i] = (float)i;
+        const bool ok = eo::router_chain_layout(R.data(), E, H, out.data());
+        if (H % 256 != 0) {
+            for (float v : out)
+                if (v != -7.0f) { printf("refused shape written to\n"); return 1; }
+            printf(ok ? "accepted\n" : "refused\n");
+            return ok ? 1 : 0;
+        }
+        if (!ok) { printf("refused\n"); return 1; }
+        for (int e = 0; e < E; ++e)
+            for (int j = 0; j < H / 64; ++j)
+                for (int i = 0; i < 64; ++i) {
+                    const float got = out[(size_t)e * H + ((size_t)(j / 4) * 64 + i) * 4 + (j % 4)];
+                    if (got != R[(size_t)e * H + i + 64 * j]) { printf("mismatch\n"); return 1; }
+                }
+        printf("ok\n");
         return 0;
     }
     if (argc >= 3 && !strcmp(argv[1], "ffn")) {

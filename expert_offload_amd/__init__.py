@@ -48,7 +48,8 @@ class eo_plan_host(ctypes.Structure):
 class eo_stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("lookups", "hits", "misses", "fills",
                                                "host_experts", "pcie_bytes", "host_bytes",
-                                               "prefill_layers")]
+                                               "prefill_layers", "device_expert_bytes",
+                                               "host_wait_ns", "host_routine_ns")]
 
 
 class EOError(RuntimeError):

@@ -131,6 +131,7 @@ struct eo_engine {
     std::vector<int32_t> plan_log;  // {layer, hits, fills, host experts} per lookup
 
     bool debug_sync = false;  // EO_DEBUG_SYNC=1: wait for the device after every stage
+    int log_level = 0;        // EO_LOG: 1 configuration, 2 + one line per plan
     bool timing = false;
     int gemv_fast = 1;  // EO_GEMV_FAST=0 selects the generic decode GEMV kernels
     std::vector<TimedSet> gemv_ev, gemm_ev, fill_ev, free_ev;
@@ -268,6 +269,14 @@ eo_status wait_plan(eo_engine* e) {
     if (!e->plan_pending) return fail(EO_ERR_STATE, "no pending plan (call eo_lookup_plan first)");
     if (e->plan_ready) return EO_OK;
     auto t0 = std::chrono::steady_clock::now();
+    struct WaitTimer {  // host time spent in this wait, on every way out
+        eo_engine* e;
+        std::chrono::steady_clock::time_point t0;
+        ~WaitTimer() {
+            e->stats.host_wait_ns += std::chrono::duration_cast<std::chrono::nanoseconds>(
+                                         std::chrono::steady_clock::now() - t0).count();
+        }
+    } wait_timer{e, t0};
     uint64_t spins = 0;
     while (__atomic_load_n(&e->h_plan->seq, __ATOMIC_ACQUIRE) != e->plan_seq) {
         _mm_pause();
@@ -311,6 +320,11 @@ eo_status wait_plan(eo_engine* e) {
     e->stats.misses += p.m;
     e->stats.fills += p.q_fill;
     e->stats.pcie_bytes += (int64_t)p.q_fill * (int64_t)e->S;
+    e->stats.device_expert_bytes += (int64_t)(p.n_hit + p.q_fill + e->shared) * (int64_t)e->S;
+    if (e->log_level >= 2)
+        std::fprintf(stderr, "eo: plan layer %d clock %lld: %d hits, %d misses, q %d, %d fills, %d host, %d evicted, credit %lld\n",
+                     p.layer, (long long)p.clock, p.n_hit, p.m, p.q, p.q_fill, p.n_host, p.n_evict,
+                     (long long)p.credit);
     if (e->plan_log_on) e->plan_log.insert(e->plan_log.end(), {p.layer, p.n_hit, p.q_fill, p.n_host});
     e->plan_ready = true;
     return EO_OK;
@@ -417,7 +431,10 @@ eo_status do_host(eo_engine* e, const void* x, const int32_t* ids, const float* 
     jb.w = hw;
     jb.experts = table.data();
     jb.y = e->h_yhost;
+    const auto th0 = std::chrono::steady_clock::now();
     host_ffn(e->tp, jb, e->host_scratch);
+    e->stats.host_routine_ns += std::chrono::duration_cast<std::chrono::nanoseconds>(
+                                    std::chrono::steady_clock::now() - th0).count();
     // one token: the combine reads the mapped host result directly
     if (T > 1)
         HIPCHK(hipMemcpyAsync(e->d_yhost, e->h_yhost, sizeof(float) * T * H, hipMemcpyHostToDevice, s));
@@ -742,6 +759,16 @@ eo_status create_impl(const eo_config* cfg, eo_engine* e) {
     if (const char* v = std::getenv("EO_FILL_SDMA")) e->fill_sdma = std::atoi(v) != 0;
     if (const char* v = std::getenv("EO_FUSED_ENTRY")) e->fused_entry = std::atoi(v) != 0;
     if (const char* v = std::getenv("EO_DEBUG_SYNC")) e->debug_sync = std::atoi(v) != 0;
+    if (const char* v = std::getenv("EO_LOG")) e->log_level = std::atoi(v);
+    if (e->log_level >= 1)
+        std::fprintf(stderr,
+                     "eo: engine on device %d: %d layers x %d experts (top-%d, H %d, I %d, format %d, "
+                     "shared %d), expert %llu bytes (%llu padded); pool %.2f GB pinned, cache %lld "
+                     "slots (%.2f GB), max tokens %d, host threads %d\n",
+                     cfg->device, e->L, e->E, e->k, e->H, e->I, e->fmt, e->shared,
+                     (unsigned long long)e->S, (unsigned long long)e->S_pad,
+                     (double)e->L * e->E * e->S_pad / 1e9, (long long)e->C,
+                     (double)e->C * e->S_pad / 1e9, cfg->max_tokens, threadpool_size(e->tp));
     e->bp = e->bh = 1;
     EOCHK(scratch_on_device(cfg->device, &e->scratch));
     EOCHK(reset_cache(e));
@@ -1186,6 +1213,7 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t flags, void
         }
     }
     e->stats.prefill_layers += e->L;
+    e->stats.device_expert_bytes += (int64_t)e->L * (e->E + e->shared) * (int64_t)e->S;
     e->stats.pcie_bytes += streamed;
     if (e->timing) EOCHK(harvest_times(e));
     return EO_OK;

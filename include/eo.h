@@ -103,6 +103,11 @@ typedef struct {
     int64_t pcie_bytes;  /* bytes copied host->device by fills and prefill streaming */
     int64_t host_bytes;  /* expert bytes read by the host-core routine */
     int64_t prefill_layers;
+    int64_t device_expert_bytes;  /* expert weight bytes the device FFN reads, once per expert
+                                     and layer call: (hits + fills + shared) * expert size for
+                                     lookups, the whole layer (+ shared) for prefill layers */
+    int64_t host_wait_ns;     /* host time spent waiting for device plans */
+    int64_t host_routine_ns;  /* host time spent in the host-core expert routine */
 } eo_stats;
 
 /* Create an engine on cfg->device: allocates the pinned host expert pool
@@ -324,6 +329,9 @@ eo_status eo_dequant(eo_engine* e, int32_t layer, int32_t expert, float* out_hos
 #define EO_DECODER_GEMV 2
 eo_status eo_dequant_with(eo_engine* e, int32_t layer, int32_t expert, int32_t decoder,
                           float* out_host);
+/* Counters since eo_create (host memory). With EO_LOG=1 in the environment at
+ * eo_create the engine prints its configuration and allocations to stderr;
+ * EO_LOG=2 also prints one line per lookup plan. */
 eo_status eo_stats_get(eo_engine* e, eo_stats* out);
 /* Device time of the expert FFN and fill kernels since the last reset, from HIP
  * start/stop events attached to each kernel launch on the compute stream while

@@ -158,3 +158,40 @@ def test_per_stage_calls_out_of_order():
         eo.eo_sync(e)
     finally:
         eo.eo_destroy(e)
+
+
+def test_plan_log_matches_the_oracle_plans():
+    """eo_set_plan_log / eo_get_plan_log over decode steps: one entry per layer
+    call, {layer, hits, fills, host experts}, equal to the oracle's plans."""
+    shape = _shape("bf16")
+    seed = 23
+    L, E, k, H = shape.layers, shape.experts, shape.top_k, shape.hidden
+    e = make_engine(shape, seed, max_tokens=1)
+    try:
+        eo.eo_set_bandwidth(e, 2, 5)
+        ref = Residency(shape.cache_slots, L, E, 2, 5)
+        trace = synth.sticky_zipf_trace(seed, 12, L, E, k)
+        eo.eo_set_plan_log(e, True)
+        for st in range(12):
+            x = dev(synth.activations(seed, 900 + st, 1, H, 1.0, True).view(np.int16))
+            eo.eo_decode_step(e, x, 1, dev(trace[st].reshape(L, 1, k)), _s())
+        torch.cuda.synchronize()
+        eo.eo_set_plan_log(e, False)
+        log = eo.eo_get_plan_log(e)
+        want = []
+        for st in range(12):
+            for l in range(L):
+                p = ref.lookup_plan(l, trace[st, l][None, :])
+                want.append([l, len(p.hits), len(p.fills), len(p.host)])
+        assert log.shape == (12 * L, 4)
+        assert np.array_equal(log, np.array(want, dtype=np.int32))
+        assert log[:, 2].sum() > 0 and log[:, 3].sum() > 0
+        # stopped: further calls are not logged; re-enabling clears
+        x = dev(synth.activations(seed, 999, 1, H, 1.0, True).view(np.int16))
+        eo.eo_decode_step(e, x, 1, dev(trace[0].reshape(L, 1, k)), _s())
+        torch.cuda.synchronize()
+        assert eo.eo_get_plan_log(e).shape == (12 * L, 4)
+        eo.eo_set_plan_log(e, True)
+        assert eo.eo_get_plan_log(e).shape == (0, 4)
+    finally:
+        eo.eo_destroy(e)

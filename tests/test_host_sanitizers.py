@@ -1,4 +1,5 @@
-"""Host code under AddressSanitizer and UndefinedBehaviorSanitizer (CPU only).
+"""Host code and the oracle's C under AddressSanitizer and UndefinedBehaviorSanitizer
+(CPU only).
 
 The host-side C++ of the library (the host-core expert routine, its thread
 pool, the expert-block layout and the router's chain-interleaved layout) is
@@ -8,7 +9,9 @@ layouts' block sizes: H in {256, 384, 512, 2048, 6144}, every weight format,
 both instruction routes. Any out-of-bounds access, use after free or
 undefined behaviour aborts the driver. The router layout at H = 384 is the
 shape whose index arithmetic once overran its buffer: it must be refused with
-the output untouched.
+the output untouched. The oracle's fixed-order router logits (its only C code)
+run under the same sanitizers at hidden sizes around the 64 chains, against
+exact integer dot products.
 """
 import os
 import shutil
@@ -93,3 +96,20 @@ def test_host_ffn_under_sanitizers(san_driver, tmp_path, H, fmt, isa):
     ref = OM.layer_output(xf, ids, w, lambda e: OF.dequant_expert(blocks[e], H, I, f))
     err = np.max(np.abs(y - ref)) / np.max(np.abs(ref))
     assert err <= (2e-2 if (isa == "native" and pair_route) else 1e-5), err
+
+
+@pytest.fixture(scope="module")
+def corder_driver(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("san") / "corder_driver_san")
+    subprocess.check_call(["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-ffp-contract=off",
+                           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                           os.path.join(ROOT, "tests", "cpp", "corder_driver.c"),
+                           os.path.join(ROOT, "oracle", "corder.c"), "-lm", "-o", out])
+    return out
+
+
+@pytest.mark.parametrize("T,E,H", [(1, 1, 1), (2, 3, 63), (1, 5, 64), (3, 2, 65), (2, 7, 130),
+                                   (1, 128, 2048), (2, 16, 6144)])
+def test_oracle_router_logits_under_sanitizers(corder_driver, T, E, H):
+    r = _run(corder_driver, [str(T), str(E), str(H)])
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr[-3000:]

@@ -32,6 +32,54 @@ __device__ __forceinline__ float chain_dot(const float4* __restrict__ rq, const 
     return acc;
 }
 
+// y = the previous layer's partial outputs summed in part order, then the
+// host part, at the 8 values of column block c: the additions of one loop over
+// the parts. Every row is requested before the first add, so the reads take one
+// memory round trip instead of one per part; the host part, read from host
+// memory, is requested first. The places past nparts (and the host part when
+// there is none) add +0.0, which changes no bits: y starts at +0.0 and a sum
+// of floats is never -0.0 under round to nearest.
+template <int NP>
+__device__ __forceinline__ void sum_parts_n(const EntryArgs& a, int c, float (&y)[8]) {
+    const bool hp = a.y_host != nullptr;
+    // with no host part, a part row stands in for its (unused) read
+    const float4* ph = (const float4*)(hp ? a.y_host : a.parts) + 2 * c;
+    const float4 h0 = ph[0], h1 = ph[1];
+    float4 p[NP > 0 ? NP : 1][2];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        const float4* pj = (const float4*)(a.parts + (size_t)min(j, a.nparts - 1) * a.H) + 2 * c;
+        p[j][0] = pj[0];
+        p[j][1] = pj[1];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) y[q] = 0.0f;
+    const float4 z4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        const bool on = j < a.nparts;
+        const float4 p0 = on ? p[j][0] : z4, p1 = on ? p[j][1] : z4;
+        y[0] += p0.x; y[1] += p0.y; y[2] += p0.z; y[3] += p0.w;
+        y[4] += p1.x; y[5] += p1.y; y[6] += p1.z; y[7] += p1.w;
+    }
+    const float4 q0 = hp ? h0 : z4, q1 = hp ? h1 : z4;
+    y[0] += q0.x; y[1] += q0.y; y[2] += q0.z; y[3] += q0.w;
+    y[4] += q1.x; y[5] += q1.y; y[6] += q1.z; y[7] += q1.w;
+}
+
+__device__ __forceinline__ void sum_parts(const EntryArgs& a, int c, float (&y)[8]) {
+    if (a.nparts <= 0)
+        sum_parts_n<0>(a, c, y);
+    else if (a.nparts <= 4)
+        sum_parts_n<4>(a, c, y);
+    else if (a.nparts <= 8)
+        sum_parts_n<8>(a, c, y);
+    else if (a.nparts <= 12)
+        sum_parts_n<12>(a, c, y);
+    else
+        sum_parts_n<kMaxK + 1>(a, c, y);
+}
+
 // s_u: [H] floats of LDS. Wavefronts past the last expert skip the logit.
 __device__ __forceinline__ void entry_body(const EntryArgs& a, float* s_u) {
     __shared__ float part[4];
@@ -55,20 +103,7 @@ __device__ __forceinline__ void entry_body(const EntryArgs& a, float* s_u) {
         uint32_t wd[4] = {v.x, v.y, v.z, v.w};
         if (a.nparts > 0 || a.y_host) {
             float y[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) y[q] = 0.0f;
-            for (int j = 0; j < a.nparts; ++j) {
-                const float4* pj = (const float4*)(a.parts + (size_t)j * H) + 2 * c;
-                float4 p0 = pj[0], p1 = pj[1];
-                y[0] += p0.x; y[1] += p0.y; y[2] += p0.z; y[3] += p0.w;
-                y[4] += p1.x; y[5] += p1.y; y[6] += p1.z; y[7] += p1.w;
-            }
-            if (a.y_host) {
-                const float4* ph = (const float4*)a.y_host + 2 * c;
-                float4 p0 = ph[0], p1 = ph[1];
-                y[0] += p0.x; y[1] += p0.y; y[2] += p0.z; y[3] += p0.w;
-                y[4] += p1.x; y[5] += p1.y; y[6] += p1.z; y[7] += p1.w;
-            }
+            sum_parts(a, c, y);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 wd[q] = f32_bf16_rne(bf16_f32(wd[q] & 0xFFFFu) + y[2 * q]) |
@@ -130,7 +165,9 @@ __device__ __forceinline__ void entry_body(const EntryArgs& a, float* s_u) {
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) acc = acc + __shfl_xor(acc, m, 64);
-    if (lane == 0) a.z[e] = acc;
+    // a device-scope store: the fused entry + plan kernel reads the logits of
+    // every workgroup without a cache writeback or invalidate
+    if (lane == 0) __hip_atomic_store(&a.z[e], acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 

@@ -420,15 +420,27 @@ __device__ __forceinline__ uint64_t wave_min_u64_1(uint64_t v) {
     return v;
 }
 
+// floor(a / b) for 0 <= a < 2^52 and b > 0, exactly: the double quotient is
+// within one of it, and the integer products correct it.
+__device__ __forceinline__ long long div_floor_small(long long a, long long b) {
+    long long q = (long long)((double)a / (double)b);
+    if (q * b > a)
+        --q;
+    else if ((q + 1) * b <= a)
+        ++q;
+    return q;
+}
+
 // The one-token plan for one workgroup of kThreads1 threads; smem64 holds
-// 12*C bytes of LDS.
+// 12*C bytes of LDS. x_lds != null: the token's row is taken from these LDS
+// floats (bf16 values) instead of from x.
 __device__ __forceinline__ void plan1_body(
     int64_t* smem64, int layer, const int32_t* ids_in, const float* w_in,
     const uint8_t* __restrict__ x, int x_bytes, int k, int E, int C,
     int32_t* __restrict__ g_slot_key, int64_t* __restrict__ g_slot_stamp,
     int32_t* __restrict__ key2slot, DevState* __restrict__ st, DevPlan* __restrict__ dp,
     DevPlan* __restrict__ hp, int32_t* __restrict__ h_ids, float* __restrict__ h_w,
-    uint8_t* __restrict__ h_x, PlanRoute rt) {
+    uint8_t* __restrict__ h_x, PlanRoute rt, const float* x_lds = nullptr) {
     int64_t* s_stamp = smem64;                // [C]
     int32_t* s_key = (int32_t*)(smem64 + C);  // [C]
     __shared__ int32_t s_ids[kMaxK];
@@ -455,10 +467,11 @@ __device__ __forceinline__ void plan1_body(
     int my_empty = 0;
     constexpr int kB = 16, kLoaders = kThreads1 - 64, kRowPer = kMaxE / 64;
     if (wave == 0) {
+        // unconditional loads (indexes clamped into the row): no load waits
+        // for the one before it
         int32_t k2[kRowPer];
 #pragma unroll
-        for (int i = 0; i < kRowPer; ++i)
-            if (lane + 64 * i < E) k2[i] = key2slot[layer * E + lane + 64 * i];
+        for (int i = 0; i < kRowPer; ++i) k2[i] = key2slot[layer * E + min(lane + 64 * i, E - 1)];
         long long c0 = 0, c1 = 0;
         int v0 = 0, v1 = 0, v2 = 0, v3 = 0;
         if (lane == 0) {
@@ -470,7 +483,7 @@ __device__ __forceinline__ void plan1_body(
             v3 = st->frozen;
         }
         if (rt.z) {
-            topk_token(rt.z, E, k, rt.forced, s_ids, s_w);
+            topk_token<true>(rt.z, E, k, rt.forced, s_ids, s_w);
         } else if (lane < k) {
             s_ids[lane] = ids_in[lane];
             s_w[lane] = w_in ? w_in[lane] : 0.0f;
@@ -493,12 +506,10 @@ __device__ __forceinline__ void plan1_body(
             int32_t kr[kB];
             int64_t sr[kB];
 #pragma unroll
-            for (int i = 0; i < kB; ++i) {
-                const int sl = lt + kLoaders * (b0 + i);
-                if (sl < C) {
-                    kr[i] = g_slot_key[sl];
-                    sr[i] = g_slot_stamp[sl];
-                }
+            for (int i = 0; i < kB; ++i) {  // unconditional (clamped): all in flight at once
+                const int sl = min(lt + kLoaders * (b0 + i), C - 1);
+                kr[i] = g_slot_key[sl];
+                sr[i] = g_slot_stamp[sl];
             }
 #pragma unroll
             for (int i = 0; i < kB; ++i) {
@@ -525,9 +536,10 @@ __device__ __forceinline__ void plan1_body(
     const int64_t clock = s_clock0 + 1;
     if (wave == 0) {
         const bool bad = act && (e < 0 || e >= E);
+        // other lanes' experts are read across the wavefront (no LDS round trips)
         bool dup = false;
-        if (act && !bad)
-            for (int jj = 0; jj < lane; ++jj) dup |= s_ids[jj] == e;
+        for (int jj = 0; jj < k; ++jj) dup |= jj < lane && __builtin_amdgcn_readlane(e, jj) == e;
+        dup = dup && act && !bad;
         const uint64_t mbad = __ballot(bad), mdup = __ballot(dup);
         if (mbad | mdup) {
             if (lane == 0) s_err = mbad ? 1 : 2;
@@ -539,10 +551,11 @@ __device__ __forceinline__ void plan1_body(
             n_hit = __popcll(mh);
             m = __popcll(mm);
             for (int jj = 0; jj < k; ++jj)  // rank among the hits (or misses) by expert id
-                rank += ((hit ? (mh >> jj) : (mm >> jj)) & 1) && s_ids[jj] < e;
+                rank += ((hit ? (mh >> jj) : (mm >> jj)) & 1) &&
+                        __builtin_amdgcn_readlane(e, jj) < e;
             if (lane == 0) {  // the split (integer credit)
                 const long long c = s_credit0, bp = s_bp, bh = s_bh;
-                q = (c + (long long)m * bp) / bh;
+                q = div_floor_small(c + (long long)m * bp, bh);
                 if (q > m) q = m;
                 c2 = c + (long long)m * bp - q * bh;
                 if (c2 > bh - 1) c2 = bh - 1;
@@ -577,21 +590,35 @@ __device__ __forceinline__ void plan1_body(
     if (q_fill > 0) {  // block-uniform
         // victims (stamp asc, key asc) among occupied slots not touched in
         // this call, one per missing empty slot: each thread keeps the oldest
-        // of its own range, one workgroup minimum per victim, and only the
-        // owner of the victim looks at its range again
+        // of its slots (tid, tid + 256, ...; read four at a time), one
+        // workgroup minimum per victim, and only the owner of the victim looks
+        // at its slots again
         const int n_vic = q_fill - s_empty;  // workgroup-uniform
         uint64_t mine = ~0ull;
         int mine_slot = -1;
         auto oldest = [&]() {
             mine = ~0ull;
-            for (int sl = s_lo; sl < s_hi; ++sl)
-                if (s_key[sl] >= 0 && s_stamp[sl] < clock) {
-                    const uint64_t v = ((uint64_t)s_stamp[sl] << 24) | (uint64_t)s_key[sl];
-                    if (v < mine) {
-                        mine = v;
-                        mine_slot = sl;
+            for (int s0 = tid; s0 < C; s0 += 4 * kThreads1) {
+                int32_t kk[4];
+                int64_t ss[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int sl = min(s0 + u * kThreads1, C - 1);
+                    kk[u] = s_key[sl];
+                    ss[u] = s_stamp[sl];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int sl = s0 + u * kThreads1;
+                    if (sl < C && kk[u] >= 0 && ss[u] < clock) {
+                        const uint64_t v = ((uint64_t)ss[u] << 24) | (uint64_t)kk[u];
+                        if (v < mine) {
+                            mine = v;
+                            mine_slot = sl;
+                        }
                     }
                 }
+            }
         };
         if (n_vic > 0) oldest();
         for (int r = 0; r < n_vic; ++r) {
@@ -683,9 +710,21 @@ __device__ __forceinline__ void plan1_body(
     }
     __syncthreads();
     if (h_x && s_nhost > 0) {
-        const uint4* xs = (const uint4*)x;
         uint4* xd = (uint4*)h_x;
-        for (int i = tid; i < x_bytes / 16; i += kThreads1) xd[i] = xs[i];
+        if (x_lds) {  // 8 bf16 values held as floats -> 16 bytes of bf16
+            for (int i = tid; i < x_bytes / 16; i += kThreads1) {
+                const float* f = x_lds + 8 * i;
+                uint32_t wd[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    wd[q] = (__float_as_uint(f[2 * q]) >> 16) |
+                            (__float_as_uint(f[2 * q + 1]) & 0xFFFF0000u);
+                xd[i] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+            }
+        } else {
+            const uint4* xs = (const uint4*)x;
+            for (int i = tid; i < x_bytes / 16; i += kThreads1) xd[i] = xs[i];
+        }
     }
     __syncthreads();
     if (tid == 0) {
@@ -709,11 +748,22 @@ __global__ __launch_bounds__(kThreads1) void k_plan1(
                key2slot, st, dp, hp, h_ids, h_w, h_x, rt);
 }
 
+// LDS of the fused kernel: the plan's slot table, then the entry's row of H floats.
+__host__ __device__ constexpr size_t entry_plan_row_off(int C) { return (12 * (size_t)C + 15) / 16 * 16; }
+__host__ __device__ constexpr size_t entry_plan_lds(int C, int H) {
+    return entry_plan_row_off(C) + 4 * (size_t)H;
+}
+// dynamic LDS limit of the fused kernel (its static LDS is under 16 KB)
+constexpr size_t kMaxLdsBytes = 144 * 1024;
+
 // Layer entry and one-token plan in one launch. Every workgroup runs the
 // entry (residual, norm, its experts' logits); the last one to finish, found
-// with a ticket counter after a device-scope release of its logits, runs the
-// plan on the complete logit vector. No workgroup waits for another, and the
-// last one resets the counter for the next launch.
+// with a ticket counter, runs the plan on the complete logit vector. No
+// workgroup waits for another, and the last one resets the counter for the
+// next launch. The logits are the only data one workgroup of the launch reads
+// from another: they are stored and read at device scope, and each workgroup's
+// stores have completed before it takes its ticket, so no cache writeback or
+// invalidate is needed. The plan takes the token's row from its own LDS copy.
 __global__ __launch_bounds__(kThreads1) void k_entry_plan1(
     EntryArgs ea, int layer, int k, int C, int32_t* __restrict__ g_slot_key,
     int64_t* __restrict__ g_slot_stamp, int32_t* __restrict__ key2slot,
@@ -722,16 +772,17 @@ __global__ __launch_bounds__(kThreads1) void k_entry_plan1(
     PlanRoute rt) {
     extern __shared__ int64_t smem64[];
     __shared__ int s_last;
-    entry_body(ea, (float*)smem64);
-    __threadfence();  // this workgroup's logits (and workgroup 0's u) reach device scope
+    float* s_u = (float*)((uint8_t*)smem64 + entry_plan_row_off(C));
+    entry_body(ea, s_u);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the logit store stays above the wait
+    __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wavefront's logit store has completed
     __syncthreads();
     if (threadIdx.x == 0) s_last = atomicAdd(&st->ticket, 1) == (int)gridDim.x - 1;
     __syncthreads();
     if (!s_last) return;
-    __threadfence();  // acquire: every other workgroup's logits are visible
     if (threadIdx.x == 0) st->ticket = 0;
-    plan1_body(smem64, layer, nullptr, nullptr, (const uint8_t*)ea.u, ea.H * 2, k, ea.E, C,
-               g_slot_key, g_slot_stamp, key2slot, st, dp, hp, h_ids, h_w, h_x, rt);
+    plan1_body(smem64, layer, nullptr, nullptr, nullptr, ea.H * 2, k, ea.E, C, g_slot_key,
+               g_slot_stamp, key2slot, st, dp, hp, h_ids, h_w, h_x, rt, s_u);
 }
 
 }  // namespace
@@ -771,7 +822,8 @@ hipError_t launch_plan(int layer, const int32_t* ids, const float* w, const void
 }
 
 bool entry_plan_ok(int T, int k, int E, int H, int64_t C, int act_bf16) {
-    return T == 1 && k <= 64 && C <= kMaxSlotsLds && entry_ok(E, H, act_bf16);
+    return T == 1 && k <= 64 && C <= kMaxSlotsLds && entry_ok(E, H, act_bf16) &&
+           entry_plan_lds((int)C, H) <= kMaxLdsBytes;
 }
 
 hipError_t launch_entry_plan(const EntryArgs& a, int layer, int k, int64_t C, int32_t* slot_key,
@@ -783,11 +835,11 @@ hipError_t launch_entry_plan(const EntryArgs& a, int layer, int k, int64_t C, in
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)k_entry_plan1,
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)std::max<size_t>(12 * kMaxSlotsLds, 4 * 16384));
+                                           (int)kMaxLdsBytes);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const size_t lds = std::max<size_t>(12 * (size_t)C, 4 * (size_t)a.H);
+    const size_t lds = entry_plan_lds((int)C, a.H);
     k_entry_plan1<<<a.E / 4, kThreads1, lds, s>>>(a, layer, k, (int)C, slot_key, slot_stamp,
                                                    key2slot, st, d_plan, h_plan, h_ids, h_w,
                                                    (uint8_t*)h_x, rt);

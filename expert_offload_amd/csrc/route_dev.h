@@ -16,8 +16,16 @@ __device__ __forceinline__ bool topk_better(float za, int ia, float zb, int ib) 
     return za > zb || (za == zb && ia < ib);
 }
 
+// A logit read; kCoherent reads at device scope (logits other workgroups of
+// the same launch stored at device scope, with no cache invalidate between).
+template <bool kCoherent>
+__device__ __forceinline__ float zload(const float* p) {
+    if (kCoherent) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return *p;
+}
+
 // k rounds of (max z, then smallest id) over E <= 64 * kPer logits.
-template <int kPer>
+template <int kPer, bool kCoherent = false>
 __device__ __forceinline__ void topk_select(const float* __restrict__ zt, int E, int k, float* zs,
                                             int* is) {
     const int lane = threadIdx.x & 63;
@@ -27,7 +35,7 @@ __device__ __forceinline__ void topk_select(const float* __restrict__ zt, int E,
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             int e = lane + 64 * i;
-            zl[i] = e < E ? zt[e] : -INFINITY;
+            zl[i] = e < E ? zload<kCoherent>(zt + e) : -INFINITY;
         }
         for (int j = 0; j < k; ++j) {
             float bz = -INFINITY;
@@ -60,13 +68,16 @@ __device__ __forceinline__ void topk_select(const float* __restrict__ zt, int E,
 // All 64 lanes of the wavefront call this; lane j < k writes ids[j] and w[j].
 // w = softmax over the k selected logits: max, exponentials, their sum in
 // j order, then one division per weight.
+template <bool kCoherent = false>
 __device__ __forceinline__ void topk_token(const float* __restrict__ zt, int E, int k,
                                            const int32_t* __restrict__ forced_t,
                                            int32_t* __restrict__ ids_t, float* __restrict__ w_t) {
     const int lane = threadIdx.x & 63;
     int my_i = 0;  // lane j < k: the j-th selected expert and its logit
     float my_z = -INFINITY;
-    __shared__ float s_zw[4][256];  // per wavefront of the workgroup (up to 4)
+    // per wavefront of the workgroup (up to 4); E <= 256 logits and -inf up
+    // to the next multiple of 4
+    __shared__ __attribute__((aligned(16))) float s_zw[4][260];
     __shared__ int32_t s_selw[4][kMaxK];
     float* s_z = s_zw[(threadIdx.x >> 6) & 3];
     int32_t* s_sel = s_selw[(threadIdx.x >> 6) & 3];
@@ -75,19 +86,20 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ zt, int E, 
         // out-of-range id is reported by the lookup, its logit read in bounds
         if (lane < k) my_i = forced_t[lane];
         if (E <= 256) {
-            for (int e = lane; e < E; e += 64) s_z[e] = zt[e];
+            for (int e = lane; e < E; e += 64) s_z[e] = zload<kCoherent>(zt + e);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
             if (lane < k) my_z = s_z[min(max(my_i, 0), E - 1)];
         } else if (lane < k) {
-            my_z = zt[min(max(my_i, 0), E - 1)];
+            my_z = zload<kCoherent>(zt + min(max(my_i, 0), E - 1));
         }
     } else if (E <= 256) {
         // each logit's rank = how many logits beat it (larger, or equal with a
         // smaller id); the k of rank < k are the selection, in (z desc, id asc)
         // order: the same result as k rounds of selection
-        for (int e = lane; e < E; e += 64) s_z[e] = zt[e];
+        for (int e = lane; e < E; e += 64) s_z[e] = zload<kCoherent>(zt + e);
+        if (lane < ((E + 3) & ~3) - E) s_z[E + lane] = -INFINITY;  // never beats a logit
         if (lane < k) s_sel[lane] = -1;  // stays -1 only for unordered (NaN) logits
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_wave_barrier();
@@ -95,9 +107,12 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ zt, int E, 
         for (int e = lane; e < E; e += 64) {
             const float z = s_z[e];
             int r = 0;
-            for (int o = 0; o < E; ++o) {
-                const float zo = s_z[o];
-                r += zo > z || (zo == z && o < e);
+            for (int o = 0; o < E; o += 4) {  // four logits per LDS read
+                const float4 zo = *(const float4*)(s_z + o);
+                r += zo.x > z || (zo.x == z && o < e);
+                r += zo.y > z || (zo.y == z && o + 1 < e);
+                r += zo.z > z || (zo.z == z && o + 2 < e);
+                r += zo.w > z || (zo.w == z && o + 3 < e);
             }
             if (r < k) s_sel[r] = e;
         }
@@ -111,7 +126,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ zt, int E, 
     } else {
         float zs[kMaxK];
         int is[kMaxK];
-        topk_select<kMaxE / 64>(zt, E, k, zs, is);
+        topk_select<kMaxE / 64, kCoherent>(zt, E, k, zs, is);
         for (int j = 0; j < k; ++j)
             if (lane == j) {
                 my_z = zs[j];

@@ -158,6 +158,9 @@ eo_status eo_remeasure_bandwidth(eo_engine* e, uint32_t* bp_mbps, uint32_t* bh_m
 eo_status eo_set_bandwidth(eo_engine* e, uint32_t bp_mbps, uint32_t bh_mbps);
 
 /* ---- step calls (stream-ordered; x, ids, w, y are device pointers) ---- */
+/* T, the tokens of a call, is 1 .. max_tokens: an empty batch (T = 0) or a
+ * larger one returns EO_ERR_INVALID_ARG before anything is launched, and the
+ * cache, the LRU clock, the credit and the statistics stay as they were. */
 
 /* Route, the first stage of a layer (explainer on papers.ananclaw.com, section
  * 4, engineering path: softmax top-k routing, the expert count and the shared

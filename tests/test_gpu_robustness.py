@@ -7,6 +7,9 @@
   75.5 MB expert, 618 GB) returns EO_ERR_OOM and leaves the engine as it was:
   the slot table is unchanged and the next layer call matches the oracle. An
   engine whose cache cannot be allocated is not created, and the next one is.
+* An empty batch (T = 0) or one above max_tokens is rejected by every step call
+  with EO_ERR_INVALID_ARG before any launch: buffers untouched, cache, clock,
+  credit and statistics unchanged, and the next calls match the oracle.
 """
 import numpy as np
 import pytest
@@ -101,6 +104,66 @@ def test_failed_device_allocation_leaves_the_engine_usable():
         xf = synth.bf16_bits_to_f32(x2)
         rids, rw, _ = OR.route(xf, synth.router_weights(seed, 0, shape.experts, H), shape.top_k)
         assert rel_err(y.cpu().numpy(), oracle_layer(shape, seed, 0, xf, rids, rw)) <= 2e-2
+        eo.eo_sync(e)
+    finally:
+        eo.eo_destroy(e)
+
+
+def test_empty_and_oversized_batches_are_rejected():
+    shape = synth.LayerShape("edge_bf16", "test", 512, 16, 4, 256, 2, synth.FMT_BF16, 8, 6,
+                             shared=1)
+    seed = 43
+    H, k, C, L = shape.hidden, shape.top_k, shape.cache_slots, shape.layers
+    e = make_engine(shape, seed, max_tokens=8)
+    try:
+        eo.eo_set_bandwidth(e, 1, 2)
+        x = synth.activations(seed, 1, 3, H, 1.0, True)
+        xd = dev(x.view(np.int16))
+        y = torch.zeros((3, H), dtype=torch.float32, device="cuda")
+        eo.eo_moe_layer(e, 0, xd, y, 3, None, _s())  # some state first
+        torch.cuda.synchronize()
+        keys0 = np.zeros(C, dtype=np.int32)
+        stamps0 = np.zeros(C, dtype=np.int64)
+        snap0 = eo.eo_cache_snapshot(e, keys0, stamps0)
+        st0 = {n: v for n, v in eo.eo_stats_get(e).items() if not n.endswith("_ns")}
+        big = dev(synth.activations(seed, 2, 9, H, 1.0, True).view(np.int16))
+        before = big.clone()
+        ids = torch.full((9, k), -7, dtype=torch.int32, device="cuda")
+        w = torch.full((9, k), -7.0, dtype=torch.float32, device="cuda")
+        yb = torch.full((9, H), -7.0, dtype=torch.float32, device="cuda")
+        calls = [
+            lambda T: eo.eo_route(e, 0, big, T, None, ids, w, _s()),
+            lambda T: eo.eo_route_noalloc(e, 0, big, T, None, ids, w, _s()),
+            lambda T: eo.eo_lookup_plan(e, 0, ids, T, _s()),
+            lambda T: eo.eo_moe_layer(e, 1, big, yb, T, None, _s()),
+            lambda T: eo.eo_decode_step(e, big, T, None, _s()),
+            lambda T: eo.eo_prefill(e, big, T, eo.EO_PREFILL_DOUBLE_BUFFER, _s()),
+        ]
+        for n, call in enumerate(calls):
+            for T in (0, 9):
+                with pytest.raises(eo.EOError) as ex:
+                    call(T)
+                assert ex.value.status == eo.EO_ERR_INVALID_ARG, (n, T)
+        torch.cuda.synchronize()
+        assert torch.equal(big, before)
+        assert bool((ids == -7).all()) and bool((w == -7.0).all()) and bool((yb == -7.0).all())
+        keys1 = np.zeros(C, dtype=np.int32)
+        stamps1 = np.zeros(C, dtype=np.int64)
+        assert eo.eo_cache_snapshot(e, keys1, stamps1) == snap0
+        assert np.array_equal(keys0, keys1) and np.array_equal(stamps0, stamps1)
+        assert {n: v for n, v in eo.eo_stats_get(e).items() if not n.endswith("_ns")} == st0
+        # no plan is pending: the per-stage calls still refuse, the layer call serves
+        with pytest.raises(eo.EOError) as ex:
+            eo.eo_fill(e, _s())
+        assert ex.value.status == eo.EO_ERR_STATE
+        x2 = synth.activations(seed, 3, 8, H, 1.0, True)
+        y2 = torch.zeros((8, H), dtype=torch.float32, device="cuda")
+        eo.eo_moe_layer(e, 1, dev(x2.view(np.int16)), y2, 8, None, _s())
+        torch.cuda.synchronize()
+        xf = synth.bf16_bits_to_f32(x2)
+        rids, rw, _ = OR.route(xf, synth.router_weights(seed, 1, shape.experts, H), k)
+        assert rel_err(y2.cpu().numpy(), oracle_layer(shape, seed, 1, xf, rids, rw)) <= 2e-2
+        assert eo.eo_last_plan(e)["clock"] == snap0[0] + 1
         eo.eo_sync(e)
     finally:
         eo.eo_destroy(e)

@@ -20,6 +20,7 @@ HIP_SOURCES = ["engine.hip", "k_router.hip", "k_plan.hip", "k_permute.hip", "k_g
 HOST_SOURCES = ["host_ffn.cpp", "layout.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ROCM_LIB = "/opt/rocm/lib"  # the trace ranges' library (roctx)
 # Packed fp32 VALU instructions are kept out of the device code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
              "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -50,7 +51,8 @@ def build(verbose: bool = False) -> str:
                 sys.stderr.write(r.stdout + r.stderr)
     objs = [j[-1] for j in jobs]
     tmp = LIB + f".tmp{os.getpid()}"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs, "-lpthread"])
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs, "-lpthread",
+          "-L" + ROCM_LIB, "-Wl,-rpath," + ROCM_LIB, "-lrocprofiler-sdk-roctx"])
     os.replace(tmp, LIB)
     return LIB
 

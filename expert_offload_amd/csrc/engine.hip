@@ -2,10 +2,13 @@
 // LRU expert cache backed by a pinned host expert pool (FreeToken; zhichai.net
 // article, section 2: Prefill, Decode and LRU paragraphs).
 //
-// Per layer call: route -> lookup/plan (device) -> the host reads the plan from
-// mapped memory -> fills on the copy stream (SDMA, host->device) -> device FFN
-// on the hits and fills -> host-core FFN on the host list, overlapped with the
-// device -> combine. Prefill streams whole layers into two staging buffers.
+// Per layer call: route -> lookup/plan (device) -> fills by a kernel that reads
+// the fill list from device memory and the pool over PCIe (hipMemcpyAsync on
+// the copy stream under EO_FILL_SDMA=1) -> device FFN on the hits and fills ->
+// host-core FFN on the host list (the host reads the plan from mapped memory),
+// overlapped with the device -> combine. Prefill streams whole layers into two
+// staging buffers. Trace ranges (roctx) name each step call, each layer of a
+// decode step or prefill, the plan wait and the host routine.
 #include <algorithm>
 #include <chrono>
 #include <cstdio>
@@ -18,9 +21,20 @@
 
 #include <immintrin.h>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "eo_internal.h"
 
 namespace eo {
+
+// A trace range for the scope (roctx: shown by profilers that record markers,
+// a no-op call otherwise).
+struct TraceRange {
+    explicit TraceRange(const char* name) { roctxRangePushA(name); }
+    ~TraceRange() { roctxRangePop(); }
+    TraceRange(const TraceRange&) = delete;
+    TraceRange& operator=(const TraceRange&) = delete;
+};
 int plan_max_slots();
 }
 
@@ -268,6 +282,7 @@ eo_status ensure_gemm(eo_engine* e, int T, hipStream_t s) {
 eo_status wait_plan(eo_engine* e) {
     if (!e->plan_pending) return fail(EO_ERR_STATE, "no pending plan (call eo_lookup_plan first)");
     if (e->plan_ready) return EO_OK;
+    TraceRange trace_range("eo.wait_plan");
     auto t0 = std::chrono::steady_clock::now();
     struct WaitTimer {  // host time spent in this wait, on every way out
         eo_engine* e;
@@ -432,6 +447,7 @@ eo_status do_host(eo_engine* e, const void* x, const int32_t* ids, const float* 
     jb.experts = table.data();
     jb.y = e->h_yhost;
     const auto th0 = std::chrono::steady_clock::now();
+    TraceRange trace_range("eo.host_routine");
     host_ffn(e->tp, jb, e->host_scratch);
     e->stats.host_routine_ns += std::chrono::duration_cast<std::chrono::nanoseconds>(
                                     std::chrono::steady_clock::now() - th0).count();
@@ -554,6 +570,7 @@ eo_status decode_one_token(eo_engine* e, uint16_t* x_inout, const int32_t* force
                            entry_plan_ok(1, k, e->E, H, e->C, e->act_bf16);
     const float* prev_host = nullptr;
     for (int l = 0; l < e->L; ++l) {
+        TraceRange trace_range("eo.decode.layer");
         int32_t* ids = e->d_ids;
         float* w = e->d_w;
         EntryArgs a;
@@ -971,10 +988,12 @@ static eo_status measure_impl(eo_engine* e, bool keep_cache, uint32_t* bp_out, u
 }
 
 eo_status eo_measure_bandwidth(eo_engine* e, uint32_t* bp_out, uint32_t* bh_out) {
+    TraceRange trace_range("eo.measure_bandwidth");
     return measure_impl(e, false, bp_out, bh_out);
 }
 
 eo_status eo_remeasure_bandwidth(eo_engine* e, uint32_t* bp_out, uint32_t* bh_out) {
+    TraceRange trace_range("eo.remeasure_bandwidth");
     return measure_impl(e, true, bp_out, bh_out);
 }
 
@@ -1045,6 +1064,7 @@ eo_status eo_expert_ffn_combine(eo_engine* e, int32_t layer, const void* x, cons
 
 eo_status eo_moe_layer(eo_engine* e, int32_t layer, const void* x, float* y, int32_t T,
                        const int32_t* forced_ids, void* stream) {
+    TraceRange trace_range("eo.moe_layer");
     EOCHK(check_layer(e, layer));
     EOCHK(check_T(e, T));
     if (!x || !y) return fail(EO_ERR_INVALID_ARG, "null argument");
@@ -1057,6 +1077,7 @@ eo_status eo_moe_layer(eo_engine* e, int32_t layer, const void* x, float* y, int
 
 eo_status eo_decode_step(eo_engine* e, void* x_inout, int32_t T, const int32_t* forced_ids,
                          void* stream) {
+    TraceRange trace_range("eo.decode_step");
     if (!e || !x_inout) return fail(EO_ERR_INVALID_ARG, "null argument");
     EOCHK(check_T(e, T));
     if (!aligned16(x_inout)) return fail(EO_ERR_INVALID_ARG, "x must be 16-byte aligned");
@@ -1089,6 +1110,7 @@ eo_status eo_decode_step(eo_engine* e, void* x_inout, int32_t T, const int32_t* 
 }
 
 eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t flags, void* stream) {
+    TraceRange trace_range("eo.prefill");
     if (!e || !x_inout) return fail(EO_ERR_INVALID_ARG, "null argument");
     EOCHK(check_T(e, T));
     if (!aligned16(x_inout)) return fail(EO_ERR_INVALID_ARG, "x must be 16-byte aligned");
@@ -1159,6 +1181,7 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t flags, void
     EOCHK(copy_layer(0, 0));
     HIPCHK(hipEventRecord(e->ev_copy[0], e->copy_stream));
     for (int l = 0; l < e->L; ++l) {
+        TraceRange trace_range("eo.prefill.layer");
         const int b = l & 1, nb = b ^ 1;
         HIPCHK(hipStreamWaitEvent(s, e->ev_copy[b], 0));
         if (double_buffer && l + 1 < e->L) {
@@ -1233,6 +1256,7 @@ eo_status eo_set_capture(eo_engine* e, void* x_in, float* y, int32_t* ids, float
 }
 
 eo_status eo_resize_cache(eo_engine* e, int64_t slots, int64_t* n_evicted, int64_t* n_moved) {
+    TraceRange trace_range("eo.resize_cache");
     if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
     if (slots < 0 || slots > plan_max_slots())
         return fail(EO_ERR_INVALID_ARG, "slots out of range [0, 8192]");

@@ -29,6 +29,11 @@
  *     fill, expert FFN, host-execute, combine; per layer in eo_decode_step and
  *     eo_prefill) and report an asynchronous device error as EO_ERR_HIP naming
  *     the stage and layer. Results are the same as without it.
+ *   - Tracing: every step call, each layer of eo_decode_step and eo_prefill,
+ *     the host's wait for a plan and the host-core routine are named trace
+ *     ranges (roctx: "eo.decode_step", "eo.decode.layer", "eo.wait_plan",
+ *     "eo.host_routine", "eo.prefill", ...), which a profiler that records
+ *     markers shows beside the kernels (rocprofv3 --marker-trace).
  * Tensor layouts are row-major. Activations are bf16 (act_bf16 = 1) or fp32.
  */
 #ifndef EO_H

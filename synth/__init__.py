@@ -196,16 +196,23 @@ class LayerShape:
     steps: int = 0
 
 
-# The five workloads, by what they are.
-SHAPES = {
-    "tiny_fp32": LayerShape("tiny_fp32", "parity", 256, 16, 2, 128, 1, FMT_FP32, 64, 8),
-    "decode_bf16_48L": LayerShape("decode_bf16_48L", "decode", 2048, 128, 8, 768, 48, FMT_BF16, 1,
-                                  int(0.37 * 48 * 128), steps=512),
-    "prefill_bf16_48L": LayerShape("prefill_bf16_48L", "prefill", 2048, 128, 8, 768, 48,
-                                   FMT_BF16, 8192, int(0.37 * 48 * 128)),
-    "decode_mxfp4_43L": LayerShape("decode_mxfp4_43L", "decode", 4096, 256, 8, 2048, 43,
-                                   FMT_MXFP4, 1, int(0.11 * 43 * 256), shared=1, steps=512),
-    "prefill_decode_nvfp4_8L": LayerShape("prefill_decode_nvfp4_8L", "prefill+decode", 6144, 256,
-                                          8, 2048, 8, FMT_NVFP4, 8192, 2 * 256, shared=1,
-                                          steps=256),
-}
+# The five workloads, by what they are (synth/workloads.json: shapes, formats,
+# cache sizes and the generators' parameters, one file for every consumer).
+WORKLOADS_JSON = os.path.join(os.path.dirname(os.path.abspath(__file__)), "workloads.json")
+
+
+def _load_shapes(path: str = WORKLOADS_JSON) -> dict:
+    import json
+    with open(path) as f:
+        doc = json.load(f)
+    out = {}
+    for w in doc["workloads"]:
+        slots = w["cache_slots"] if "cache_slots" in w else \
+            int(w["cache_fraction"] * w["layers"] * w["experts"])
+        out[w["name"]] = LayerShape(w["name"], w["mode"], w["hidden"], w["experts"], w["top_k"],
+                                    w["inter"], w["layers"], FMT_NAMES[w["format"]], w["tokens"],
+                                    slots, shared=w["shared"], steps=w["steps"])
+    return out
+
+
+SHAPES = _load_shapes()

@@ -285,6 +285,24 @@ def test_decode_fused_entry_matches_separate_kernels(forced):
     assert a[-2:] == b[-2:]
 
 
+def test_decode_entry_and_plan_in_one_launch_long_run():
+    # the one-launch entry + plan at the benchmark's layer shape (H 2048, 128
+    # experts: 32 workgroups store their logits at device scope for the last
+    # one to plan from) over 1200 launches, the router choosing the experts:
+    # every capture, the statistics and the slot table equal the separate
+    # entry and plan launches, whose logits cross a kernel boundary
+    base = synth.SHAPES["decode_bf16_48L"]
+    shape = dataclasses.replace(base, layers=8, cache_slots=int(0.37 * 8 * base.experts))
+    steps = 150
+    a = _decode_capture(shape, 31, steps, False, {"EO_ENTRY_PLAN": "1"}, shape.cache_slots)
+    b = _decode_capture(shape, 31, steps, False, {"EO_ENTRY_PLAN": "0"}, shape.cache_slots)
+    for s in range(steps):
+        for i in range(1, 6):
+            assert np.array_equal(a[s][i], b[s][i]), (s, i)
+    assert a[-2:] == b[-2:]
+    assert a[-2]["fills"] > 0 and a[-2]["host_experts"] > 0
+
+
 @pytest.mark.parametrize("experts,top_k,slots", [(16, 4, 7), (128, 8, 90), (128, 8, 0)])
 @pytest.mark.parametrize("forced", [True, False])
 def test_decode_entry_and_plan_in_one_launch(experts, top_k, slots, forced):

@@ -91,6 +91,7 @@ _SIGS = {
     "eo_clear_static_placement": [_P],
     "eo_kernel_times": [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64), _I32],
     "eo_set_timing": [_P, _I32],
+    "eo_stream_times": [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64), _I32],
     "eo_set_plan_log": [_P, _I32],
     "eo_get_plan_log": [_P, _P, _I64, ctypes.POINTER(_I64)],
     "eo_expert_bytes": [_I32, _I32, _I32],
@@ -319,6 +320,13 @@ def eo_kernel_times(e, reset: bool = False) -> dict:
     return {"gemv_gate_up_ms": ms[0], "gemv_down_ms": ms[1], "gemm_gate_up_ms": ms[2],
             "gemm_down_ms": ms[3], "fill_ms": ms[4], "gemv_launches": n[0],
             "gemm_launches": n[1], "fill_launches": n[2]}
+
+
+def eo_stream_times(e, reset: bool = False) -> dict:
+    ms = (ctypes.c_double * 2)()
+    n = (_I64 * 2)()
+    _check(lib().eo_stream_times(e, ms, n, 1 if reset else 0))
+    return {"copy_ms": ms[0], "compute_ms": ms[1], "copy_layers": n[0], "compute_layers": n[1]}
 
 
 def eo_sync(e) -> None:

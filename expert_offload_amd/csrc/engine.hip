@@ -151,6 +151,10 @@ struct eo_engine {
     std::vector<TimedSet> gemv_ev, gemm_ev, fill_ev, free_ev;
     double kms[5] = {0, 0, 0, 0, 0};  // gemv gate/up, gemv down, gemm1, gemm2, fill
     int64_t gemv_n = 0, gemm_n = 0, fill_n = 0;
+    // prefill: one layer's copies on the copy stream / its kernels on the compute stream
+    std::vector<TimedSet> copy_ev, comp_ev;
+    double sms[2] = {0, 0};
+    int64_t copy_n = 0, comp_n = 0;
 
     void* cap_x = nullptr;
     float* cap_y = nullptr;
@@ -216,15 +220,19 @@ eo_status harvest_times(eo_engine* e) {
         }
         v->clear();
     }
-    for (auto& p : e->fill_ev) {
-        HIPCHK(hipEventSynchronize(p.ev[1]));
-        float m0 = 0;
-        HIPCHK(hipEventElapsedTime(&m0, p.ev[0], p.ev[1]));
-        e->kms[4] += m0;
-        e->fill_n += 1;
-        e->free_ev.push_back(p);
+    for (auto* v : {&e->fill_ev, &e->copy_ev, &e->comp_ev}) {
+        double& acc = v == &e->fill_ev ? e->kms[4] : e->sms[v == &e->copy_ev ? 0 : 1];
+        int64_t& n = v == &e->fill_ev ? e->fill_n : v == &e->copy_ev ? e->copy_n : e->comp_n;
+        for (auto& p : *v) {
+            HIPCHK(hipEventSynchronize(p.ev[1]));
+            float m0 = 0;
+            HIPCHK(hipEventElapsedTime(&m0, p.ev[0], p.ev[1]));
+            acc += m0;
+            n += 1;
+            e->free_ev.push_back(p);
+        }
+        v->clear();
     }
-    e->fill_ev.clear();
     return EO_OK;
 }
 
@@ -660,7 +668,7 @@ void destroy_all(eo_engine* e) {
     for (hipEvent_t ev : {e->ev_fill, e->ev_copy[0], e->ev_copy[1], e->ev_comp[0], e->ev_comp[1],
                           e->ev_start})
         if (ev) (void)hipEventDestroy(ev);
-    for (auto* v : {&e->gemv_ev, &e->gemm_ev, &e->fill_ev, &e->free_ev})
+    for (auto* v : {&e->gemv_ev, &e->gemm_ev, &e->fill_ev, &e->copy_ev, &e->comp_ev, &e->free_ev})
         for (auto& p : *v)
             for (hipEvent_t ev : p.ev) (void)hipEventDestroy(ev);
     if (e->tp) threadpool_destroy(e->tp);
@@ -1153,7 +1161,7 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t flags, void
     int64_t streamed = 0;
     // layer l's experts into staging buffer `buf` on the copy stream (runs of
     // consecutive non-resident experts when skipping)
-    auto copy_layer = [&](int l, int buf) -> eo_status {
+    auto copy_layer_bytes = [&](int l, int buf) -> eo_status {
         if (!skip) {
             HIPCHK(hipMemcpyAsync(e->d_staging[buf], e->pool[l], layer_bytes, hipMemcpyHostToDevice,
                                   e->copy_stream));
@@ -1175,6 +1183,20 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t flags, void
         }
         return EO_OK;
     };
+    // the same between two timing events on the copy stream when timing is on
+    auto copy_layer = [&](int l, int buf) -> eo_status {
+        TimedSet ts{};
+        if (e->timing) {
+            EOCHK(get_set(e, &ts));
+            HIPCHK(hipEventRecord(ts.ev[0], e->copy_stream));
+        }
+        EOCHK(copy_layer_bytes(l, buf));
+        if (e->timing) {
+            HIPCHK(hipEventRecord(ts.ev[1], e->copy_stream));
+            e->copy_ev.push_back(ts);
+        }
+        return EO_OK;
+    };
     // the first copy must not overwrite staging still read by earlier work on s
     HIPCHK(hipEventRecord(e->ev_start, s));
     HIPCHK(hipStreamWaitEvent(e->copy_stream, e->ev_start, 0));
@@ -1184,6 +1206,11 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t flags, void
         TraceRange trace_range("eo.prefill.layer");
         const int b = l & 1, nb = b ^ 1;
         HIPCHK(hipStreamWaitEvent(s, e->ev_copy[b], 0));
+        TimedSet tc{};  // this layer's kernels, once its weights are in
+        if (e->timing) {
+            EOCHK(get_set(e, &tc));
+            HIPCHK(hipEventRecord(tc.ev[0], s));
+        }
         if (double_buffer && l + 1 < e->L) {
             // buffer nb was last read by layer l-1's compute
             if (l >= 1) HIPCHK(hipStreamWaitEvent(e->copy_stream, e->ev_comp[nb], 0));
@@ -1228,6 +1255,10 @@ eo_status eo_prefill(eo_engine* e, void* x_inout, int32_t T, int32_t flags, void
                                 x_inout, e->act_bf16, s, e->E);
         if (he != hipSuccess) return fail(EO_ERR_HIP, std::string("prefill layer: ") + hipGetErrorString(he));
         EOCHK(stage_done(e, s, "prefill layer (norm, route, permute, grouped FFN, combine)", l));
+        if (e->timing) {
+            HIPCHK(hipEventRecord(tc.ev[1], s));
+            e->comp_ev.push_back(tc);
+        }
         HIPCHK(hipEventRecord(e->ev_comp[b], s));
         if (!double_buffer && l + 1 < e->L) {
             HIPCHK(hipStreamWaitEvent(e->copy_stream, e->ev_comp[b], 0));
@@ -1491,6 +1522,24 @@ eo_status eo_kernel_times(eo_engine* e, double* ms, int64_t* launches, int32_t r
     if (reset) {
         for (double& v : e->kms) v = 0;
         e->gemv_n = e->gemm_n = e->fill_n = 0;
+    }
+    return EO_OK;
+}
+
+eo_status eo_stream_times(eo_engine* e, double* ms, int64_t* layers, int32_t reset) {
+    if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
+    EOCHK(harvest_times(e));
+    if (ms) {
+        ms[0] = e->sms[0];
+        ms[1] = e->sms[1];
+    }
+    if (layers) {
+        layers[0] = e->copy_n;
+        layers[1] = e->comp_n;
+    }
+    if (reset) {
+        e->sms[0] = e->sms[1] = 0;
+        e->copy_n = e->comp_n = 0;
     }
     return EO_OK;
 }

@@ -352,6 +352,18 @@ eo_status eo_stats_get(eo_engine* e, eo_stats* out);
  * be NULL; reset != 0 clears after reading. Synchronises on the events. */
 eo_status eo_kernel_times(eo_engine* e, double* ms /*[5]*/, int64_t* launches /*[3]*/,
                           int32_t reset);
+/* Prefill streaming, copy against compute (zhichai.net article, section 2,
+ * Prefill paragraph: the next layer's weights cross PCIe while the current
+ * layer computes). While timing is enabled, eo_prefill stamps each layer's
+ * copies on the copy stream (from when the copy stream reaches them, after any
+ * wait for the staging buffer to be free) and each layer's kernels on the
+ * compute stream (from when the layer's weights are in): ms[0] the summed copy
+ * time, ms[1] the summed compute time; layers[0] / layers[1] the layers stamped
+ * on each. With double buffering the chunk takes about max(ms[0], ms[1]),
+ * without it about their sum. Either pointer may be NULL; reset != 0 clears
+ * after reading. Synchronises on the events. */
+eo_status eo_stream_times(eo_engine* e, double* ms /*[2]*/, int64_t* layers /*[2]*/,
+                          int32_t reset);
 /* Plan sizes of each lookup, recorded on the host when it reads the plan
  * (zhichai.net article, section 2, Decode paragraph: per layer call, hits are
  * served from the device, q* misses filled over PCIe, the rest run on the host;
@@ -362,7 +374,8 @@ eo_status eo_kernel_times(eo_engine* e, double* ms /*[5]*/, int64_t* launches /*
  * in *n (may be NULL). */
 eo_status eo_set_plan_log(eo_engine* e, int32_t enable);
 eo_status eo_get_plan_log(eo_engine* e, int32_t* out, int64_t cap, int64_t* n);
-/* Enable (1) or disable (0) the per-launch timing events behind eo_kernel_times. */
+/* Enable (1) or disable (0) the per-launch timing events behind eo_kernel_times
+ * and eo_stream_times. */
 eo_status eo_set_timing(eo_engine* e, int32_t enable);
 /* Size in bytes of one packed expert block (unpadded). */
 uint64_t eo_expert_bytes(int32_t hidden, int32_t inter, int32_t wfmt);

@@ -50,3 +50,14 @@ def test_gemv_counters_sha_covers_the_gemv_sources():
         assert traffic[0] is not None and 0.9 < traffic[1] < 1.2
     else:
         assert traffic == (None, None) or traffic[0] is None
+
+
+def test_prefill_overlap_efficiency_hand_worked():
+    # two chunks: 2.0 s of copies and 0.6 s of kernels in all, 1.05 s per chunk:
+    # per chunk 1.0 s copy, 0.3 s compute, efficiency 1.0 / 1.05
+    st = {"copy_ms": 2000.0, "compute_ms": 600.0, "copy_layers": 96, "compute_layers": 96}
+    ov = bench.overlap(st, 1.05, 2)
+    assert ov["copy_s"] == 1.0 and ov["compute_s"] == 0.3 and ov["chunk_s"] == 1.05
+    assert ov["efficiency"] == round(1.0 / 1.05, 4) and ov["layers_stamped"] == [96, 96]
+    # compute the longer of the two: it sets the efficiency
+    assert bench.overlap({**st, "compute_ms": 2200.0}, 1.25, 2)["efficiency"] == 0.88

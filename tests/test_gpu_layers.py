@@ -164,6 +164,46 @@ def test_prefill_per_layer(fmt, db):
         eo.eo_destroy(e)
 
 
+def test_prefill_stream_times():
+    # per-layer copy and compute stamps of a streamed prefill: every layer
+    # stamped on both streams; with double buffering the chunk is at least the
+    # longer of the two sums, without it at least their sum (the copy of layer
+    # l + 1 then waits for layer l's kernels); the events change no bits
+    import time
+    shape = small_shape("bf16", layers=4)
+    seed = 8
+    L, H, T = shape.layers, shape.hidden, 300
+    e = make_engine(shape, seed, cache_slots=0, max_tokens=T)
+    try:
+        x = dev(synth.activations(seed, 310, T, H, 1.0, True).view(np.int16))
+        outs, walls, times = [], [], []
+        for timing, db in ((False, 1), (True, 1), (True, 0)):
+            xd = x.clone()
+            eo.eo_set_timing(e, timing)
+            eo.eo_stream_times(e, reset=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            eo.eo_prefill(e, xd, T, db, _stream())
+            torch.cuda.synchronize()
+            walls.append(1e3 * (time.perf_counter() - t0))
+            times.append(eo.eo_stream_times(e, reset=True))
+            outs.append(xd.cpu().numpy())
+        eo.eo_set_timing(e, False)
+        assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+        assert times[0] == {"copy_ms": 0.0, "compute_ms": 0.0, "copy_layers": 0,
+                            "compute_layers": 0}
+        for st in times[1:]:
+            assert st["copy_layers"] == L and st["compute_layers"] == L
+            assert st["copy_ms"] > 0 and st["compute_ms"] > 0
+        layer_bytes = shape.experts * ((synth.expert_bytes(H, shape.inter, shape.fmt) + 4095)
+                                       // 4096 * 4096)
+        assert L * layer_bytes / (times[1]["copy_ms"] * 1e-3) > 1e9  # over 1 GB/s
+        assert max(times[1]["copy_ms"], times[1]["compute_ms"]) <= walls[1]
+        assert times[2]["copy_ms"] + times[2]["compute_ms"] <= walls[2]
+    finally:
+        eo.eo_destroy(e)
+
+
 def test_prefill_streaming_matches_cache_path():
     # streaming must not change the arithmetic: same layer through the cache path
     shape = small_shape("bf16", layers=1, shared=0)

@@ -82,6 +82,7 @@ struct eo_engine {
     std::vector<uint8_t*> pool;      // per layer, E * S_pad pinned bytes
     std::vector<uint8_t*> pool_dev;  // the same, as device-visible addresses
     bool fill_sdma = false;          // EO_FILL_SDMA=1: fills by hipMemcpyAsync (ablation)
+    bool fill_gemv = true;  // EO_FILL_GEMV=0: decode fills and gate/up in separate launches
     uint8_t* d_slots = nullptr;
     uint8_t* d_shared = nullptr;
     float* d_router = nullptr;
@@ -319,6 +320,8 @@ eo_status wait_plan(eo_engine* e) {
     const DevPlan* hp = e->h_plan;
     if (hp->pad != 0) {
         e->plan_pending = false;
+        if (hp->pad == 3)
+            return fail(EO_ERR_HIP, "the previous decode launch gave up waiting for its fills");
         return fail(EO_ERR_INVALID_ARG, hp->pad == 1 ? "expert id out of range in ids"
                                                      : "expert id repeated within a token");
     }
@@ -525,6 +528,27 @@ eo_status do_ffn_device(eo_engine* e, int layer, const void* x, const int32_t* i
     return EO_OK;
 }
 
+// One-token decode: the fills and the expert GEMV, in one launch that copies
+// the fills while the other experts' gate/up rows run (then the down kernel),
+// unless timing is on (the kernels are then timed apart), fills go by
+// hipMemcpyAsync, the cache is empty of slots or the tuned GEMV does not apply.
+eo_status do_fill_gemv(eo_engine* e, int layer, const int32_t* ids, const float* w,
+                       hipStream_t s) {
+    if (!e->plan_pending) return fail(EO_ERR_STATE, "no pending plan (call eo_lookup_plan first)");
+    if (e->fill_gemv && e->gemv_fast && !e->timing && !e->fill_sdma && e->C > 0 &&
+        e->plan_T == 1) {
+        hipError_t he = launch_fill_gemv(e->fmt, e->lay, slots_gw(e, layer), e->d_slots, e->d_plan,
+                                         e->pool_dev[e->plan_layer], e->S, e->S_pad, ids, w, e->k,
+                                         e->E, e->shared, e->H, e->I, e->d_u, e->act_bf16,
+                                         e->d_hgemv, e->d_yparts, e->d_state, s);
+        if (he == hipSuccess) return EO_OK;
+        if (he != hipErrorNotSupported)
+            return fail(EO_ERR_HIP, std::string("fill and GEMV: ") + hipGetErrorString(he));
+    }
+    EOCHK(do_fill(e, s));
+    return do_ffn_device(e, layer, e->d_u, ids, w, s);
+}
+
 eo_status do_combine(eo_engine* e, const int32_t* ids, float* y, void* x_res, hipStream_t s) {
     const int T = e->plan_T;
     const float* yh = e->host_staged ? (T == 1 ? e->h_yhost_dev : e->d_yhost) : nullptr;
@@ -610,10 +634,8 @@ eo_status decode_one_token(eo_engine* e, uint16_t* x_inout, const int32_t* force
         if (cap)  // u is not changed by the plan
             HIPCHK(hipMemcpyAsync((uint8_t*)e->cap_x + (size_t)l * e->cap_T * H * 2, e->d_u,
                                   (size_t)H * 2, hipMemcpyDeviceToDevice, s));
-        EOCHK(do_fill(e, s));
-        EOCHK(stage_done(e, s, "fill", l));
-        EOCHK(do_ffn_device(e, l, e->d_u, ids, w, s));
-        EOCHK(stage_done(e, s, "expert GEMV", l));
+        EOCHK(do_fill_gemv(e, l, ids, w, s));
+        EOCHK(stage_done(e, s, "fill and expert GEMV", l));
         EOCHK(do_host(e, e->d_u, ids, w, s));
         EOCHK(stage_done(e, s, "host-execute", l));
         prev_host = e->host_staged ? e->h_yhost_dev : nullptr;
@@ -782,6 +804,7 @@ eo_status create_impl(const eo_config* cfg, eo_engine* e) {
     e->tp = threadpool_create(nt);
     if (const char* v = std::getenv("EO_GEMV_FAST")) e->gemv_fast = std::atoi(v) != 0;
     if (const char* v = std::getenv("EO_FILL_SDMA")) e->fill_sdma = std::atoi(v) != 0;
+    if (const char* v = std::getenv("EO_FILL_GEMV")) e->fill_gemv = std::atoi(v) != 0;
     if (const char* v = std::getenv("EO_FUSED_ENTRY")) e->fused_entry = std::atoi(v) != 0;
     if (const char* v = std::getenv("EO_DEBUG_SYNC")) e->debug_sync = std::atoi(v) != 0;
     if (const char* v = std::getenv("EO_LOG")) e->log_level = std::atoi(v);

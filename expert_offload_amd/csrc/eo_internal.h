@@ -36,6 +36,12 @@ struct DevState {
     int32_t seq;
     int32_t frozen;  // static placement: lookups fill and evict nothing
     int32_t ticket;  // workgroups done in the fused entry + plan launch (0 between launches)
+    int32_t sync_err;  // a fill + gate/up launch gave up waiting for its fills: the next
+                       // one-token plan reports the error and clears it
+    // fill workgroups of the fill + gate/up launch that have copied what gate/up
+    // reads of the r-th filled expert; every plan sets them to 0 for the launch
+    // that follows it
+    uint32_t fill_ready[kMaxK];
 };
 
 // ---------------------------------------------------------------- launches
@@ -160,6 +166,22 @@ hipError_t launch_ffn_gemv(int fmt, const Layout& lay, GroupW gw, const DevPlan*
                            float* y_parts, hipStream_t s,
                            hipEvent_t* ev /*[4]: start/stop of each kernel, entries may be null*/,
                            int allow_fast, const GemvExperts* ex /*may be null*/);
+// One-token decode, fill and GEMV with the copies overlapped: one launch whose
+// first kFillBlocks workgroups copy the plan's fills from the layer's pool into
+// their slots (slots: gw.slots, writable; as launch_fill) while the others run
+// gate/up for every expert slot, those of a filled expert once the bytes gate/up
+// reads are in (st->fill_ready[r], which the plan set to 0, reaching
+// kFillBlocks; a bounded wait that sets st->sync_err when it runs out); then
+// the down kernel. The same arithmetic as launch_fill followed by
+// launch_ffn_gemv.
+// hipErrorNotSupported (nothing launched) where the tuned one-token GEMV does
+// not apply (activations not bf16, fp32 weights, untuned shapes).
+hipError_t launch_fill_gemv(int fmt, const Layout& lay, GroupW gw, uint8_t* slots,
+                            const DevPlan* plan, const uint8_t* pool_layer_dev, uint64_t S,
+                            uint64_t S_pad,
+                            const int32_t* ids, const float* w, int k, int E, int has_shared,
+                            int H, int I, const void* x, int act_bf16, float* h_buf,
+                            float* y_parts, DevState* st, hipStream_t s);
 // Sum of the GEMV partials (k + shared rows of [H]) plus host results; with
 // x_res, x_res = act(x_in + y) (x_in null: in place).
 hipError_t launch_gemv_reduce(const float* y_parts, int nparts, const float* y_host, int H,

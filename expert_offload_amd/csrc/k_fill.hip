@@ -10,37 +10,11 @@
 #include <hip/hip_ext.h>
 
 #include "eo_internal.h"
+#include "fill_dev.h"
 
 namespace eo {
 
 namespace {
-
-constexpr int kFillBlocks = 64;
-constexpr int kFillUnroll = 4;
-
-// This workgroup's share of one S-byte copy (grid-stride over 16-byte words).
-__device__ __forceinline__ void copy_block(const uint8_t* __restrict__ src8,
-                                           uint8_t* __restrict__ dst8, uint64_t S) {
-    const uint4* src = (const uint4*)src8;
-    uint4* dst = (uint4*)dst8;
-    const uint64_t n16 = S / 16;
-    const uint64_t step = (uint64_t)gridDim.x * 256 * kFillUnroll;
-    for (uint64_t b = (uint64_t)blockIdx.x * 256 * kFillUnroll + threadIdx.x; b < n16; b += step) {
-        uint4 v[kFillUnroll];
-#pragma unroll
-        for (int u = 0; u < kFillUnroll; ++u) {
-            const uint64_t i = b + (uint64_t)u * 256;
-            if (i < n16) v[u] = src[i];
-        }
-#pragma unroll
-        for (int u = 0; u < kFillUnroll; ++u) {
-            const uint64_t i = b + (uint64_t)u * 256;
-            if (i < n16) dst[i] = v[u];
-        }
-    }
-    const uint64_t tail = S - n16 * 16;
-    if (blockIdx.x == 0 && threadIdx.x < tail) dst8[n16 * 16 + threadIdx.x] = src8[n16 * 16 + threadIdx.x];
-}
 
 __global__ __launch_bounds__(256) void k_fill(const DevPlan* __restrict__ plan,
                                               const uint8_t* __restrict__ pool,
@@ -50,13 +24,13 @@ __global__ __launch_bounds__(256) void k_fill(const DevPlan* __restrict__ plan,
     const int q = plan->q_fill;
     for (int r = 0; r < q; ++r)
         copy_block(pool + (uint64_t)plan->fill_e[r] * S_pad,
-                   slots + (uint64_t)plan->fill_slot[r] * S_pad, S);
+                   slots + (uint64_t)plan->fill_slot[r] * S_pad, S, blockIdx.x, gridDim.x);
 }
 
 // One expert, the fill kernel's way (the B_P probe).
 __global__ __launch_bounds__(256) void k_copy_expert(const uint8_t* __restrict__ src,
                                                      uint8_t* __restrict__ dst, uint64_t S) {
-    copy_block(src, dst, S);
+    copy_block(src, dst, S, blockIdx.x, gridDim.x);
 }
 
 }  // namespace

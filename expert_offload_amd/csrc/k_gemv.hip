@@ -17,6 +17,7 @@
 #include "decode_dev.h"
 #include "dev_common.h"
 #include "eo_internal.h"
+#include "fill_dev.h"
 
 namespace eo {
 
@@ -376,10 +377,12 @@ __device__ __forceinline__ void rows_dot(const uint8_t* data, const uint8_t* sca
         for (int s = G / 2; s >= 1; s >>= 1) out[r] += __shfl_xor(out[r], s, 64);
 }
 
+// Gate/up rows of workgroup `bidx`: expert slot bidx / nA_per, row block bidx % nA_per.
 template <int FMT, int GA, int NCA, int RA>
-__global__ __launch_bounds__(256) void k_gemv_gu(GemvArgs a, uint16_t* __restrict__ hb, int nA_per) {
+__device__ __forceinline__ void gu_body(const GemvArgs& a, uint16_t* __restrict__ hb, int nA_per,
+                                        int bidx) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int j = blockIdx.x / nA_per, blk = blockIdx.x % nA_per;
+    const int j = bidx / nA_per, blk = bidx % nA_per;
     const uint8_t* wb = expert_base(a, j);
     if (!wb) return;
     const int grp = lane / GA, gl = lane % GA;
@@ -408,6 +411,90 @@ __global__ __launch_bounds__(256) void k_gemv_gu(GemvArgs a, uint16_t* __restric
             hb[(size_t)j * a.I + r0 + r] = (uint16_t)f32_bf16_rne(silu_f32(g) * u);
         }
     }
+}
+
+template <int FMT, int GA, int NCA, int RA>
+__global__ __launch_bounds__(256) void k_gemv_gu(GemvArgs a, uint16_t* __restrict__ hb, int nA_per) {
+    gu_body<FMT, GA, NCA, RA>(a, hb, nA_per, blockIdx.x);
+}
+
+// The fills of a one-token call and the gate/up rows in one launch.
+struct FillSync {
+    const uint8_t* pool;  // the layer's pinned pool, device-visible
+    uint8_t* slots;       // the cache slots the fills write (the GEMV's gw.slots)
+    uint64_t S_pad;
+    uint32_t* ready;  // [kMaxK]: fill workgroups done with the r-th fill's gate/up bytes
+    int32_t* err;     // set when a wait for the fills runs out
+};
+
+// Longest wait for the fills: 1 s of the device's 100 MHz wall clock (the fills
+// of one call take a few ms at most).
+constexpr uint64_t kFillWaitTicks = 100000000ull;
+
+// Rank among this call's fills of a one-token plan's expert slot j, or -1.
+__device__ __forceinline__ int fill_rank(const DevPlan* p, int j, int k) {
+    if (j >= k || p->pad != 0) return -1;
+    const int sl = p->tok_slot[j];
+    int rank = -1;
+    for (int r = 0; r < p->q_fill; ++r)
+        if (p->fill_slot[r] == sl) rank = r;
+    return sl >= 0 ? rank : -1;
+}
+
+// Workgroups [0, kFillBlocks) copy the fills as the fill kernel does, in two
+// passes: first, for each filled expert, the bytes gate/up reads (its weights,
+// their scales and the global scales), released at device scope (the counter's
+// increment carries the release: the L2 lines written are written back) and
+// counted; then the down projection's bytes, which the next launch reads. The
+// other workgroups run gate/up; those of a filled expert first wait for its
+// counter to reach kFillBlocks (lower workgroup ids, dispatched first: the wait
+// ends), then acquire at device scope before they read the slot, while the
+// fill workgroups copy the down rows.
+template <int FMT, int GA, int NCA, int RA>
+__global__ __launch_bounds__(256) void k_fill_gu(GemvArgs a, uint16_t* __restrict__ hb, int nA_per,
+                                                 FillSync f) {
+    if ((int)blockIdx.x < kFillBlocks) {
+        const DevPlan* p = a.plan;
+        const int q = p->pad == 0 ? p->q_fill : 0;
+        const Layout& L = a.lay;
+        const int part = blockIdx.x;
+        for (int r = 0; r < q; ++r) {
+            const uint8_t* src = f.pool + (uint64_t)p->fill_e[r] * f.S_pad;
+            uint8_t* dst = f.slots + (uint64_t)p->fill_slot[r] * f.S_pad;
+            copy_block(src + L.d13, dst + L.d13, L.d2 - L.d13, part, kFillBlocks);
+            copy_block(src + L.s13, dst + L.s13, L.s2 - L.s13, part, kFillBlocks);
+            copy_block(src + L.gl, dst + L.gl, L.bytes - L.gl, part, kFillBlocks);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's stores have completed
+            __syncthreads();
+            if (threadIdx.x == 0)
+                __hip_atomic_fetch_add(&f.ready[r], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        for (int r = 0; r < q; ++r) {
+            const uint8_t* src = f.pool + (uint64_t)p->fill_e[r] * f.S_pad;
+            uint8_t* dst = f.slots + (uint64_t)p->fill_slot[r] * f.S_pad;
+            copy_block(src + L.d2, dst + L.d2, L.s13 - L.d2, part, kFillBlocks);
+            copy_block(src + L.s2, dst + L.s2, L.gl - L.s2, part, kFillBlocks);
+        }
+        return;
+    }
+    const int bidx = blockIdx.x - kFillBlocks;
+    const int r = fill_rank(a.plan, bidx / nA_per, a.k);  // workgroup-uniform
+    if (r >= 0) {
+        if (threadIdx.x == 0) {
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            while (__hip_atomic_load(&f.ready[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                   (uint32_t)kFillBlocks) {
+                if (__builtin_amdgcn_s_memrealtime() - t0 > kFillWaitTicks) {
+                    __hip_atomic_store(f.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(16);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        __syncthreads();
+    }
+    gu_body<FMT, GA, NCA, RA>(a, hb, nA_per, bidx);
 }
 
 template <int FMT, int GB, int NCB, int RB>
@@ -454,12 +541,17 @@ bool split_rows(int nch, int* G, int* NC) {
 }
 
 template <int FMT, int GA, int NCA, int RA, int GB, int NCB, int RB>
-hipError_t run_fast(const GemvArgs& a, uint16_t* hb, hipStream_t s, hipEvent_t* ev) {
+hipError_t run_fast(const GemvArgs& a, uint16_t* hb, hipStream_t s, hipEvent_t* ev,
+                    const FillSync* fill) {
     const int rowsA = 4 * (64 / GA) * RA, rowsB = 4 * (64 / GB) * RB;
     if (a.I % rowsA || a.H % rowsB) return hipErrorNotSupported;
     const int nA_per = a.I / rowsA, nB_per = a.H / rowsB;
-    hipExtLaunchKernelGGL(k_gemv_gu<FMT, GA, NCA, RA>, dim3(a.nexp * nA_per), dim3(256), 0, s,
-                          ev[0], ev[1], 0, a, hb, nA_per);
+    if (fill)
+        hipExtLaunchKernelGGL(k_fill_gu<FMT, GA, NCA, RA>, dim3(kFillBlocks + a.nexp * nA_per),
+                              dim3(256), 0, s, ev[0], ev[1], 0, a, hb, nA_per, *fill);
+    else
+        hipExtLaunchKernelGGL(k_gemv_gu<FMT, GA, NCA, RA>, dim3(a.nexp * nA_per), dim3(256), 0, s,
+                              ev[0], ev[1], 0, a, hb, nA_per);
     hipExtLaunchKernelGGL(k_gemv_dn<FMT, GB, NCB, RB>, dim3(a.nexp * nB_per), dim3(256), 0, s,
                           ev[2], ev[3], 0, a, (const uint16_t*)hb, nB_per);
     return hipGetLastError();
@@ -467,14 +559,15 @@ hipError_t run_fast(const GemvArgs& a, uint16_t* hb, hipStream_t s, hipEvent_t* 
 
 // Shapes with a tuned instantiation: (GA, NCA) from H, (GB, NCB) from I.
 template <int FMT>
-hipError_t fast_dispatch(const GemvArgs& a, uint16_t* hb, hipStream_t s, hipEvent_t* ev) {
+hipError_t fast_dispatch(const GemvArgs& a, uint16_t* hb, hipStream_t s, hipEvent_t* ev,
+                         const FillSync* fill = nullptr) {
     constexpr int N = FastC<FMT>::n;
     int GA, NCA, GB, NCB;
     if (a.H % N || a.I % N || !split_rows(a.H / N, &GA, &NCA) || !split_rows(a.I / N, &GB, &NCB))
         return hipErrorNotSupported;
 #define EO_FAST(ga, nca, ra, gb, ncb, rb)                         \
     if (GA == ga && NCA == nca && GB == gb && NCB == ncb)         \
-        return run_fast<FMT, ga, nca, ra, gb, ncb, rb>(a, hb, s, ev);
+        return run_fast<FMT, ga, nca, ra, gb, ncb, rb>(a, hb, s, ev, fill);
     EO_FAST(64, 4, 1, 32, 3, 1)  // bf16 H 2048, I 768
     EO_FAST(64, 1, 4, 32, 1, 4)  // bf16 H 512, I 256
     EO_FAST(32, 1, 4, 16, 1, 4)  // fp8 H 512, I 256
@@ -543,6 +636,41 @@ hipError_t launch_ffn_gemv(int fmt, const Layout& lay, GroupW gw, const DevPlan*
         }
     }
     return hipGetLastError();
+}
+
+hipError_t launch_fill_gemv(int fmt, const Layout& lay, GroupW gw, uint8_t* slots,
+                            const DevPlan* plan, const uint8_t* pool_layer_dev, uint64_t S,
+                            uint64_t S_pad,
+                            const int32_t* ids, const float* w, int k, int E, int has_shared,
+                            int H, int I, const void* x, int act_bf16, float* h_buf,
+                            float* y_parts, DevState* st, hipStream_t s) {
+    if (!act_bf16) return hipErrorNotSupported;
+    GemvArgs a{};
+    a.gw = gw;
+    a.lay = lay;
+    a.plan = plan;
+    a.ids = ids;
+    a.w = w;
+    a.k = k;
+    a.E = E;
+    a.H = H;
+    a.I = I;
+    a.nexp = k + (has_shared ? 1 : 0);
+    a.x = x;
+    a.h = h_buf;
+    a.yp = y_parts;
+    if (slots != gw.slots) return hipErrorInvalidValue;
+    if (lay.bytes != S) return hipErrorInvalidValue;
+    const FillSync f{pool_layer_dev, slots, S_pad, st->fill_ready, &st->sync_err};
+    uint16_t* hb = (uint16_t*)h_buf;
+    hipEvent_t none[4] = {nullptr, nullptr, nullptr, nullptr};
+    switch (fmt) {
+    case EO_W_BF16: return fast_dispatch<EO_W_BF16>(a, hb, s, none, &f);
+    case EO_W_FP8: return fast_dispatch<EO_W_FP8>(a, hb, s, none, &f);
+    case EO_W_MXFP4: return fast_dispatch<EO_W_MXFP4>(a, hb, s, none, &f);
+    case EO_W_NVFP4: return fast_dispatch<EO_W_NVFP4>(a, hb, s, none, &f);
+    default: return hipErrorNotSupported;
+    }
 }
 
 hipError_t launch_gemv_reduce(const float* y_parts, int nparts, const float* y_host, int H,

@@ -210,6 +210,7 @@ __global__ __launch_bounds__(kThreads) void k_plan(
         if (tid == 0) {
             int seq = s_seq0 + 1;
             st->seq = seq;
+            for (int i = 0; i < kMaxK; ++i) st->fill_ready[i] = 0;  // for the launch after the plan
             dp->pad = s_err;
             hp->pad = s_err;
             dp->seq = seq;
@@ -394,6 +395,7 @@ __global__ __launch_bounds__(kThreads) void k_plan(
     if (tid == 0) {
         int seq = s_seq0 + 1;
         st->seq = seq;
+        for (int i = 0; i < kMaxK; ++i) st->fill_ready[i] = 0;  // for the launch after the plan
         dp->seq = seq;
         __threadfence_system();
         __hip_atomic_store(&hp->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -473,7 +475,7 @@ __device__ __forceinline__ void plan1_body(
 #pragma unroll
         for (int i = 0; i < kRowPer; ++i) k2[i] = key2slot[layer * E + min(lane + 64 * i, E - 1)];
         long long c0 = 0, c1 = 0;
-        int v0 = 0, v1 = 0, v2 = 0, v3 = 0;
+        int v0 = 0, v1 = 0, v2 = 0, v3 = 0, v4 = 0;
         if (lane == 0) {
             c0 = st->clock;
             c1 = st->credit;
@@ -481,6 +483,7 @@ __device__ __forceinline__ void plan1_body(
             v1 = st->bh;
             v2 = st->seq;
             v3 = st->frozen;
+            v4 = st->sync_err;
         }
         if (rt.z) {
             topk_token<true>(rt.z, E, k, rt.forced, s_ids, s_w);
@@ -498,7 +501,7 @@ __device__ __forceinline__ void plan1_body(
             s_bh = v1;
             s_seq0 = v2;
             s_frozen = v3;
-            s_err = 0;
+            s_err = v4 ? 3 : 0;
         }
     } else {
         const int lt = tid - 64;
@@ -541,8 +544,9 @@ __device__ __forceinline__ void plan1_body(
         for (int jj = 0; jj < k; ++jj) dup |= jj < lane && __builtin_amdgcn_readlane(e, jj) == e;
         dup = dup && act && !bad;
         const uint64_t mbad = __ballot(bad), mdup = __ballot(dup);
-        if (mbad | mdup) {
-            if (lane == 0) s_err = mbad ? 1 : 2;
+        const bool late = s_err == 3;  // the previous call's decode launch lost its fills
+        if (late || (mbad | mdup)) {
+            if (lane == 0) s_err = late ? 3 : mbad ? 1 : 2;
         } else {
             slot = act ? s_k2s[e] : -1;
             hit = act && slot >= 0;
@@ -577,6 +581,8 @@ __device__ __forceinline__ void plan1_body(
         if (tid == 0) {
             const int seq = s_seq0 + 1;
             st->seq = seq;
+            for (int i = 0; i < kMaxK; ++i) st->fill_ready[i] = 0;  // for the launch after the plan
+            if (s_err == 3) st->sync_err = 0;
             dp->pad = s_err;
             hp->pad = s_err;
             dp->seq = seq;
@@ -730,6 +736,7 @@ __device__ __forceinline__ void plan1_body(
     if (tid == 0) {
         const int seq = s_seq0 + 1;
         st->seq = seq;
+        for (int i = 0; i < kMaxK; ++i) st->fill_ready[i] = 0;  // for the launch after the plan
         dp->seq = seq;
         __threadfence_system();
         __hip_atomic_store(&hp->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);

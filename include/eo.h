@@ -259,14 +259,22 @@ eo_status eo_moe_layer(eo_engine* e, int32_t layer, const void* x, float* y, int
  * + 1e-6) per token (stored in the activation dtype; a parameter-free RMS
  * normalisation, as in pre-norm transformer blocks) and r_{l+1} = r_l + y_l(u_l)
  * (stored in the activation dtype). forced_ids: device [L, T, k] or NULL.
- * One token with bf16 activations runs four kernels per layer and no host wait
+ * One token with bf16 activations runs three kernels per layer and no host wait
  * between layers other than the plan readback for the host-list experts:
- * layer entry + plan (one launch), fill, gate/up GEMV, down GEMV. The results
+ * layer entry + plan (one launch); the fills and the gate/up GEMV (one launch:
+ * 64 workgroups copy the fills, the gate/up bytes of each filled expert first,
+ * while the others run the gate/up rows, a filled expert's once its bytes are
+ * in); the down GEMV. Should a gate/up workgroup's wait for those bytes run
+ * out (1 s), the next one-token plan returns EO_ERR_HIP and changes nothing.
+ * The results
  * do not depend on which kernels run; the environment switches EO_ENTRY_PLAN=0
  * (entry and plan as two launches), EO_PLAN1=0 (the general plan kernel for
  * one token), EO_FUSED_ENTRY=0 (separate norm, router and top-k kernels, read
- * at engine creation) and EO_GEMV_FAST=0 (the generic GEMV, read at engine
- * creation) select the alternatives that the tests compare. */
+ * at engine creation), EO_GEMV_FAST=0 (the generic GEMV, read at engine
+ * creation) and EO_FILL_GEMV=0 (fill kernel and gate/up GEMV as two launches,
+ * read at engine creation; also the case while timing is enabled, so that the
+ * kernel times stay those of each kernel alone) select the alternatives that the
+ * tests compare. */
 eo_status eo_decode_step(eo_engine* e, void* x_inout, int32_t T, const int32_t* forced_ids,
                          void* stream);
 
@@ -375,7 +383,8 @@ eo_status eo_stream_times(eo_engine* e, double* ms /*[2]*/, int64_t* layers /*[2
 eo_status eo_set_plan_log(eo_engine* e, int32_t enable);
 eo_status eo_get_plan_log(eo_engine* e, int32_t* out, int64_t cap, int64_t* n);
 /* Enable (1) or disable (0) the per-launch timing events behind eo_kernel_times
- * and eo_stream_times. */
+ * and eo_stream_times. While enabled, a decode step launches the fill kernel
+ * and the gate/up GEMV apart, so that each is timed alone. */
 eo_status eo_set_timing(eo_engine* e, int32_t enable);
 /* Size in bytes of one packed expert block (unpadded). */
 uint64_t eo_expert_bytes(int32_t hidden, int32_t inter, int32_t wfmt);

@@ -261,7 +261,7 @@ def test_decode_stack_against_oracle_chain(fmt):
         eo.eo_destroy(e)
 
 
-def _decode_capture(shape, seed, steps, forced, env, cache_slots=7):
+def _decode_capture(shape, seed, steps, forced, env, cache_slots=7, bw=(3, 5)):
     """Decode `steps` tokens on a fresh engine with EO_FUSED_ENTRY=env (a string)
     or with the variables of env (a dict) set throughout; returns the final
     streams, every capture as bytes, the statistics and the cache snapshot."""
@@ -271,7 +271,7 @@ def _decode_capture(shape, seed, steps, forced, env, cache_slots=7):
     saved = {v: os.environ.get(v) for v in env}
     os.environ.update(env)
     try:
-        return _decode_capture_run(shape, seed, steps, forced, cache_slots)
+        return _decode_capture_run(shape, seed, steps, forced, cache_slots, bw)
     finally:
         for v, old in saved.items():
             if old is None:
@@ -280,12 +280,12 @@ def _decode_capture(shape, seed, steps, forced, env, cache_slots=7):
                 os.environ[v] = old
 
 
-def _decode_capture_run(shape, seed, steps, forced, cache_slots):
+def _decode_capture_run(shape, seed, steps, forced, cache_slots, bw):
     L, k, H = shape.layers, shape.top_k, shape.hidden
     e = make_engine(shape, seed, cache_slots=cache_slots, max_tokens=1)
     out = []
     try:
-        eo.eo_set_bandwidth(e, 3, 5)
+        eo.eo_set_bandwidth(e, *bw)
         tr = synth.sticky_zipf_trace(seed, steps, L, shape.experts, k)
         cx = torch.zeros((L, 1, H), dtype=torch.int16, device="cuda")
         cy = torch.zeros((L, 1, H), dtype=torch.float32, device="cuda")
@@ -336,6 +336,38 @@ def test_decode_entry_and_plan_in_one_launch_long_run():
     steps = 150
     a = _decode_capture(shape, 31, steps, False, {"EO_ENTRY_PLAN": "1"}, shape.cache_slots)
     b = _decode_capture(shape, 31, steps, False, {"EO_ENTRY_PLAN": "0"}, shape.cache_slots)
+    for s in range(steps):
+        for i in range(1, 6):
+            assert np.array_equal(a[s][i], b[s][i]), (s, i)
+    assert a[-2:] == b[-2:]
+    assert a[-2]["fills"] > 0 and a[-2]["host_experts"] > 0
+
+
+@pytest.mark.parametrize("bw", [(3, 5), (1, 1)])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4", "nvfp4"])
+def test_decode_fill_and_gate_up_in_one_launch(fmt, bw):
+    # the one launch that copies a call's fills while the other experts'
+    # gate/up rows run (a filled expert's rows once the bytes they read are in)
+    # gives the bits of the fill kernel followed by the GEMV kernels: every
+    # capture, the counters and the slot table; B_P = B_H fills every miss the
+    # capacity allows (several fills per call)
+    shape = small_shape(fmt, layers=3)
+    a = _decode_capture(shape, 17, 8, False, {"EO_FILL_GEMV": "1"}, 7, bw)
+    b = _decode_capture(shape, 17, 8, False, {"EO_FILL_GEMV": "0"}, 7, bw)
+    for s in range(8):
+        for i in range(1, 6):
+            assert np.array_equal(a[s][i], b[s][i]), (s, i)
+    assert a[-2:] == b[-2:]
+    assert a[-2]["fills"] > 0 and (a[-2]["host_experts"] > 0) == (bw != (1, 1))
+
+
+def test_decode_fill_and_gate_up_in_one_launch_long_run():
+    # the same at the benchmark's layer shape over 1200 layer calls
+    base = synth.SHAPES["decode_bf16_48L"]
+    shape = dataclasses.replace(base, layers=8, cache_slots=int(0.37 * 8 * base.experts))
+    steps = 150
+    a = _decode_capture(shape, 33, steps, False, {"EO_FILL_GEMV": "1"}, shape.cache_slots)
+    b = _decode_capture(shape, 33, steps, False, {"EO_FILL_GEMV": "0"}, shape.cache_slots)
     for s in range(steps):
         for i in range(1, 6):
             assert np.array_equal(a[s][i], b[s][i]), (s, i)

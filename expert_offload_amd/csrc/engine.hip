@@ -83,6 +83,10 @@ struct eo_engine {
     std::vector<uint8_t*> pool_dev;  // the same, as device-visible addresses
     bool fill_sdma = false;          // EO_FILL_SDMA=1: fills by hipMemcpyAsync (ablation)
     bool fill_gemv = true;  // EO_FILL_GEMV=0: decode fills and gate/up in separate launches
+    // longest wait of a filled expert's gate/up rows for its bytes: 1 s of the
+    // device's 100 MHz clock (EO_TEST_FILL_WAIT_TICKS sets it, for the test of
+    // the path where the wait runs out)
+    uint64_t fill_wait_ticks = 100000000ull;
     uint8_t* d_slots = nullptr;
     uint8_t* d_shared = nullptr;
     float* d_router = nullptr;
@@ -540,7 +544,8 @@ eo_status do_fill_gemv(eo_engine* e, int layer, const int32_t* ids, const float*
         hipError_t he = launch_fill_gemv(e->fmt, e->lay, slots_gw(e, layer), e->d_slots, e->d_plan,
                                          e->pool_dev[e->plan_layer], e->S, e->S_pad, ids, w, e->k,
                                          e->E, e->shared, e->H, e->I, e->d_u, e->act_bf16,
-                                         e->d_hgemv, e->d_yparts, e->d_state, s);
+                                         e->d_hgemv, e->d_yparts, e->d_state,
+                                         e->fill_wait_ticks, s);
         if (he == hipSuccess) return EO_OK;
         if (he != hipErrorNotSupported)
             return fail(EO_ERR_HIP, std::string("fill and GEMV: ") + hipGetErrorString(he));
@@ -805,6 +810,7 @@ eo_status create_impl(const eo_config* cfg, eo_engine* e) {
     if (const char* v = std::getenv("EO_GEMV_FAST")) e->gemv_fast = std::atoi(v) != 0;
     if (const char* v = std::getenv("EO_FILL_SDMA")) e->fill_sdma = std::atoi(v) != 0;
     if (const char* v = std::getenv("EO_FILL_GEMV")) e->fill_gemv = std::atoi(v) != 0;
+    if (const char* v = std::getenv("EO_TEST_FILL_WAIT_TICKS")) e->fill_wait_ticks = std::strtoull(v, nullptr, 10);
     if (const char* v = std::getenv("EO_FUSED_ENTRY")) e->fused_entry = std::atoi(v) != 0;
     if (const char* v = std::getenv("EO_DEBUG_SYNC")) e->debug_sync = std::atoi(v) != 0;
     if (const char* v = std::getenv("EO_LOG")) e->log_level = std::atoi(v);

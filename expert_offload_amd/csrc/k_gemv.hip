@@ -425,11 +425,8 @@ struct FillSync {
     uint64_t S_pad;
     uint32_t* ready;  // [kMaxK]: fill workgroups done with the r-th fill's gate/up bytes
     int32_t* err;     // set when a wait for the fills runs out
+    uint64_t wait_ticks;  // longest wait, in ticks of the device's 100 MHz wall clock
 };
-
-// Longest wait for the fills: 1 s of the device's 100 MHz wall clock (the fills
-// of one call take a few ms at most).
-constexpr uint64_t kFillWaitTicks = 100000000ull;
 
 // Rank among this call's fills of a one-token plan's expert slot j, or -1.
 __device__ __forceinline__ int fill_rank(const DevPlan* p, int j, int k) {
@@ -484,7 +481,7 @@ __global__ __launch_bounds__(256) void k_fill_gu(GemvArgs a, uint16_t* __restric
             const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
             while (__hip_atomic_load(&f.ready[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
                    (uint32_t)kFillBlocks) {
-                if (__builtin_amdgcn_s_memrealtime() - t0 > kFillWaitTicks) {
+                if (__builtin_amdgcn_s_memrealtime() - t0 > f.wait_ticks) {
                     __hip_atomic_store(f.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
@@ -643,7 +640,8 @@ hipError_t launch_fill_gemv(int fmt, const Layout& lay, GroupW gw, uint8_t* slot
                             uint64_t S_pad,
                             const int32_t* ids, const float* w, int k, int E, int has_shared,
                             int H, int I, const void* x, int act_bf16, float* h_buf,
-                            float* y_parts, DevState* st, hipStream_t s) {
+                            float* y_parts, DevState* st, uint64_t wait_ticks,
+                            hipStream_t s) {
     if (!act_bf16) return hipErrorNotSupported;
     GemvArgs a{};
     a.gw = gw;
@@ -661,7 +659,7 @@ hipError_t launch_fill_gemv(int fmt, const Layout& lay, GroupW gw, uint8_t* slot
     a.yp = y_parts;
     if (slots != gw.slots) return hipErrorInvalidValue;
     if (lay.bytes != S) return hipErrorInvalidValue;
-    const FillSync f{pool_layer_dev, slots, S_pad, st->fill_ready, &st->sync_err};
+    const FillSync f{pool_layer_dev, slots, S_pad, st->fill_ready, &st->sync_err, wait_ticks};
     uint16_t* hb = (uint16_t*)h_buf;
     hipEvent_t none[4] = {nullptr, nullptr, nullptr, nullptr};
     switch (fmt) {

@@ -265,7 +265,9 @@ eo_status eo_moe_layer(eo_engine* e, int32_t layer, const void* x, float* y, int
  * 64 workgroups copy the fills, the gate/up bytes of each filled expert first,
  * while the others run the gate/up rows, a filled expert's once its bytes are
  * in); the down GEMV. Should a gate/up workgroup's wait for those bytes run
- * out (1 s), the next one-token plan returns EO_ERR_HIP and changes nothing.
+ * out (1 s; EO_TEST_FILL_WAIT_TICKS=n at engine creation sets it to n ticks of
+ * the device's 100 MHz clock, for tests of this path), the next one-token plan
+ * returns EO_ERR_HIP and changes nothing.
  * The results
  * do not depend on which kernels run; the environment switches EO_ENTRY_PLAN=0
  * (entry and plan as two launches), EO_PLAN1=0 (the general plan kernel for

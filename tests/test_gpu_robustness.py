@@ -10,6 +10,12 @@
 * An empty batch (T = 0) or one above max_tokens is rejected by every step call
   with EO_ERR_INVALID_ARG before any launch: buffers untouched, cache, clock,
   credit and statistics unchanged, and the next calls match the oracle.
+* A filled expert's gate/up rows wait, bounded, for the fill workgroups of the
+  same launch. With the bound forced to one tick from the host
+  (EO_TEST_FILL_WAIT_TICKS) the wait runs out at once; no kernel faults or
+  hangs, the launch records it, and the next one-token plan returns EO_ERR_HIP
+  and changes nothing (the clock stays at the last plan read); the record is
+  cleared and the next layer call matches the oracle.
 """
 import numpy as np
 import pytest
@@ -164,6 +170,41 @@ def test_empty_and_oversized_batches_are_rejected():
         rids, rw, _ = OR.route(xf, synth.router_weights(seed, 1, shape.experts, H), k)
         assert rel_err(y2.cpu().numpy(), oracle_layer(shape, seed, 1, xf, rids, rw)) <= 2e-2
         assert eo.eo_last_plan(e)["clock"] == snap0[0] + 1
+        eo.eo_sync(e)
+    finally:
+        eo.eo_destroy(e)
+
+
+def test_fill_wait_that_runs_out_fails_the_next_plan(monkeypatch):
+    shape = synth.LayerShape("fw_bf16", "test", 512, 16, 4, 256, 3, synth.FMT_BF16, 8, 6,
+                             shared=1)
+    seed = 49
+    H, k, C = shape.hidden, shape.top_k, shape.cache_slots
+    monkeypatch.setenv("EO_TEST_FILL_WAIT_TICKS", "1")
+    e = make_engine(shape, seed, max_tokens=8)
+    monkeypatch.delenv("EO_TEST_FILL_WAIT_TICKS")
+    try:
+        eo.eo_set_bandwidth(e, 1, 1)  # every miss filled: layer 0 of the first step fills k
+        x = dev(synth.activations(seed, 100, 1, H, 1.0, True).view(np.int16))
+        with pytest.raises(eo.EOError) as ex:
+            eo.eo_decode_step(e, x, 1, None, _s())
+        assert ex.value.status == eo.EO_ERR_HIP and "gave up waiting for its fills" in str(ex.value)
+        torch.cuda.synchronize()
+        keys = np.zeros(C, dtype=np.int32)
+        stamps = np.zeros(C, dtype=np.int64)
+        snap = eo.eo_cache_snapshot(e, keys, stamps)
+        st = eo.eo_stats_get(e)
+        # layer 0's plan was read (k fills); layer 1's plan reported the error and ticked nothing
+        assert snap[0] == 1 == eo.eo_last_plan(e)["clock"] == st["lookups"]
+        assert st["fills"] == k and int((keys >= 0).sum()) == k
+        x2 = synth.activations(seed, 3, 8, H, 1.0, True)
+        y2 = torch.zeros((8, H), dtype=torch.float32, device="cuda")
+        eo.eo_moe_layer(e, 1, dev(x2.view(np.int16)), y2, 8, None, _s())
+        torch.cuda.synchronize()
+        xf = synth.bf16_bits_to_f32(x2)
+        rids, rw, _ = OR.route(xf, synth.router_weights(seed, 1, shape.experts, H), k)
+        assert rel_err(y2.cpu().numpy(), oracle_layer(shape, seed, 1, xf, rids, rw)) <= 2e-2
+        assert eo.eo_last_plan(e)["clock"] == 2
         eo.eo_sync(e)
     finally:
         eo.eo_destroy(e)

@@ -14,7 +14,10 @@ constexpr int kFillBlocks = 64;
 constexpr int kFillUnroll = 4;
 
 // Workgroup `part` of `nparts`: its share of one S-byte copy (grid-stride over
-// 16-byte words).
+// 16-byte words). CLAMP: the reads take indexes clamped to the last word
+// instead of a bounds check (only the stores are checked), which keeps the
+// words in registers where the bounds-checked form would stage them in scratch.
+template <bool CLAMP = false>
 __device__ __forceinline__ void copy_block(const uint8_t* __restrict__ src8,
                                            uint8_t* __restrict__ dst8, uint64_t S, int part,
                                            int nparts) {
@@ -27,7 +30,10 @@ __device__ __forceinline__ void copy_block(const uint8_t* __restrict__ src8,
 #pragma unroll
         for (int u = 0; u < kFillUnroll; ++u) {
             const uint64_t i = b + (uint64_t)u * 256;
-            if (i < n16) v[u] = src[i];
+            if (CLAMP)
+                v[u] = src[i < n16 ? i : n16 - 1];
+            else if (i < n16)
+                v[u] = src[i];
         }
 #pragma unroll
         for (int u = 0; u < kFillUnroll; ++u) {

@@ -458,9 +458,9 @@ __global__ __launch_bounds__(256) void k_fill_gu(GemvArgs a, uint16_t* __restric
         for (int r = 0; r < q; ++r) {
             const uint8_t* src = f.pool + (uint64_t)p->fill_e[r] * f.S_pad;
             uint8_t* dst = f.slots + (uint64_t)p->fill_slot[r] * f.S_pad;
-            copy_block(src + L.d13, dst + L.d13, L.d2 - L.d13, part, kFillBlocks);
-            copy_block(src + L.s13, dst + L.s13, L.s2 - L.s13, part, kFillBlocks);
-            copy_block(src + L.gl, dst + L.gl, L.bytes - L.gl, part, kFillBlocks);
+            copy_block<true>(src + L.d13, dst + L.d13, L.d2 - L.d13, part, kFillBlocks);
+            copy_block<true>(src + L.s13, dst + L.s13, L.s2 - L.s13, part, kFillBlocks);
+            copy_block<true>(src + L.gl, dst + L.gl, L.bytes - L.gl, part, kFillBlocks);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's stores have completed
             __syncthreads();
             if (threadIdx.x == 0)
@@ -469,8 +469,8 @@ __global__ __launch_bounds__(256) void k_fill_gu(GemvArgs a, uint16_t* __restric
         for (int r = 0; r < q; ++r) {
             const uint8_t* src = f.pool + (uint64_t)p->fill_e[r] * f.S_pad;
             uint8_t* dst = f.slots + (uint64_t)p->fill_slot[r] * f.S_pad;
-            copy_block(src + L.d2, dst + L.d2, L.s13 - L.d2, part, kFillBlocks);
-            copy_block(src + L.s2, dst + L.s2, L.gl - L.s2, part, kFillBlocks);
+            copy_block<true>(src + L.d2, dst + L.d2, L.s13 - L.d2, part, kFillBlocks);
+            copy_block<true>(src + L.s2, dst + L.s2, L.gl - L.s2, part, kFillBlocks);
         }
         return;
     }

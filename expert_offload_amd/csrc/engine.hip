@@ -1039,6 +1039,7 @@ eo_status eo_route(eo_engine* e, int32_t layer, const void* x, int32_t T, const 
     EOCHK(check_layer(e, layer));
     EOCHK(check_T(e, T));
     if (!x || !ids || !w) return fail(EO_ERR_INVALID_ARG, "null pointer");
+    HIPCHK(hipSetDevice(e->cfg.device));
     const size_t roff = (size_t)layer * e->E * e->H;
     hipError_t he = launch_route(x, e->act_bf16, e->d_router + roff, e->d_router_t + roff, T, e->E,
                                  e->H, e->k, forced_ids, ids, w, e->d_z, e->d_xt,
@@ -1053,6 +1054,7 @@ eo_status eo_route_noalloc(eo_engine* e, int32_t layer, const void* x, int32_t T
     EOCHK(check_T(e, T));
     if (!x || !ids || !w) return fail(EO_ERR_INVALID_ARG, "null pointer");
     if (!e->scratch) return fail(EO_ERR_STATE, "no scratch address on this engine's device");
+    HIPCHK(hipSetDevice(e->cfg.device));
     // logits [T, E] fp32 at the start, then (chain-interleaved kernel) x as
     // [T][H/512][64][8] bf16 at the next 256-byte boundary
     const bool chains = route_chains_ok(T, e->E, e->H, e->act_bf16);
@@ -1073,17 +1075,20 @@ eo_status eo_lookup_plan(eo_engine* e, int32_t layer, const int32_t* ids, int32_
     EOCHK(check_layer(e, layer));
     EOCHK(check_T(e, T));
     if (!ids) return fail(EO_ERR_INVALID_ARG, "null ids");
+    HIPCHK(hipSetDevice(e->cfg.device));
     return do_plan(e, layer, ids, nullptr, nullptr, T, (hipStream_t)stream);
 }
 
 eo_status eo_fill(eo_engine* e, void* stream) {
     if (!e) return fail(EO_ERR_INVALID_ARG, "null engine");
+    HIPCHK(hipSetDevice(e->cfg.device));
     return do_fill(e, (hipStream_t)stream);
 }
 
 eo_status eo_host_execute(eo_engine* e, const void* x, const int32_t* ids, const float* w,
                           void* stream) {
     if (!e || !x || !ids || !w) return fail(EO_ERR_INVALID_ARG, "null argument");
+    HIPCHK(hipSetDevice(e->cfg.device));
     return do_host(e, x, ids, w, (hipStream_t)stream);
 }
 
@@ -1094,6 +1099,7 @@ eo_status eo_expert_ffn_combine(eo_engine* e, int32_t layer, const void* x, cons
     EOCHK(wait_plan(e));
     if (layer != e->plan_layer) return fail(EO_ERR_STATE, "layer differs from the pending plan's");
     if (!aligned16(x) || !aligned16(y)) return fail(EO_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+    HIPCHK(hipSetDevice(e->cfg.device));
     hipStream_t s = (hipStream_t)stream;
     EOCHK(do_ffn_device(e, layer, x, ids, w, s));
     return do_combine(e, ids, y, nullptr, s);
@@ -1106,6 +1112,7 @@ eo_status eo_moe_layer(eo_engine* e, int32_t layer, const void* x, float* y, int
     EOCHK(check_T(e, T));
     if (!x || !y) return fail(EO_ERR_INVALID_ARG, "null argument");
     if (!aligned16(x) || !aligned16(y)) return fail(EO_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+    HIPCHK(hipSetDevice(e->cfg.device));
     EOCHK(moe_layer_impl(e, layer, x, y, T, forced_ids, e->d_ids, e->d_w, nullptr,
                          (hipStream_t)stream));
     if (e->timing) EOCHK(harvest_times(e));
@@ -1118,6 +1125,7 @@ eo_status eo_decode_step(eo_engine* e, void* x_inout, int32_t T, const int32_t* 
     if (!e || !x_inout) return fail(EO_ERR_INVALID_ARG, "null argument");
     EOCHK(check_T(e, T));
     if (!aligned16(x_inout)) return fail(EO_ERR_INVALID_ARG, "x must be 16-byte aligned");
+    HIPCHK(hipSetDevice(e->cfg.device));
     hipStream_t s = (hipStream_t)stream;
     if (T == 1 && e->fused_entry && entry_ok(e->E, e->H, e->act_bf16)) {
         EOCHK(decode_one_token(e, (uint16_t*)x_inout, forced_ids, s));

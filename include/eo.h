@@ -23,7 +23,9 @@
  *     caller buffers are valid once the stream has reached that point.
  *   - Asynchronous device errors surface at the next call or at eo_sync() as
  *     EO_ERR_HIP.
- *   - An engine is used from one host thread at a time.
+ *   - An engine is used from one host thread at a time. Calls that touch the
+ *     device make the engine's device (cfg->device) current on the calling
+ *     thread; a stream passed in must belong to that device.
  *   - Debugging: with EO_DEBUG_SYNC=1 in the environment at eo_create, the step
  *     calls wait for the device after every stage (route, lookup and plan,
  *     fill, expert FFN, host-execute, combine; per layer in eo_decode_step and

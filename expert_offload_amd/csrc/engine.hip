@@ -87,6 +87,7 @@ struct eo_engine {
     // device's 100 MHz clock (EO_TEST_FILL_WAIT_TICKS sets it, for the test of
     // the path where the wait runs out)
     uint64_t fill_wait_ticks = 100000000ull;
+    uint32_t* d_fill_counters = nullptr;  // counters of the fill + GEMV launch (zero between)
     uint8_t* d_slots = nullptr;
     uint8_t* d_shared = nullptr;
     float* d_router = nullptr;
@@ -545,7 +546,7 @@ eo_status do_fill_gemv(eo_engine* e, int layer, const int32_t* ids, const float*
                                          e->pool_dev[e->plan_layer], e->S, e->S_pad, ids, w, e->k,
                                          e->E, e->shared, e->H, e->I, e->d_u, e->act_bf16,
                                          e->d_hgemv, e->d_yparts, e->d_state,
-                                         e->fill_wait_ticks, s);
+                                         e->d_fill_counters, e->fill_wait_ticks, s);
         if (he == hipSuccess) return EO_OK;
         if (he != hipErrorNotSupported)
             return fail(EO_ERR_HIP, std::string("fill and GEMV: ") + hipGetErrorString(he));
@@ -685,7 +686,7 @@ void destroy_all(eo_engine* e) {
     auto fh = [](void* p) { if (p) (void)hipHostFree(p); };
     fr(e->d_slots); fr(e->d_shared); fr(e->d_router); fr(e->d_router_t); fr(e->d_xt);
     fr(e->d_slot_key); fr(e->d_slot_stamp);
-    fr(e->d_key2slot); fr(e->d_state); fr(e->d_plan); fr(e->d_ids); fr(e->d_w); fr(e->d_z);
+    fr(e->d_key2slot); fr(e->d_state); fr(e->d_fill_counters); fr(e->d_plan); fr(e->d_ids); fr(e->d_w); fr(e->d_z);
     fr(e->d_y); fr(e->d_u); fr(e->d_r); fr(e->d_hgemv); fr(e->d_yparts); fr(e->d_yhost);
     fr(e->pb.counts); fr(e->pb.offsets); fr(e->pb.tile_off); fr(e->pb.perm_pair);
     fr(e->pb.chunk_cnt); fr(e->d_hbuf); fr(e->d_opairs);
@@ -772,6 +773,8 @@ eo_status create_impl(const eo_config* cfg, eo_engine* e) {
     EOCHK(dmalloc(&e->d_key2slot, sizeof(int32_t) * e->L * e->E));
     EOCHK(dmalloc(&e->d_state, sizeof(DevState)));
     HIPCHK(hipMemset(e->d_state, 0, sizeof(DevState)));
+    EOCHK(dmalloc(&e->d_fill_counters, fill_gemv_counter_bytes()));
+    HIPCHK(hipMemset(e->d_fill_counters, 0, fill_gemv_counter_bytes()));
     EOCHK(dmalloc(&e->d_plan, sizeof(DevPlan)));
     HIPCHK(hipMemset(e->d_plan, 0, sizeof(DevPlan)));
     const unsigned mflags = hipHostMallocMapped | hipHostMallocCoherent;

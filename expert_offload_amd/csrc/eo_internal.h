@@ -172,7 +172,10 @@ hipError_t launch_ffn_gemv(int fmt, const Layout& lay, GroupW gw, const DevPlan*
 // gate/up for every expert slot, those of a filled expert once the bytes gate/up
 // reads are in (st->fill_ready[r], which the plan set to 0, reaching
 // kFillBlocks; a wait bounded by wait_ticks of the device's 100 MHz clock that
-// sets st->sync_err when it runs out); then the down kernel. The same
+// sets st->sync_err when it runs out); on a layer call with fills the same
+// launch also runs the down rows of the slots resident before the call, once
+// their gate/up rows are counted in `counters`; then the down kernel (the
+// filled experts' down rows on such a call, every slot's otherwise). The same
 // arithmetic as launch_fill followed by launch_ffn_gemv.
 // hipErrorNotSupported (nothing launched) where the tuned one-token GEMV does
 // not apply (activations not bf16, fp32 weights, untuned shapes).
@@ -181,8 +184,11 @@ hipError_t launch_fill_gemv(int fmt, const Layout& lay, GroupW gw, uint8_t* slot
                             uint64_t S_pad,
                             const int32_t* ids, const float* w, int k, int E, int has_shared,
                             int H, int I, const void* x, int act_bf16, float* h_buf,
-                            float* y_parts, DevState* st, uint64_t wait_ticks,
-                            hipStream_t s);
+                            float* y_parts, DevState* st, uint32_t* counters,
+                            uint64_t wait_ticks, hipStream_t s);
+// Bytes of the counters launch_fill_gemv takes (device memory, zero before the
+// first launch; each launch leaves them zero).
+size_t fill_gemv_counter_bytes();
 // Sum of the GEMV partials (k + shared rows of [H]) plus host results; with
 // x_res, x_res = act(x_in + y) (x_in null: in place).
 hipError_t launch_gemv_reduce(const float* y_parts, int nparts, const float* y_host, int H,

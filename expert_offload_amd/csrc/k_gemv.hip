@@ -312,7 +312,8 @@ __device__ __forceinline__ const uint8_t* row_ptr(const uint8_t* data, int row, 
 
 // Partial dots of R weight rows with the bf16 vector x over this lane's chunks
 // c = gl + G*i (i < NC); block scales are applied, row/tensor scales are not.
-template <int FMT, int G, int NC, int R>
+// XC: x is read at device scope (written by other workgroups of the same launch).
+template <int FMT, int G, int NC, int R, bool XC = false>
 __device__ __forceinline__ void rows_dot(const uint8_t* data, const uint8_t* scal, int K,
                                          const int (&rows)[R], const uint16_t* x, int gl,
                                          float (&out)[R]) {
@@ -328,7 +329,18 @@ __device__ __forceinline__ void rows_dot(const uint8_t* data, const uint8_t* sca
 #pragma unroll
     for (int i = 0; i < NC; ++i)
 #pragma unroll
-        for (int q = 0; q < XQ; ++q) xq[i][q] = *(const uint4*)(x + (size_t)(gl + G * i) * N + 8 * q);
+        for (int q = 0; q < XQ; ++q) {
+            const uint16_t* px = x + (size_t)(gl + G * i) * N + 8 * q;
+            if (XC) {
+                const uint32_t* p32 = (const uint32_t*)px;
+                xq[i][q] = make_uint4(__hip_atomic_load(p32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                                      __hip_atomic_load(p32 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                                      __hip_atomic_load(p32 + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                                      __hip_atomic_load(p32 + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            } else {
+                xq[i][q] = *(const uint4*)px;
+            }
+        }
     if (FMT == EO_W_MXFP4 || FMT == EO_W_NVFP4) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -378,7 +390,8 @@ __device__ __forceinline__ void rows_dot(const uint8_t* data, const uint8_t* sca
 }
 
 // Gate/up rows of workgroup `bidx`: expert slot bidx / nA_per, row block bidx % nA_per.
-template <int FMT, int GA, int NCA, int RA>
+// HC: h is stored at device scope (read by other workgroups of the same launch).
+template <int FMT, int GA, int NCA, int RA, bool HC = false>
 __device__ __forceinline__ void gu_body(const GemvArgs& a, uint16_t* __restrict__ hb, int nA_per,
                                         int bidx) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -408,7 +421,12 @@ __device__ __forceinline__ void gu_body(const GemvArgs& a, uint16_t* __restrict_
         for (int r = 0; r < RA; ++r) {
             float g = out[r] * (FMT == EO_W_FP8 ? rs[r0 + r] : sg);
             float u = out[RA + r] * (FMT == EO_W_FP8 ? rs[a.I + r0 + r] : su);
-            hb[(size_t)j * a.I + r0 + r] = (uint16_t)f32_bf16_rne(silu_f32(g) * u);
+            const uint16_t hv = (uint16_t)f32_bf16_rne(silu_f32(g) * u);
+            if (HC)
+                __hip_atomic_store(hb + (size_t)j * a.I + r0 + r, hv, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            else
+                hb[(size_t)j * a.I + r0 + r] = hv;
         }
     }
 }
@@ -418,7 +436,79 @@ __global__ __launch_bounds__(256) void k_gemv_gu(GemvArgs a, uint16_t* __restric
     gu_body<FMT, GA, NCA, RA>(a, hb, nA_per, blockIdx.x);
 }
 
-// The fills of a one-token call and the gate/up rows in one launch.
+// Down rows of workgroup `bidx`: expert slot bidx / nB_per, row block bidx % nB_per.
+// XC: h is read at device scope.
+template <int FMT, int GB, int NCB, int RB, bool XC = false>
+__device__ __forceinline__ void dn_body(const GemvArgs& a, const uint16_t* __restrict__ hb,
+                                        int nB_per, int bidx) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = bidx / nB_per, blk = bidx % nB_per;
+    const int grp = lane / GB, gl = lane % GB;
+    const int o0 = ((blk * 4 + wave) * (64 / GB) + grp) * RB;
+    const uint8_t* wb = expert_base(a, j);
+    if (!wb) {
+        if (gl == 0)
+#pragma unroll
+            for (int r = 0; r < RB; ++r) a.yp[(size_t)j * a.H + o0 + r] = 0.0f;
+        return;
+    }
+    int rows[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) rows[r] = o0 + r;
+    float out[RB];
+    rows_dot<FMT, GB, NCB, RB, XC>(wb + a.lay.d2, wb + a.lay.s2, a.I, rows, hb + (size_t)j * a.I,
+                                   gl, out);
+    if (gl == 0) {
+        const float wj = a.ex.valid ? a.ex.w[j] : (j < a.k ? a.w[j] : 1.0f);
+        const float* rs = (const float*)(wb + a.lay.s2);
+        const float gs = FMT == EO_W_NVFP4 ? ((const float*)(wb + a.lay.gl))[2] : 1.0f;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            float v = out[r] * (FMT == EO_W_FP8 ? rs[o0 + r] : gs);
+            a.yp[(size_t)j * a.H + o0 + r] = v * wj;
+        }
+    }
+}
+
+// Gate/up workgroups of each hit expert slot of a layer call with fills are
+// counted on kSub counters, one 128-byte line apiece (workgroup blk on counter
+// blk % kSub); the one that completes a counter counts it on the slot's total.
+constexpr int kSub = 64;
+struct DownSync {
+    uint32_t* sub;   // [nexp][kSub] x 32 words
+    uint32_t* done;  // [nexp] x 32 words: counters complete
+};
+__host__ __device__ constexpr size_t down_sync_words() { return (size_t)(kMaxK + 1) * (kSub + 1) * 32; }
+
+// Whether expert slot j of a one-token plan is a hit (resident before this
+// call: not filled, not host-executed); the shared expert counts as one.
+__device__ __forceinline__ bool slot_hit(const GemvArgs& a, int j) {
+    const DevPlan* p = a.plan;
+    if (j == a.k) return a.gw.shared_w != nullptr;
+    if (p->pad != 0) return false;
+    const int sl = p->tok_slot[j];
+    bool filled = false;
+    for (int r = 0; r < p->q_fill; ++r) filled |= p->fill_slot[r] == sl;
+    return sl >= 0 && !filled;
+}
+
+// ds != null (behind the fill + GEMV launch): on a layer call with fills the
+// hit slots' rows were done by that launch, so their workgroups leave at once,
+// and workgroup 0 clears its counters for the next launch.
+template <int FMT, int GB, int NCB, int RB>
+__global__ __launch_bounds__(256) void k_gemv_dn(GemvArgs a, const uint16_t* __restrict__ hb,
+                                                 int nB_per, DownSync ds) {
+    if (ds.sub && a.plan->pad == 0 && a.plan->q_fill > 0) {
+        if (blockIdx.x == 0)
+            for (int i = threadIdx.x; i < a.nexp * (kSub + 1); i += 256)
+                (i < a.nexp * kSub ? ds.sub[i * 32] : ds.done[(i - a.nexp * kSub) * 32]) = 0;
+        if (slot_hit(a, blockIdx.x / nB_per)) return;
+    }
+    dn_body<FMT, GB, NCB, RB>(a, hb, nB_per, blockIdx.x);
+}
+
+// The fills of a one-token call, the gate/up rows and the hit slots' down rows
+// in one launch.
 struct FillSync {
     const uint8_t* pool;  // the layer's pinned pool, device-visible
     uint8_t* slots;       // the cache slots the fills write (the GEMV's gw.slots)
@@ -426,6 +516,7 @@ struct FillSync {
     uint32_t* ready;  // [kMaxK]: fill workgroups done with the r-th fill's gate/up bytes
     int32_t* err;     // set when a wait for the fills runs out
     uint64_t wait_ticks;  // longest wait, in ticks of the device's 100 MHz wall clock
+    DownSync down;        // counters of the hit slots' gate/up rows (zero between launches)
 };
 
 // Rank among this call's fills of a one-token plan's expert slot j, or -1.
@@ -443,13 +534,18 @@ __device__ __forceinline__ int fill_rank(const DevPlan* p, int j, int k) {
 // their scales and the global scales), released at device scope (the counter's
 // increment carries the release: the L2 lines written are written back) and
 // counted; then the down projection's bytes, which the next launch reads. The
-// other workgroups run gate/up; those of a filled expert first wait for its
-// counter to reach kFillBlocks (lower workgroup ids, dispatched first: the wait
-// ends), then acquire at device scope before they read the slot, while the
-// fill workgroups copy the down rows.
-template <int FMT, int GA, int NCA, int RA>
+// next nexp * nA_per workgroups run gate/up; those of a filled expert first
+// wait for its counter to reach kFillBlocks (lower workgroup ids, dispatched
+// first: the wait ends), then acquire at device scope before they read the
+// slot, while the fill workgroups copy the down rows. On a layer call with
+// fills, the hit slots' gate/up workgroups store h at device scope and count
+// themselves, and the last nexp * nB_per workgroups run those slots' down rows
+// once their counts are complete (one polling thread per workgroup, reading h
+// at device scope), so that only the filled experts' down rows are left to the
+// down kernel behind this launch.
+template <int FMT, int GA, int NCA, int RA, int GB, int NCB, int RB>
 __global__ __launch_bounds__(256) void k_fill_gu(GemvArgs a, uint16_t* __restrict__ hb, int nA_per,
-                                                 FillSync f) {
+                                                 int nB_per, FillSync f, DownSync ds) {
     if ((int)blockIdx.x < kFillBlocks) {
         const DevPlan* p = a.plan;
         const int q = p->pad == 0 ? p->q_fill : 0;
@@ -474,8 +570,44 @@ __global__ __launch_bounds__(256) void k_fill_gu(GemvArgs a, uint16_t* __restric
         }
         return;
     }
+    const int q = a.plan->pad == 0 ? a.plan->q_fill : 0;
+    const int nGU = a.nexp * nA_per;
+    if ((int)blockIdx.x >= kFillBlocks + nGU) {  // down rows of a hit slot
+        const int bidx = blockIdx.x - kFillBlocks - nGU, j = bidx / nB_per;
+        if (q == 0 || !slot_hit(a, j)) return;  // the down kernel does these rows
+        if (threadIdx.x == 0) {
+            const uint32_t nsub = (uint32_t)min(kSub, nA_per);
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            while (__hip_atomic_load(&ds.done[j * 32], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                   nsub) {
+                if (__builtin_amdgcn_s_memrealtime() - t0 > f.wait_ticks) {
+                    __hip_atomic_store(f.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(32);
+            }
+        }
+        __syncthreads();
+        dn_body<FMT, GB, NCB, RB, true>(a, hb, nB_per, bidx);
+        return;
+    }
     const int bidx = blockIdx.x - kFillBlocks;
-    const int r = fill_rank(a.plan, bidx / nA_per, a.k);  // workgroup-uniform
+    const int j = bidx / nA_per;
+    if (q > 0 && slot_hit(a, j)) {  // workgroup-uniform
+        gu_body<FMT, GA, NCA, RA, true>(a, hb, nA_per, bidx);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's h stores have completed
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const int blk = bidx % nA_per, sub = blk % kSub;
+            const uint32_t per = (uint32_t)((nA_per - sub + kSub - 1) / kSub);
+            if (__hip_atomic_fetch_add(&ds.sub[(j * kSub + sub) * 32], 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT) + 1 == per)
+                __hip_atomic_fetch_add(&ds.done[j * 32], 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return;
+    }
+    const int r = fill_rank(a.plan, j, a.k);  // workgroup-uniform
     if (r >= 0) {
         if (threadIdx.x == 0) {
             const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -494,37 +626,6 @@ __global__ __launch_bounds__(256) void k_fill_gu(GemvArgs a, uint16_t* __restric
     gu_body<FMT, GA, NCA, RA>(a, hb, nA_per, bidx);
 }
 
-template <int FMT, int GB, int NCB, int RB>
-__global__ __launch_bounds__(256) void k_gemv_dn(GemvArgs a, const uint16_t* __restrict__ hb,
-                                                 int nB_per) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int j = blockIdx.x / nB_per, blk = blockIdx.x % nB_per;
-    const int grp = lane / GB, gl = lane % GB;
-    const int o0 = ((blk * 4 + wave) * (64 / GB) + grp) * RB;
-    const uint8_t* wb = expert_base(a, j);
-    if (!wb) {
-        if (gl == 0)
-#pragma unroll
-            for (int r = 0; r < RB; ++r) a.yp[(size_t)j * a.H + o0 + r] = 0.0f;
-        return;
-    }
-    int rows[RB];
-#pragma unroll
-    for (int r = 0; r < RB; ++r) rows[r] = o0 + r;
-    float out[RB];
-    rows_dot<FMT, GB, NCB, RB>(wb + a.lay.d2, wb + a.lay.s2, a.I, rows, hb + (size_t)j * a.I, gl,
-                               out);
-    if (gl == 0) {
-        const float wj = a.ex.valid ? a.ex.w[j] : (j < a.k ? a.w[j] : 1.0f);
-        const float* rs = (const float*)(wb + a.lay.s2);
-        const float gs = FMT == EO_W_NVFP4 ? ((const float*)(wb + a.lay.gl))[2] : 1.0f;
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            float v = out[r] * (FMT == EO_W_FP8 ? rs[o0 + r] : gs);
-            a.yp[(size_t)j * a.H + o0 + r] = v * wj;
-        }
-    }
-}
 
 // Lanes per row G and chunks per lane NC for a row of `nch` chunks.
 bool split_rows(int nch, int* G, int* NC) {
@@ -543,14 +644,16 @@ hipError_t run_fast(const GemvArgs& a, uint16_t* hb, hipStream_t s, hipEvent_t* 
     const int rowsA = 4 * (64 / GA) * RA, rowsB = 4 * (64 / GB) * RB;
     if (a.I % rowsA || a.H % rowsB) return hipErrorNotSupported;
     const int nA_per = a.I / rowsA, nB_per = a.H / rowsB;
+    const DownSync ds = fill ? fill->down : DownSync{nullptr, nullptr};
     if (fill)
-        hipExtLaunchKernelGGL(k_fill_gu<FMT, GA, NCA, RA>, dim3(kFillBlocks + a.nexp * nA_per),
-                              dim3(256), 0, s, ev[0], ev[1], 0, a, hb, nA_per, *fill);
+        hipExtLaunchKernelGGL((k_fill_gu<FMT, GA, NCA, RA, GB, NCB, RB>),
+                              dim3(kFillBlocks + a.nexp * (nA_per + nB_per)), dim3(256), 0, s,
+                              ev[0], ev[1], 0, a, hb, nA_per, nB_per, *fill, ds);
     else
         hipExtLaunchKernelGGL(k_gemv_gu<FMT, GA, NCA, RA>, dim3(a.nexp * nA_per), dim3(256), 0, s,
                               ev[0], ev[1], 0, a, hb, nA_per);
     hipExtLaunchKernelGGL(k_gemv_dn<FMT, GB, NCB, RB>, dim3(a.nexp * nB_per), dim3(256), 0, s,
-                          ev[2], ev[3], 0, a, (const uint16_t*)hb, nB_per);
+                          ev[2], ev[3], 0, a, (const uint16_t*)hb, nB_per, ds);
     return hipGetLastError();
 }
 
@@ -635,13 +738,15 @@ hipError_t launch_ffn_gemv(int fmt, const Layout& lay, GroupW gw, const DevPlan*
     return hipGetLastError();
 }
 
+size_t fill_gemv_counter_bytes() { return sizeof(uint32_t) * down_sync_words(); }
+
 hipError_t launch_fill_gemv(int fmt, const Layout& lay, GroupW gw, uint8_t* slots,
                             const DevPlan* plan, const uint8_t* pool_layer_dev, uint64_t S,
                             uint64_t S_pad,
                             const int32_t* ids, const float* w, int k, int E, int has_shared,
                             int H, int I, const void* x, int act_bf16, float* h_buf,
-                            float* y_parts, DevState* st, uint64_t wait_ticks,
-                            hipStream_t s) {
+                            float* y_parts, DevState* st, uint32_t* counters,
+                            uint64_t wait_ticks, hipStream_t s) {
     if (!act_bf16) return hipErrorNotSupported;
     GemvArgs a{};
     a.gw = gw;
@@ -659,7 +764,9 @@ hipError_t launch_fill_gemv(int fmt, const Layout& lay, GroupW gw, uint8_t* slot
     a.yp = y_parts;
     if (slots != gw.slots) return hipErrorInvalidValue;
     if (lay.bytes != S) return hipErrorInvalidValue;
-    const FillSync f{pool_layer_dev, slots, S_pad, st->fill_ready, &st->sync_err, wait_ticks};
+    if (!counters) return hipErrorInvalidValue;
+    const DownSync ds{counters, counters + (size_t)(kMaxK + 1) * kSub * 32};
+    const FillSync f{pool_layer_dev, slots, S_pad, st->fill_ready, &st->sync_err, wait_ticks, ds};
     uint16_t* hb = (uint16_t*)h_buf;
     hipEvent_t none[4] = {nullptr, nullptr, nullptr, nullptr};
     switch (fmt) {

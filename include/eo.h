@@ -263,10 +263,12 @@ eo_status eo_moe_layer(eo_engine* e, int32_t layer, const void* x, float* y, int
  * (stored in the activation dtype). forced_ids: device [L, T, k] or NULL.
  * One token with bf16 activations runs three kernels per layer and no host wait
  * between layers other than the plan readback for the host-list experts:
- * layer entry + plan (one launch); the fills and the gate/up GEMV (one launch:
+ * layer entry + plan (one launch); the fills and the expert GEMV (one launch:
  * 64 workgroups copy the fills, the gate/up bytes of each filled expert first,
  * while the others run the gate/up rows, a filled expert's once its bytes are
- * in); the down GEMV. Should a gate/up workgroup's wait for those bytes run
+ * in, and, on a layer with fills, the down rows of the experts resident before
+ * it once their gate/up rows are done); the down GEMV (the filled experts' rows
+ * after a layer with fills, else all). Should one of these bounded waits run
  * out (1 s; EO_TEST_FILL_WAIT_TICKS=n at engine creation sets it to n ticks of
  * the device's 100 MHz clock, for tests of this path), the next one-token plan
  * returns EO_ERR_HIP and changes nothing.

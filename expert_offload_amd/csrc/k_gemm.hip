@@ -12,11 +12,14 @@
 // scale — are applied to the fp32 accumulators in the epilogue. The format
 // list is the juejin.cn overview's (section 5).
 //
-// Four kernels share the grouping (128-row tiles per group from tile_off) and
+// Five kernels share the grouping (128-row tiles per group from tile_off) and
 // the GEMM1 split (each wavefront holds matching gate and up accumulators and
 // forms h in registers):
-//   v4 (bf16, the default): 128 x 256 tiles, a three-stage direct-to-LDS ring,
-//      two workgroups per CU;
+//   v5 (bf16, the default): 128 x 256 tiles, two workgroups per CU, direct-to-
+//      LDS rings of two slots for each operand, the weight tile in 128-byte
+//      rows (K step 64), the activation tile in 64-byte rows (K step 32);
+//   v4 (bf16, on request): the same tiles with one three-stage ring of K-32
+//      tiles for both operands;
 //   v4q (FP8 / MXFP4 / NVFP4, the default): v4's ring for the activation tile,
 //      with each weight row's next 64-byte span of codes in registers, decoded
 //      into the ring one tile per step between the two halves of its MFMAs;
@@ -29,6 +32,7 @@
 #include <hip/hip_ext.h>
 
 #include <cstdlib>
+#include <type_traits>
 
 #include "decode_dev.h"
 #include "dev_common.h"
@@ -43,9 +47,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;  // LDS row stride in bf16
 
-// 2: the async-ring kernels (v4 for bf16, v4q for fp8 / fp4); 1: v3 for all;
-// 0: the plain 128 x 128 kernel. EO_GEMM_PATH overrides.
-int g_gemm_tiles = 2;
+// 3: v5 for bf16, v4q for fp8 / fp4; 2: the one-ring kernels (v4 for bf16,
+// v4q for fp8 / fp4); 1: v3 for all; 0: the plain 128 x 128 kernel.
+// EO_GEMM_PATH overrides.
+int g_gemm_tiles = 3;
 
 struct GemmArgs {
     GroupW gw;
@@ -651,6 +656,13 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
 }
 
+// The same, and all of this thread's LDS operations done.
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | ((N >> 4) << 14));
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int swz(int row, int seg) { return seg ^ ((row >> 2) & 3); }
@@ -856,6 +868,237 @@ bool run_v4(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hi
                           ev[0], ev[1], 0, a1, n1);
     hipExtLaunchKernelGGL((k_gemm_v4<1, S>), dim3(grid(n2)), dim3(256), (uint32_t)v4_lds<S>(), s,
                           ev[2], ev[3], 0, a2, n2);
+    return true;
+}
+
+// ------------------------------------------------------------------ v5 (bf16)
+// v4's tiles, MFMAs and epilogue with the weight tile loaded as 128-byte rows.
+// A direct-to-LDS load instruction fills 1 KB: with 64-byte rows it touches 16
+// rows, i.e. 16 cache lines, with 128-byte rows 8. In a loop-only probe of the
+// same tiles and swizzle the 128-byte rows ran ~20% faster, but v4's
+// three-stage ring at K step 64 needs 144 KB. Here the two operands get rings of
+// their own, two slots each: A (128 rows) keeps 64-byte rows at K step 32
+// (8 KB a slot), B (256 rows) has 128-byte rows at K step 64 (32 KB a slot),
+// 80 KB in all, so two workgroups still share a CU. Each K-32 step issues the
+// next A tile and half of the next B tile (128 of its rows): 6 loads per
+// wavefront as in v4. Segment s of a 128-byte B row r sits in slot
+// s ^ ((r >> 1) & 7): the 16 lanes of a ds_read_b128 quarter (16 rows, one
+// logical segment) then hit 16 distinct 16-byte bank groups.
+constexpr size_t kV5ASlot = (size_t)V3M * 64;            // 8 KB: 128 rows x K 32
+constexpr size_t kV5BSlot = (size_t)V3N * 128;           // 32 KB: 256 rows x K 64
+constexpr size_t kV5Lds = 2 * kV5ASlot + 2 * kV5BSlot;   // 80 KB
+static_assert(kV3Out + 2 * V3M * sizeof(int32_t) <= kV5Lds, "epilogue tile and pair table");
+static_assert(2 * kV5Lds <= 160 * 1024, "v5 LDS: two workgroups per CU");
+
+// Half h (rows h*128 .. h*128 + 127) of the B tile at K offset k0 (64 wide):
+// 4 x 1 KB per wavefront, 8 rows of 128 B each.
+template <int MODE>
+__device__ __forceinline__ void v5_issue_b(const GemmArgs& a, const uint16_t* wdata, int n0,
+                                           int k0, int h, uint8_t* bslot, int wave, int lane) {
+    const int K = a.K;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int rbase = h * 128 + (it * 4 + wave) * 8;
+        const int row = rbase + (lane >> 3);
+        const int wr = MODE == 0 ? (h == 0 ? n0 + row : a.I + n0 + row - 128) : n0 + row;
+        const int seg = (lane & 7) ^ ((row >> 1) & 7);
+        __builtin_amdgcn_global_load_lds(wdata + (size_t)wr * K + k0 + seg * 8,
+                                         (lds_void*)(bslot + rbase * 128), 16, 0, 0);
+    }
+}
+
+// The A tile at K offset k0 (32 wide): 2 x 1 KB per wavefront, as in v4.
+__device__ __forceinline__ void v5_issue_a(const uint16_t* const (&ap)[2], int k0, uint8_t* aslot,
+                                           int wave) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+        __builtin_amdgcn_global_load_lds(ap[it] + k0, (lds_void*)(aslot + (it * 4 + wave) * 1024),
+                                         16, 0, 0);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void k_gemm_v5(GemmArgs a, int nN) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    uint8_t* sb = (uint8_t*)smem;
+    uint8_t* const sa = sb;                   // A slots
+    uint8_t* const sw = sb + 2 * kV5ASlot;    // B slots
+
+    const int real = a.tile_off[a.G] * nN;
+    const int per = (real + 7) >> 3;
+    const int logical = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if ((int)(blockIdx.x >> 3) >= per || logical >= real) return;
+    const int tile = logical / nN, ntile = logical - tile * nN;
+    const int g = find_group(a.tile_off, a.G, tile);
+    const int m0 = a.offsets[g] + (tile - a.tile_off[g]) * V3M;
+    const int m_end = a.offsets[g + 1];
+    const uint8_t* wb = group_base(a.gw, g, a.E);
+    const uint16_t* wdata = (const uint16_t*)(wb + (MODE == 0 ? a.lay.d13 : a.lay.d2));
+    const int n0 = ntile * (MODE == 0 ? 128 : 256);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nk = a.K / V3K, nb = nk >> 1;
+
+    // the pair table goes to LDS after the K loop, which uses all of it
+    int my_pair = -1;
+    if (MODE == 1 && tid < V3M) my_pair = m0 + tid < m_end ? a.perm_pair[m0 + tid] : -1;
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    const uint16_t* ap[2];
+    v4_arows<MODE>(a, m0, m_end, wave, lane, ap);
+    v5_issue_a(ap, 0, sa, wave);
+    v5_issue_b<MODE>(a, wdata, n0, 0, 0, sw, wave, lane);
+    v5_issue_b<MODE>(a, wdata, n0, 0, 1, sw, wave, lane);
+
+    int arow[2], aseg[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        arow[i] = wm * 64 + i * 32 + (lane & 31);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) aseg[i][ks] = swz(arow[i], 2 * ks + (lane >> 5));
+    }
+    // byte offset of this lane's B operand in the first K-32 half of a slot;
+    // the second half's segments are the first's + 4, i.e. offset ^ 64
+    int boff[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int br = (MODE == 0 ? (j >> 1) * 128 + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32) +
+                       (lane & 31);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            boff[j][ks] = br * 128 + (((2 * ks + (lane >> 5)) ^ ((br >> 1) & 7)) << 4);
+    }
+
+    // One K-32 step. At an even step the A tile and the B tile's second half
+    // came with the previous step's loads (wait for all); at an odd step only
+    // the A tile did (its 2 loads go before the step's 4 B loads, and loads
+    // count down in issue order).
+    // Past the end the last tiles are loaded again, into the free slots, so
+    // every step has the same 6 loads.
+    auto step = [&](int kt, auto odd_t) {
+        constexpr int ODD = decltype(odd_t)::value;
+        // this wavefront's LDS reads of the previous step are done too: the
+        // compiler may hoist them above their MFMAs, and after the barrier
+        // other wavefronts load into the slot they read
+        wait_vm_lds<ODD ? 4 : 0>();
+        __builtin_amdgcn_s_barrier();
+        const uint8_t* sta = sa + (kt & 1) * kV5ASlot;
+        const uint8_t* stb = sw + ((kt >> 1) & 1) * kV5BSlot;
+        constexpr int hx = ODD << 6;
+        bf16x8 av[2][2], bv[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) av[0][i] = *(const bf16x8*)(sta + arow[i] * 64 + aseg[i][0] * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[0][j] = *(const bf16x8*)(stb + (boff[j][0] ^ hx));
+        v5_issue_a(ap, min(kt + 1, nk - 1) * V3K, sa + ((kt + 1) & 1) * kV5ASlot, wave);
+        v5_issue_b<MODE>(a, wdata, n0, min((kt >> 1) + 1, nb - 1) * 64, ODD,
+                         sw + (((kt >> 1) + 1) & 1) * kV5BSlot, wave, lane);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) av[1][i] = *(const bf16x8*)(sta + arow[i] * 64 + aseg[i][1] * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[1][j] = *(const bf16x8*)(stb + (boff[j][1] ^ hx));
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks][i], bv[ks][j],
+                                                                        acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int q = 0; q < 6; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, std::integral_constant<int, 0>{});
+        step(kt + 1, std::integral_constant<int, 1>{});
+    }
+    wait_vm<0>();
+    __syncthreads();  // all tile loads landed and all LDS reads done: reuse as the epilogue tile
+
+    uint16_t* ot = smem;
+    int32_t* s_pair = (int32_t*)(sb + kV3Out);
+    float* s_wp = (float*)(s_pair + V3M);
+    const int col = lane & 31;
+    if (MODE == 0) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int c = wn * 64 + jj * 32 + col;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    ot[row * V3_OUT_LD + c] =
+                        (uint16_t)f32_bf16_rne(silu_f32(acc[i][jj][v]) * acc[i][2 + jj][v]);
+                }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            int cidx = tid + 256 * it, row = cidx >> 4, seg = cidx & 15;
+            if (m0 + row < m_end)
+                *(uint4*)(a.h_out + (size_t)(m0 + row) * a.I + n0 + seg * 8) =
+                    *(const uint4*)(ot + row * V3_OUT_LD + seg * 8);
+        }
+    } else {
+        if (tid < V3M) {
+            s_pair[tid] = my_pair;
+            s_wp[tid] = my_pair < 0 ? 0.0f : (my_pair < a.Tk ? a.w[my_pair] : 1.0f);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = wn * 128 + j * 32 + col;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    ot[row * V3_OUT_LD + c] = (uint16_t)f32_bf16_rne(acc[i][j][v] * s_wp[row]);
+                }
+        }
+        __syncthreads();
+        uint16_t* op = (uint16_t*)a.o_pairs;
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            int cidx = tid + 256 * it, row = cidx >> 5, seg = cidx & 31;
+            int pair = s_pair[row];
+            if (pair >= 0)
+                *(uint4*)(op + (size_t)pair * a.H + n0 + seg * 8) =
+                    *(const uint4*)(ot + row * V3_OUT_LD + seg * 8);
+        }
+    }
+}
+
+bool run_v5(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hipEvent_t* ev) {
+    if (I % 128 || H % 256) return false;  // K = H or I: whole K-64 tiles
+    static bool attr = false;
+    if (!attr) {
+        if (hipFuncSetAttribute((const void*)k_gemm_v5<0>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kV5Lds) != hipSuccess ||
+            hipFuncSetAttribute((const void*)k_gemm_v5<1>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kV5Lds) != hipSuccess)
+            return false;
+        attr = true;
+    }
+    const int n1 = I / 128, n2 = H / 256;
+    auto grid = [&](int nN) { return ((tiles * nN + 7) / 8) * 8; };
+    hipExtLaunchKernelGGL(k_gemm_v5<0>, dim3(grid(n1)), dim3(256), (uint32_t)kV5Lds, s, ev[0],
+                          ev[1], 0, a1, n1);
+    hipExtLaunchKernelGGL(k_gemm_v5<1>, dim3(grid(n2)), dim3(256), (uint32_t)kV5Lds, s, ev[2],
+                          ev[3], 0, a2, n2);
     return true;
 }
 
@@ -1195,6 +1438,8 @@ bool run_v4q(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, h
 
 template <int FMT>
 void run_mfma(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hipEvent_t* ev) {
+    if (FMT == EO_W_BF16 && g_gemm_tiles >= 3)
+        if (run_v5(a1, a2, tiles, I, H, s, ev)) return;
     if (FMT == EO_W_BF16 && g_gemm_tiles >= 2) {
         if (run_v4<kV4Ring>(a1, a2, tiles, I, H, s, ev)) return;
     }
@@ -1217,7 +1462,7 @@ hipError_t launch_ffn_gemm(int fmt, const Layout& lay, GroupW gw, int E, int has
     (void)ids;
     // EO_GEMM_PATH (read per call, so that tests can compare the kernels)
     const char* path = getenv("EO_GEMM_PATH");
-    g_gemm_tiles = path ? atoi(path) : 2;
+    g_gemm_tiles = path ? atoi(path) : 3;
     const int G = E + (has_shared ? 1 : 0);
     const int tiles = (P_max + kTileM - 1) / kTileM + G;  // upper bound on row tiles
     GemmArgs a1{};

@@ -602,7 +602,7 @@ def test_grouped_gemm_at_its_shortest_contraction(fmt, monkeypatch):
                              synth.FMT_NAMES[fmt], 197, 8, shared=1)
     seed = 23
     x = synth.activations(seed, 91, 197, shape.hidden, 1.0, True)
-    for path in ("0", "1", "2"):
+    for path in ("0", "1", "2", "3"):
         monkeypatch.setenv("EO_GEMM_PATH", path)
         e = make_engine(shape, seed, max_tokens=197)
         try:
@@ -690,13 +690,14 @@ def test_one_token_calls_at_an_odd_multiple_of_128(fmt, lane):
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4", "nvfp4"])
 def test_every_gemm_and_gemv_kernel_against_the_oracle(fmt, monkeypatch):
-    # the grouped GEMM's three kernels (plain 128x128, register-prefetch
-    # 128x256, async-ring 128x256: v4 for bf16, v4q for quantised weights) and
-    # both decode GEMV families on one shape, each against the oracle
+    # the grouped GEMM's kernels (plain 128x128, register-prefetch 128x256,
+    # async-ring 128x256: v4 for bf16, v4q for quantised weights; bf16 with
+    # 128-byte weight rows, v5) and both decode GEMV families on one shape,
+    # each against the oracle
     shape = small_shape(fmt)
     seed = 19
     x = synth.activations(seed, 77, 300, shape.hidden, 1.0, True)
-    for path in ("0", "1", "2"):
+    for path in ("0", "1", "2", "3"):
         monkeypatch.setenv("EO_GEMM_PATH", path)
         e = make_engine(shape, seed, max_tokens=300)
         try:
@@ -780,3 +781,40 @@ def test_invalid_forced_ids_rejected():
             eo.eo_fill(e, _stream())  # no pending plan
     finally:
         eo.eo_destroy(e)
+
+
+@pytest.mark.timeout(600)
+def test_bf16_gemm_with_128_byte_weight_rows_matches_the_ring_kernel():
+    # v5 (EO_GEMM_PATH=3) runs the same MFMAs in the same K order as v4, so a
+    # prefill through either gives the same bits; the per-layer shape of the
+    # 48-layer bf16 model (H 2048, 128 experts, top-8, I 768), two layers, one
+    # 4096-token chunk (K 2048 and 768: 32 and 12 K-64 tiles), plus the oracle
+    # on sampled tokens
+    import os
+    shape = synth.LayerShape("v5_bf16", "test", 2048, 128, 8, 768, 2, synth.FMT_NAMES["bf16"],
+                             4096, 94)
+    T, L, H, k, seed = 4096, 2, 2048, 8, 5
+    x = synth.activations(seed, 5000, T, H, 1.0, True)
+    outs = {}
+    for path in ("2", "3"):
+        os.environ["EO_GEMM_PATH"] = path
+        try:
+            e = make_engine(shape, seed, max_tokens=T)
+            try:
+                cy = torch.zeros((L, T, H), dtype=torch.float32, device="cuda")
+                cx = torch.zeros((L, T, H), dtype=torch.int16, device="cuda")
+                ci = torch.zeros((L, T, k), dtype=torch.int32, device="cuda")
+                cw = torch.zeros((L, T, k), dtype=torch.float32, device="cuda")
+                eo.eo_set_capture(e, cx, cy, ci, cw, T)
+                eo.eo_prefill(e, dev(x.view(np.int16)), T, 1, _stream())
+                torch.cuda.synchronize()
+                outs[path] = (cx.cpu().numpy(), cy.cpu().numpy())
+            finally:
+                eo.eo_destroy(e)
+        finally:
+            del os.environ["EO_GEMM_PATH"]
+    assert np.array_equal(outs["2"][0], outs["3"][0])
+    assert np.array_equal(outs["2"][1].view(np.uint32), outs["3"][1].view(np.uint32))
+    rows = np.sort(np.random.default_rng(seed).choice(T, size=12, replace=False))
+    for l in range(L):
+        check_layer(shape, seed, l, outs["3"][0][l][rows].view(np.uint16), outs["3"][1][l][rows])

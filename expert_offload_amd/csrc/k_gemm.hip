@@ -880,8 +880,10 @@ bool run_v4(GemmArgs a1, GemmArgs a2, int tiles, int I, int H, hipStream_t s, hi
 // their own, two slots each: A (128 rows) keeps 64-byte rows at K step 32
 // (8 KB a slot), B (256 rows) has 128-byte rows at K step 64 (32 KB a slot),
 // 80 KB in all, so two workgroups still share a CU. Each K-32 step issues the
-// next A tile and half of the next B tile (128 of its rows): 6 loads per
-// wavefront as in v4. Segment s of a 128-byte B row r sits in slot
+// next A tile (2 loads per wavefront), which has one step to land; each even
+// step also issues the whole next B tile (8 loads), which has two. (Half of
+// the B tile at each step, 6 loads per step as in v4, ran 2-3% slower.)
+// Segment s of a 128-byte B row r sits in slot
 // s ^ ((r >> 1) & 7): the 16 lanes of a ds_read_b128 quarter (16 rows, one
 // logical segment) then hit 16 distinct 16-byte bank groups.
 constexpr size_t kV5ASlot = (size_t)V3M * 64;            // 8 KB: 128 rows x K 32
@@ -975,18 +977,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v5(GemmArgs a, int nN) {
             boff[j][ks] = br * 128 + (((2 * ks + (lane >> 5)) ^ ((br >> 1) & 7)) << 4);
     }
 
-    // One K-32 step. At an even step the A tile and the B tile's second half
-    // came with the previous step's loads (wait for all); at an odd step only
-    // the A tile did (its 2 loads go before the step's 4 B loads, and loads
-    // count down in issue order).
+    // One K-32 step. At an even step the previous step's loads brought the A
+    // tile (wait for all); at an odd step they brought the A tile and the next
+    // B tile (its 2 A loads go before the 8 B loads, and loads count down in
+    // issue order, so wait until 8 are left).
     // Past the end the last tiles are loaded again, into the free slots, so
-    // every step has the same 6 loads.
+    // the waits stay constant.
     auto step = [&](int kt, auto odd_t) {
         constexpr int ODD = decltype(odd_t)::value;
         // this wavefront's LDS reads of the previous step are done too: the
         // compiler may hoist them above their MFMAs, and after the barrier
         // other wavefronts load into the slot they read
-        wait_vm_lds<ODD ? 4 : 0>();
+        wait_vm_lds<ODD ? 8 : 0>();
         __builtin_amdgcn_s_barrier();
         const uint8_t* sta = sa + (kt & 1) * kV5ASlot;
         const uint8_t* stb = sw + ((kt >> 1) & 1) * kV5BSlot;
@@ -997,8 +999,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v5(GemmArgs a, int nN) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) bv[0][j] = *(const bf16x8*)(stb + (boff[j][0] ^ hx));
         v5_issue_a(ap, min(kt + 1, nk - 1) * V3K, sa + ((kt + 1) & 1) * kV5ASlot, wave);
-        v5_issue_b<MODE>(a, wdata, n0, min((kt >> 1) + 1, nb - 1) * 64, ODD,
-                         sw + (((kt >> 1) + 1) & 1) * kV5BSlot, wave, lane);
+        if (!ODD) {
+            v5_issue_b<MODE>(a, wdata, n0, min((kt >> 1) + 1, nb - 1) * 64, 0,
+                             sw + (((kt >> 1) + 1) & 1) * kV5BSlot, wave, lane);
+            v5_issue_b<MODE>(a, wdata, n0, min((kt >> 1) + 1, nb - 1) * 64, 1,
+                             sw + (((kt >> 1) + 1) & 1) * kV5BSlot, wave, lane);
+        }
 #pragma unroll
         for (int i = 0; i < 2; ++i) av[1][i] = *(const bf16x8*)(sta + arow[i] * 64 + aseg[i][1] * 16);
 #pragma unroll
@@ -1012,13 +1018,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v5(GemmArgs a, int nN) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks][i], bv[ks][j],
                                                                         acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+        constexpr int NV = ODD ? 2 : 10;  // this step's loads
+        constexpr int NQ = NV > 6 ? NV : 6;
 #pragma unroll
-        for (int q = 0; q < 6; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (q < NV) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+            if (q < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16 - NQ, 0);
     };
     for (int kt = 0; kt < nk; kt += 2) {
         step(kt, std::integral_constant<int, 0>{});

@@ -938,7 +938,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v5(GemmArgs a, int nN) {
     const int n0 = ntile * (MODE == 0 ? 128 : 256);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int nk = a.K / V3K, nb = nk >> 1;
+    const int nk = a.K / V3K;
 
     // the pair table goes to LDS after the K loop, which uses all of it
     int my_pair = -1;
@@ -980,15 +980,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v5(GemmArgs a, int nN) {
     // One K-32 step. At an even step the previous step's loads brought the A
     // tile (wait for all); at an odd step they brought the A tile and the next
     // B tile (its 2 A loads go before the 8 B loads, and loads count down in
-    // issue order, so wait until 8 are left).
-    // Past the end the last tiles are loaded again, into the free slots, so
-    // the waits stay constant.
-    auto step = [&](int kt, auto odd_t) {
-        constexpr int ODD = decltype(odd_t)::value;
+    // issue order, so wait until 8 are left). The last two steps load only
+    // what is left (the last A tile) and wait for everything, so no load is in
+    // flight when the K loop ends.
+    auto step = [&](int kt, auto odd_t, auto last_t) {
+        constexpr int ODD = decltype(odd_t)::value, LAST = decltype(last_t)::value;
         // this wavefront's LDS reads of the previous step are done too: the
         // compiler may hoist them above their MFMAs, and after the barrier
         // other wavefronts load into the slot they read
-        wait_vm_lds<ODD ? 8 : 0>();
+        wait_vm_lds<ODD && !LAST ? 8 : 0>();
         __builtin_amdgcn_s_barrier();
         const uint8_t* sta = sa + (kt & 1) * kV5ASlot;
         const uint8_t* stb = sw + ((kt >> 1) & 1) * kV5BSlot;
@@ -998,11 +998,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v5(GemmArgs a, int nN) {
         for (int i = 0; i < 2; ++i) av[0][i] = *(const bf16x8*)(sta + arow[i] * 64 + aseg[i][0] * 16);
 #pragma unroll
         for (int j = 0; j < 4; ++j) bv[0][j] = *(const bf16x8*)(stb + (boff[j][0] ^ hx));
-        v5_issue_a(ap, min(kt + 1, nk - 1) * V3K, sa + ((kt + 1) & 1) * kV5ASlot, wave);
-        if (!ODD) {
-            v5_issue_b<MODE>(a, wdata, n0, min((kt >> 1) + 1, nb - 1) * 64, 0,
+        if (!(LAST && ODD)) v5_issue_a(ap, (kt + 1) * V3K, sa + ((kt + 1) & 1) * kV5ASlot, wave);
+        if (!ODD && !LAST) {
+            v5_issue_b<MODE>(a, wdata, n0, ((kt >> 1) + 1) * 64, 0,
                              sw + (((kt >> 1) + 1) & 1) * kV5BSlot, wave, lane);
-            v5_issue_b<MODE>(a, wdata, n0, min((kt >> 1) + 1, nb - 1) * 64, 1,
+            v5_issue_b<MODE>(a, wdata, n0, ((kt >> 1) + 1) * 64, 1,
                              sw + (((kt >> 1) + 1) & 1) * kV5BSlot, wave, lane);
         }
 #pragma unroll
@@ -1018,7 +1018,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v5(GemmArgs a, int nN) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks][i], bv[ks][j],
                                                                         acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-        constexpr int NV = ODD ? 2 : 10;  // this step's loads
+        constexpr int NV = LAST ? (ODD ? 0 : 2) : (ODD ? 2 : 10);  // this step's loads
         constexpr int NQ = NV > 6 ? NV : 6;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
@@ -1028,10 +1028,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v5(GemmArgs a, int nN) {
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 16 - NQ, 0);
     };
-    for (int kt = 0; kt < nk; kt += 2) {
-        step(kt, std::integral_constant<int, 0>{});
-        step(kt + 1, std::integral_constant<int, 1>{});
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    for (int kt = 0; kt < nk - 2; kt += 2) {
+        step(kt, I0{}, I0{});
+        step(kt + 1, I1{}, I0{});
     }
+    step(nk - 2, I0{}, I1{});
+    step(nk - 1, I1{}, I1{});
     wait_vm<0>();
     __syncthreads();  // all tile loads landed and all LDS reads done: reuse as the epilogue tile
 

@@ -240,7 +240,11 @@ eo_status eo_host_execute(eo_engine* e, const void* x, const int32_t* ids, const
  * y fp32 [T,H] = sum_j w[t,j] * FFN_{e_j}(x_t) + FFN_shared(x_t).
  * No residual. Consumes the plan. x [T,H] and y device, 16-byte aligned; ids
  * and w as passed to the lookup. EO_ERR_STATE without a pending plan or when
- * `layer` is not the plan's. */
+ * `layer` is not the plan's. For T > 1 the environment switch EO_GEMM_PATH,
+ * read at each call, selects the grouped GEMM kernel that the tests compare:
+ * 3 (the default; bf16 weights load in 128-byte rows), 2 (one three-stage
+ * ring), 1 (register-staged tiles) or 0 (plain 128 x 128 tiles); all are held
+ * to the same bar against the oracle, and paths 3 and 2 give the same bits. */
 eo_status eo_expert_ffn_combine(eo_engine* e, int32_t layer, const void* x, const int32_t* ids,
                                 const float* w, float* y, void* stream);
 

@@ -958,10 +958,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v5(GemmArgs a, int nN) {
     v5_issue_b<MODE>(a, wdata, n0, 0, 0, sw, wave, lane);
     v5_issue_b<MODE>(a, wdata, n0, 0, 1, sw, wave, lane);
 
+    // A tile with at most 64 rows of its group (the group's ragged end) is
+    // split over the four wavefronts by columns alone: each multiplies rows
+    // 0..63 by a quarter of the 256 columns (8 MFMAs a step instead of 16),
+    // MODE 0 a quarter of the gate columns and the matching up columns. The
+    // same MFMAs run in the same K order for each output, so the results are
+    // the same bits.
+    const bool half = m_end - m0 <= 64;  // workgroup-uniform
     int arow[2], aseg[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        arow[i] = wm * 64 + i * 32 + (lane & 31);
+        arow[i] = (half ? 0 : wm * 64) + i * 32 + (lane & 31);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) aseg[i][ks] = swz(arow[i], 2 * ks + (lane >> 5));
     }
@@ -970,8 +977,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v5(GemmArgs a, int nN) {
     int boff[4][2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int br = (MODE == 0 ? (j >> 1) * 128 + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32) +
-                       (lane & 31);
+        const int br = half ? (MODE == 0 ? (j & 1) * 128 + wave * 32 : wave * 64 + (j & 1) * 32) +
+                                  (lane & 31)
+                            : (MODE == 0 ? (j >> 1) * 128 + wn * 64 + (j & 1) * 32
+                                         : wn * 128 + j * 32) +
+                                  (lane & 31);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
             boff[j][ks] = br * 128 + (((2 * ks + (lane >> 5)) ^ ((br >> 1) & 7)) << 4);
@@ -982,9 +992,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v5(GemmArgs a, int nN) {
     // B tile (its 2 A loads go before the 8 B loads, and loads count down in
     // issue order, so wait until 8 are left). The last two steps load only
     // what is left (the last A tile) and wait for everything, so no load is in
-    // flight when the K loop ends.
-    auto step = [&](int kt, auto odd_t, auto last_t) {
+    // flight when the K loop ends. HALF: the ragged tile's 2 column blocks per
+    // wavefront (acc[.][0..1]) instead of 4.
+    auto step = [&](int kt, auto odd_t, auto last_t, auto half_t) {
         constexpr int ODD = decltype(odd_t)::value, LAST = decltype(last_t)::value;
+        constexpr int NB = decltype(half_t)::value ? 2 : 4;
         // this wavefront's LDS reads of the previous step are done too: the
         // compiler may hoist them above their MFMAs, and after the barrier
         // other wavefronts load into the slot they read
@@ -993,11 +1005,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v5(GemmArgs a, int nN) {
         const uint8_t* sta = sa + (kt & 1) * kV5ASlot;
         const uint8_t* stb = sw + ((kt >> 1) & 1) * kV5BSlot;
         constexpr int hx = ODD << 6;
-        bf16x8 av[2][2], bv[2][4];
+        bf16x8 av[2][2], bv[2][NB];
 #pragma unroll
         for (int i = 0; i < 2; ++i) av[0][i] = *(const bf16x8*)(sta + arow[i] * 64 + aseg[i][0] * 16);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bv[0][j] = *(const bf16x8*)(stb + (boff[j][0] ^ hx));
+        for (int j = 0; j < NB; ++j) bv[0][j] = *(const bf16x8*)(stb + (boff[j][0] ^ hx));
         if (!(LAST && ODD)) v5_issue_a(ap, (kt + 1) * V3K, sa + ((kt + 1) & 1) * kV5ASlot, wave);
         if (!ODD && !LAST) {
             v5_issue_b<MODE>(a, wdata, n0, ((kt >> 1) + 1) * 64, 0,
@@ -1008,34 +1020,41 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v5(GemmArgs a, int nN) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) av[1][i] = *(const bf16x8*)(sta + arow[i] * 64 + aseg[i][1] * 16);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bv[1][j] = *(const bf16x8*)(stb + (boff[j][1] ^ hx));
+        for (int j = 0; j < NB; ++j) bv[1][j] = *(const bf16x8*)(stb + (boff[j][1] ^ hx));
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < NB; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks][i], bv[ks][j],
                                                                         acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+        constexpr int NDS = 2 + NB, NM = 4 * NB;  // each half step's LDS reads; MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
         constexpr int NV = LAST ? (ODD ? 0 : 2) : (ODD ? 2 : 10);  // this step's loads
-        constexpr int NQ = NV > 6 ? NV : 6;
+        constexpr int NQ = NV > NDS ? NV : NDS;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (q < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (q < NV) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-            if (q < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (q < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 16 - NQ, 0);
+        if (NM > NQ) __builtin_amdgcn_sched_group_barrier(0x008, NM - NQ, 0);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    for (int kt = 0; kt < nk - 2; kt += 2) {
-        step(kt, I0{}, I0{});
-        step(kt + 1, I1{}, I0{});
-    }
-    step(nk - 2, I0{}, I1{});
-    step(nk - 1, I1{}, I1{});
+    auto kloop = [&](auto half_t) {
+        for (int kt = 0; kt < nk - 2; kt += 2) {
+            step(kt, I0{}, I0{}, half_t);
+            step(kt + 1, I1{}, I0{}, half_t);
+        }
+        step(nk - 2, I0{}, I1{}, half_t);
+        step(nk - 1, I1{}, I1{}, half_t);
+    };
+    if (half)
+        kloop(I1{});
+    else
+        kloop(I0{});
     wait_vm<0>();
     __syncthreads();  // all tile loads landed and all LDS reads done: reuse as the epilogue tile
 
@@ -1044,17 +1063,29 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v5(GemmArgs a, int nN) {
     float* s_wp = (float*)(s_pair + V3M);
     const int col = lane & 31;
     if (MODE == 0) {
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int c = wn * 64 + jj * 32 + col;
+        if (half) {  // rows 0..63; gate block acc[.][0], up block acc[.][1]
+            const int c = wave * 32 + col;
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    int row = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
                     ot[row * V3_OUT_LD + c] =
-                        (uint16_t)f32_bf16_rne(silu_f32(acc[i][jj][v]) * acc[i][2 + jj][v]);
+                        (uint16_t)f32_bf16_rne(silu_f32(acc[i][0][v]) * acc[i][1][v]);
                 }
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int c = wn * 64 + jj * 32 + col;
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                        ot[row * V3_OUT_LD + c] =
+                            (uint16_t)f32_bf16_rne(silu_f32(acc[i][jj][v]) * acc[i][2 + jj][v]);
+                    }
+            }
         }
         __syncthreads();
 #pragma unroll
@@ -1070,16 +1101,30 @@ __global__ __launch_bounds__(256, 2) void k_gemm_v5(GemmArgs a, int nN) {
             s_wp[tid] = my_pair < 0 ? 0.0f : (my_pair < a.Tk ? a.w[my_pair] : 1.0f);
         }
         __syncthreads();
+        if (half) {  // rows 0..63, columns wave * 64 ..
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = wn * 128 + j * 32 + col;
+            for (int j = 0; j < 2; ++j) {
+                const int c = wave * 64 + j * 32 + col;
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                    ot[row * V3_OUT_LD + c] = (uint16_t)f32_bf16_rne(acc[i][j][v] * s_wp[row]);
-                }
+                    for (int v = 0; v < 16; ++v) {
+                        int row = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                        ot[row * V3_OUT_LD + c] = (uint16_t)f32_bf16_rne(acc[i][j][v] * s_wp[row]);
+                    }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = wn * 128 + j * 32 + col;
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        int row = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                        ot[row * V3_OUT_LD + c] = (uint16_t)f32_bf16_rne(acc[i][j][v] * s_wp[row]);
+                    }
+            }
         }
         __syncthreads();
         uint16_t* op = (uint16_t*)a.o_pairs;

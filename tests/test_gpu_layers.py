@@ -818,3 +818,43 @@ def test_bf16_gemm_with_128_byte_weight_rows_matches_the_ring_kernel():
     rows = np.sort(np.random.default_rng(seed).choice(T, size=12, replace=False))
     for l in range(L):
         check_layer(shape, seed, l, outs["3"][0][l][rows].view(np.uint16), outs["3"][1][l][rows])
+
+
+def test_bf16_gemm_split_ragged_tiles_at_their_boundary():
+    # Forced routing gives the experts groups of exactly 0, 1, 24, 30..33, 63, 64,
+    # 65, 128 and 129 rows (150 tokens, top-4, 16 experts, plus the shared expert's
+    # 150 rows), so the grouped GEMM meets tiles of at most 64 rows, which the
+    # 128-byte-row kernel splits over its wavefronts by columns, right beside
+    # tiles of 65 rows, which it does not. Its layer output must be the bits of
+    # the three-stage ring kernel's and within the bar of the oracle's.
+    import os
+    shape = small_shape("bf16")
+    seed, T, k, E = 41, 150, shape.top_k, shape.experts
+    counts = [64, 65, 1, 128, 129, 63, 0, 32, 33, 31, 30, 24, 0, 0, 0, 0]
+    assert sum(counts) == T * k and max(counts) <= T
+    pool = np.repeat(np.arange(E, dtype=np.int32), counts)
+    ids = np.stack([pool[j * T:(j + 1) * T] for j in range(k)], axis=1)  # token t: pool[t + jT]
+    assert all(len(set(r)) == k for r in ids)
+    x = synth.activations(seed, 93, T, shape.hidden, 1.0, True)
+    ys = {}
+    for path in ("2", "3"):
+        os.environ["EO_GEMM_PATH"] = path
+        try:
+            e = make_engine(shape, seed, max_tokens=T)
+            try:
+                eo.eo_set_bandwidth(e, 50, 50)
+                y = torch.zeros((T, shape.hidden), dtype=torch.float32, device="cuda")
+                eo.eo_moe_layer(e, 0, dev(x.view(np.int16)), y, T, dev(ids), _stream())
+                torch.cuda.synchronize()
+                ys[path] = y.cpu().numpy()
+            finally:
+                eo.eo_destroy(e)
+        finally:
+            del os.environ["EO_GEMM_PATH"]
+    assert np.array_equal(ys["2"].view(np.uint32), ys["3"].view(np.uint32))
+    xf = synth.bf16_bits_to_f32(x)
+    R = synth.router_weights(seed, 0, E, shape.hidden)
+    ids_o, w_o, _ = OR.route(xf, R, k, ids)
+    assert np.array_equal(ids_o, ids)
+    err = rel_err(ys["3"], oracle_layer(shape, seed, 0, xf, ids_o, w_o))
+    assert err <= TOL, f"rel err {err:.3e}"
